@@ -1,0 +1,71 @@
+"""Plant plausible mistakes in copies of the oracle source and check that the
+pins catch every one of them (CPU only; the real oracle is never modified)."""
+import shutil
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+# (name, exact text in the oracle source, replacement)
+MUTANTS = [
+    ("dropped_scale", "s[j] = sm_scale * acc;", "s[j] = acc;"),
+    ("length_off_by_one", "if (is_valid_index(idx_row[j], bound)) L = j + 1;",
+     "if (is_valid_index(idx_row[j], bound)) L = j;"),
+    ("validity_inclusive_bound", "return idx >= 0 && (int64_t)idx < bound;",
+     "return idx >= 0 && (int64_t)idx <= bound;"),
+    ("validity_admits_negative", "return idx >= 0 && (int64_t)idx < bound;",
+     "return idx >= -1 && (int64_t)idx < bound;"),
+    ("lse_drops_max", "lse_row[h] = m + log(Z);", "lse_row[h] = log(Z);"),
+    ("lse_includes_sink", "lse_row[h] = m + log(Z);", "lse_row[h] = m + log(denom);"),
+    ("sink_unshifted", "denom += exp((double)attn_sink[h] - m);", "denom += exp((double)attn_sink[h]);"),
+    ("sink_sign", "denom += exp((double)attn_sink[h] - m);", "denom += exp(-(double)attn_sink[h] - m);"),
+    ("value_from_tail_columns", "o[c] += p * bf16_to_double(keys[j][c]);",
+     "o[c] += p * bf16_to_double(keys[j][c + (d_qk - d_v)]);"),
+    ("no_normalisation", "for (int32_t c = 0; c < d_v; ++c) o[c] /= denom;", ""),
+    ("head_ignored", "const uint16_t *qh = q_row + (int64_t)h * d_qk;", "const uint16_t *qh = q_row;"),
+    ("explicit_length_ignored", "if (explicit_len != NULL) {", "if (0) {"),
+    ("explicit_length_unclamped_low", "if (L < 0) L = 0;", ""),
+    ("empty_lse_sign", "lse_row[h] = INFINITY;", "lse_row[h] = -INFINITY;"),
+    ("empty_max_sign", "ml_row[h] = -INFINITY;", "ml_row[h] = INFINITY;"),
+    ("max_logits_unscaled", "ml_row[h] = m;", "ml_row[h] = m / sm_scale;"),
+    ("page_slot_wrong", "keys[nk++] = kv_cache + (page * page_size + idx[j] % page_size) * (int64_t)d_qk;",
+     "keys[nk++] = kv_cache + (page * page_size + idx[j] / page_size) * (int64_t)d_qk;"),
+    ("page_table_row_wrong", "int64_t page = block_table[b * max_blocks_per_seq + idx[j] / page_size];",
+     "int64_t page = block_table[idx[j] / page_size];"),
+    ("decode_bound_ignored", "if (!is_valid_index(idx[j], bound)) continue;",
+     "if (!is_valid_index(idx[j], 1 << 30)) continue;"),
+    ("row_bound_not_clamped",
+     "int64_t addressable = (int64_t)max_blocks_per_seq * page_size;\n            if (bound > addressable) bound = addressable;",
+     "int64_t addressable = (int64_t)max_blocks_per_seq * page_size;"),
+    ("row_length_bound_not_clamped", "bound = cache_seqlens[r / rows_per_seq];\n            if (bound > addressable) bound = addressable;",
+     "bound = cache_seqlens[r / rows_per_seq];"),
+    ("positions_past_length_used", "for (int32_t j = 0; j < L; ++j)\n                if (is_valid_index(idx[j], s_kv))",
+     "for (int32_t j = 0; j < topk; ++j)\n                if (is_valid_index(idx[j], s_kv))"),
+    ("softmax_not_shifted", "Z += exp(s[j] - m);", "Z += exp(s[j]);"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(workdir, name, old, new):
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/absent"
+    mutated = workdir / f"{name}.c"
+    mutated.write_text(src.replace(old, new))
+    lib_path = workdir / f"lib_{name}.so"
+    oracle.build(mutated, lib_path)
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} passed every pin"

@@ -1,0 +1,16 @@
+"""The CPU oracle against its pins (library attention, brute force, closed
+forms, page fixtures).  CPU only."""
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(lib, pin):
+    pin(lib)
