@@ -1,0 +1,350 @@
+#!/usr/bin/env python
+"""Benchmark of the sparse top-k MLA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one call of the hot path (row lengths, index validity, gather,
+S = QK^T, masked online softmax, P.V, finalize) over one batch of synthetic
+input that is resident in HBM before timing starts.  The default workload is
+the sparse prefill with 64 heads, d_qk = d_v = 512, s_q = s_kv = 8192 and a
+1152-wide causal ramp capped at 1027 keys (no topk_length, so the tail scan
+runs); the same rows with topk_length are timed beside it.
+
+Prints ONE JSON line: throughput in TFLOP/s over valid (query, key) pairs
+(FLOPs = 2 * h_q * (d_qk + d_v) * sum of valid keys, counted from the data),
+ms per call, the roofline of the kernel and the CPU oracle timed on a bounded
+sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+PROFILES = ROOT / "profiles"
+METRIC = "sparse MLA fwd ms/call + TFLOP/s over valid keys; % MFMA / HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_h64",
+                    choices=["prefill_h64", "prefill_h64_len", "prefill_h128", "decode_dynamic",
+                             "decode_dynamic_nolen", "decode_fixed", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain device copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workload
+# ---------------------------------------------------------------------------
+
+def make_case(name):
+    from sparse_top_mla_amd import workloads as W
+    if name == "prefill_h64":
+        return W.prefill_h64(with_length=False)
+    if name == "prefill_h64_len":
+        return W.prefill_h64(with_length=True)
+    if name == "prefill_h128":
+        return W.prefill_h128()
+    if name == "decode_dynamic":
+        return W.decode_dynamic(with_length=True)
+    if name == "decode_dynamic_nolen":
+        return W.decode_dynamic(with_length=False)
+    if name == "decode_fixed":
+        return W.decode_fixed()
+    if name == "tiny":
+        return W.tiny_prefill()
+    raise ValueError(name)
+
+
+def is_decode(case):
+    return hasattr(case, "kv_cache")
+
+
+def valid_mask(case):
+    """[rows, topk] bool: position j of row r is one of the row's keys."""
+    idx = case.indices.reshape(-1, case.topk).numpy().astype(np.int64)
+    rows = idx.shape[0]
+    if is_decode(case):
+        mbps = case.block_table.shape[1]
+        bound = np.minimum(case.cache_seqlens.numpy().astype(np.int64), mbps * 64)
+        bound = np.repeat(bound, case.s_q)
+    else:
+        bound = np.full(rows, case.s_kv, dtype=np.int64)
+    ok = (idx >= 0) & (idx < bound[:, None])
+    pos = np.arange(case.topk)[None, :]
+    if case.topk_length is not None:
+        L = np.clip(case.topk_length.reshape(-1).numpy().astype(np.int64), 0, case.topk)
+    else:
+        last = np.where(ok, pos, -1).max(axis=1)
+        L = last + 1
+    ok &= pos < L[:, None]
+    if is_decode(case):
+        b = np.repeat(np.arange(case.batch), case.s_q)
+        bt = case.block_table.numpy().astype(np.int64)
+        page = np.where(ok, bt[b[:, None], np.where(ok, idx, 0) // 64], -1)
+        ok &= (page >= 0) & (page < case.kv_cache.shape[0])
+    return ok, idx
+
+
+def algorithmic_counts(case):
+    """FLOPs over valid keys and the minimum HBM bytes one call must move:
+    Q once, every distinct KV row a request names once, the index vectors,
+    the optional lengths / block table / cache lengths, and the outputs."""
+    ok, idx = valid_mask(case)
+    n_valid = int(ok.sum())
+    d_qk, d_v, h_q = case.d_qk, case.d_v, case.h_q
+    flops = 2.0 * h_q * (d_qk + d_v) * n_valid
+    rows = ok.shape[0]
+    if is_decode(case):
+        b = np.repeat(np.arange(case.batch), case.s_q)
+        keys = np.unique(b[:, None].repeat(case.topk, 1)[ok] * (1 << 32) + idx[ok])
+        kv_rows = keys.size
+        extra = case.block_table.numel() * 4 + case.cache_seqlens.numel() * 4
+    else:
+        kv_rows = np.unique(idx[ok]).size
+        extra = 0
+    bytes_ = (rows * h_q * d_qk * 2 + kv_rows * d_qk * 2 + idx.size * 4
+              + (rows * 4 if case.topk_length is not None else 0) + extra
+              + rows * h_q * d_v * 2 + 2 * rows * h_q * 4)
+    return dict(flops=flops, bytes=float(bytes_), valid_pairs=n_valid, kv_rows=int(kv_rows),
+                rows=rows, valid_per_row=ok.sum(axis=1))
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def gpu_call(case, dev):
+    import torch
+    import sparse_top_mla_amd as smla
+    t = lambda x: None if x is None else x.to(dev)  # noqa: E731
+    if is_decode(case):
+        args = [t(case.q), t(case.kv_cache), t(case.block_table), t(case.cache_seqlens),
+                t(case.indices)]
+        sink, tl = t(case.attn_sink), t(case.topk_length)
+        out = torch.empty(case.batch, case.s_q, case.h_q, case.d_v, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(case.batch, case.s_q, case.h_q, dtype=torch.float32, device=dev)
+        ml = torch.empty_like(lse)
+
+        def call():
+            smla.decode_fwd(*args, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl,
+                            out=out, lse=lse, max_logits=ml)
+    else:
+        args = [t(case.q), t(case.kv), t(case.indices)]
+        sink, tl = t(case.attn_sink), t(case.topk_length)
+        out = torch.empty(case.s_q, case.h_q, case.d_v, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(case.s_q, case.h_q, dtype=torch.float32, device=dev)
+        ml = torch.empty_like(lse)
+
+        def call():
+            smla.fwd(*args, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl, out=out,
+                     lse=lse, max_logits=ml)
+    return call
+
+
+def time_steps(call, steps, warmup):
+    """W untimed calls, then exactly K calls between two synchronisations.
+    Every call is bracketed by events on the stream it is launched on (the
+    current torch stream), so the per-launch durations are kernel times."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall_ms / steps, per
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle as it stands, on a bounded row sample)
+# ---------------------------------------------------------------------------
+
+def host_threads():
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(case, counts, target_s):
+    import oracle
+    rows = counts["rows"]
+    per_row = counts["valid_per_row"]
+    threads = host_threads()
+
+    def run(sel):
+        t0 = time.perf_counter()
+        if is_decode(case):
+            oracle.sparse_mla_decode_fwd(case.q, case.kv_cache, case.block_table, case.cache_seqlens,
+                                         case.indices, case.sm_scale, case.d_v,
+                                         attn_sink=case.attn_sink, topk_length=case.topk_length,
+                                         rows=sel, threads=threads)
+        else:
+            oracle.sparse_mla_fwd(case.q, case.kv, case.indices, case.sm_scale, case.d_v,
+                                  attn_sink=case.attn_sink, topk_length=case.topk_length,
+                                  rows=sel, threads=threads)
+        return time.perf_counter() - t0
+
+    def sample(n):
+        n = max(1, min(rows, n))
+        return np.unique(np.linspace(0, rows - 1, n).round().astype(np.int64))
+
+    probe = sample(2 * threads)
+    t = run(probe)
+    flops_per_s = 2.0 * case.h_q * (case.d_qk + case.d_v) * per_row[probe].sum() / max(t, 1e-9)
+    avg_row_flops = 2.0 * case.h_q * (case.d_qk + case.d_v) * per_row.mean()
+    n = int(target_s * flops_per_s / max(avg_row_flops, 1.0))
+    sel = sample(n)
+    t = run(sel)
+    flops = 2.0 * case.h_q * (case.d_qk + case.d_v) * per_row[sel].sum()
+    return {"value": float(flops / t / 1e12), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sel.size} of {rows} rows, evenly spaced ({flops / counts['flops']:.2%} of "
+                      f"the valid-key FLOPs), {t:.1f} s, fp64 C oracle",
+            "seconds": t, "ms_per_call_extrapolated": float(t * counts["flops"] / flops * 1e3)}
+
+
+# ---------------------------------------------------------------------------
+# roofline
+# ---------------------------------------------------------------------------
+
+def kernel_source_digest():
+    src = (ROOT / "sparse_top_mla_amd" / "csrc" / "sparse_mla.hip").read_bytes()
+    return hashlib.sha256(src).hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel source."""
+    f = PROFILES / f"traffic_{workload}.json"
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text())
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def roofline(workload, case, counts, kernel_ms):
+    if is_decode(case):
+        achieved = counts["bytes"] / (kernel_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": stored_traffic(workload)}
+    achieved = counts["flops"] / (kernel_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic(workload)}
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    case = make_case(args.workload)
+    counts = algorithmic_counts(case)
+    call = gpu_call(case, dev)
+    call()
+    torch.cuda.synchronize()
+    ms_per_step, per = time_steps(call, args.steps, args.warmup)
+    kernel_ms = statistics.fmean(per)
+    value = counts["flops"] / (ms_per_step * 1e-3) / 1e12
+
+    variants = {}
+    if args.workload == "prefill_h64":
+        case_len = make_case("prefill_h64_len")
+        call_len = gpu_call(case_len, dev)
+        ms_len, per_len = time_steps(call_len, args.steps, args.warmup)
+        variants["with_topk_length"] = {"ms_per_call": ms_len,
+                                        "kernel_ms": statistics.fmean(per_len),
+                                        "tflops": counts["flops"] / (ms_len * 1e-3) / 1e12}
+        del call_len, case_len
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "rows": counts["rows"],
+            "h_q": case.h_q, "d_qk": case.d_qk, "d_v": case.d_v, "topk": case.topk,
+            "valid_pairs": counts["valid_pairs"],
+            "flops_per_call": counts["flops"],
+            "algorithmic_bytes_per_call": counts["bytes"],
+            "topk_length": case.topk_length is not None,
+            "attn_sink": case.attn_sink is not None,
+        },
+        "kernel_ms": {"mean": kernel_ms, "median": statistics.median(per), "min": min(per),
+                      "max": max(per)},
+        "roofline": roofline(args.workload, case, counts, kernel_ms),
+        "hbm_gbs_algorithmic": counts["bytes"] / (kernel_ms * 1e-3) / 1e9,
+    }
+    if variants:
+        result["variants"] = variants
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(case, counts, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

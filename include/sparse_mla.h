@@ -1,0 +1,130 @@
+/*
+ * sparse_mla.h -- C ABI of the MI355X (gfx950) sparse top-k MLA attention
+ * forward library (libsparse_mla.so).
+ *
+ * The operation (FlashMLA PR #196, "Problem" and "Fix"; PR #216, "Summary";
+ * PR #198, "Summary" for the sink):
+ *   every query row attends, with all h_q heads sharing one latent KV head
+ *   (h_kv = 1), to the KV rows named by its own int32 index vector.  V is the
+ *   first d_v columns of each KV row.  An index entry is valid iff
+ *   0 <= idx < K (K = s_kv for prefill, the request's cache length for
+ *   decode); invalid entries are masked.  The row length L is topk_length[r]
+ *   clamped to [0, topk] when topk_length is given, else one past the last
+ *   valid entry of the row (0 when none); positions >= L are never used to
+ *   address KV.  With a per-head attn_sink, exp(sink[h]) joins the softmax
+ *   denominator (out only).  A row without valid entries yields out = 0,
+ *   lse = +inf and max_logits = -inf.
+ *
+ * Outputs, per row r and head h:
+ *   out[r,h,:]     = sum_j softmax_j * V[key_j]            (bf16, RNE)
+ *   lse[r,h]       = natural-log log-sum-exp of the scaled logits
+ *                    sm_scale * q.k over the row's keys (without the sink)
+ *   max_logits[r,h]= max of those scaled logits
+ *
+ * Conventions shared by all entry points
+ *   Memory:    every pointer is a device pointer to caller-owned, contiguous,
+ *              16-byte aligned memory.  The library allocates, frees and
+ *              synchronises nothing; work is enqueued on `stream` only
+ *              (0 = the null stream).
+ *   Values:    index, length and block-table contents are data, never
+ *              validated and never errors: invalid entries are masked.
+ *   Errors:    shape and pointer problems are reported synchronously as a
+ *              status code before anything is launched; a failed launch is
+ *              SMLA_ERR_LAUNCH.  sparse_mla_last_error() returns a
+ *              thread-local text for the last non-OK status.
+ *   Threading: stateless apart from the thread-local error text.
+ *   Support:   h_kv = 1; d_qk in {512, 576}; d_v = 512; h_q a multiple of 16
+ *              in [16, 128]; page_size = 64 for decode.
+ */
+#ifndef SPARSE_MLA_H
+#define SPARSE_MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SMLA_OK = 0,
+    SMLA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                 */
+    SMLA_ERR_BAD_SHAPE = 2,   /* a size is non-positive or inconsistent     */
+    SMLA_ERR_UNSUPPORTED = 3, /* outside the support list above             */
+    SMLA_ERR_LAUNCH = 4       /* the kernel launch reported an error        */
+} smla_status;
+
+/* A HIP stream handle (hipStream_t); void* keeps this header free of HIP. */
+typedef void *smla_stream_t;
+
+/*
+ * Sparse prefill forward (FlashMLA PR #196).
+ *   q           bf16  [s_q, h_q, d_qk]
+ *   kv          bf16  [s_kv, h_kv, d_qk]; V = kv[..., :d_v] (may be NULL when s_kv = 0)
+ *   indices     int32 [s_q, h_kv, topk]
+ *   topk_length int32 [s_q] or NULL (NULL: derive L by the tail scan)
+ *   attn_sink   fp32  [h_q] or NULL
+ *   out         bf16  [s_q, h_q, d_v]
+ *   lse         fp32  [s_q, h_q]
+ *   max_logits  fp32  [s_q, h_q]
+ * s_q = 0 is a valid no-op (pointers may then be NULL).
+ */
+smla_status sparse_mla_fwd(const void *q, const void *kv, const int32_t *indices,
+                           const int32_t *topk_length, const float *attn_sink, int32_t s_q,
+                           int32_t s_kv, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v,
+                           int32_t topk, float sm_scale, void *out, float *lse,
+                           float *max_logits, smla_stream_t stream);
+
+/*
+ * Paged sparse decode forward (FlashMLA PR #216: 64-token page blocks, a
+ * block table, per-row dynamic top-k).
+ *   q             bf16  [B, s_q, h_q, d_qk]
+ *   kv_cache      bf16  [num_blocks, page_size, h_kv, d_qk] (NULL allowed when num_blocks = 0)
+ *   block_table   int32 [B, max_blocks_per_seq]: physical page of each
+ *                 64-token logical page of request b
+ *   cache_seqlens int32 [B]: KV length of request b.  An index is valid iff
+ *                 0 <= idx < min(cache_seqlens[b], max_blocks_per_seq*64);
+ *                 a valid index whose page entry is outside [0, num_blocks)
+ *                 is masked.
+ *   indices       int32 [B, s_q, topk]: logical token positions
+ *   topk_length   int32 [B, s_q] or NULL (one length per query row)
+ *   attn_sink     fp32  [h_q] or NULL
+ *   out           bf16  [B, s_q, h_q, d_v]
+ *   lse           fp32  [B, s_q, h_q]
+ *   max_logits    fp32  [B, s_q, h_q]
+ * B = 0 is a valid no-op (pointers may then be NULL).
+ */
+smla_status sparse_mla_decode_fwd(const void *q, const void *kv_cache,
+                                  const int32_t *block_table, const int32_t *cache_seqlens,
+                                  const int32_t *indices, const int32_t *topk_length,
+                                  const float *attn_sink, int32_t B, int32_t s_q, int32_t h_q,
+                                  int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+                                  int32_t num_blocks, int32_t page_size,
+                                  int32_t max_blocks_per_seq, float sm_scale, void *out,
+                                  float *lse, float *max_logits, smla_stream_t stream);
+
+/*
+ * The row length L every kernel above uses (FlashMLA PR #196, "Fix": tail
+ * scan for the last valid entry; PR #216, "Summary": explicit lengths), from
+ * the same device routine.
+ *   indices       int32 [rows, topk]
+ *   topk_length   int32 [rows] or NULL
+ *   cache_seqlens int32 [rows / rows_per_seq] or NULL.  NULL: the bound is
+ *                 s_kv for every row.  Else the bound of row r is
+ *                 min(cache_seqlens[r / rows_per_seq], addressable) with
+ *                 addressable = max_blocks_per_seq * 64.
+ *   row_len       int32 [rows] (output)
+ */
+smla_status sparse_mla_row_lengths(const int32_t *indices, const int32_t *topk_length,
+                                   const int32_t *cache_seqlens, int32_t rows,
+                                   int32_t rows_per_seq, int32_t topk, int32_t s_kv,
+                                   int32_t max_blocks_per_seq, int32_t *row_len,
+                                   smla_stream_t stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char *sparse_mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MLA_H */

@@ -1,0 +1,194 @@
+"""ctypes binding of libsparse_mla.so (the C ABI in include/sparse_mla.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the current HIP
+stream.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIBRARY = _PKG / "libsparse_mla.so"
+
+_STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL_ARG", 2: "SMLA_ERR_BAD_SHAPE", 3: "SMLA_ERR_UNSUPPORTED",
+           4: "SMLA_ERR_LAUNCH"}
+
+EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_row_lengths",
+           "sparse_mla_last_error")
+
+_lib = None
+
+
+class SparseMLAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library(path: Path | None = None):
+    """Load the HIP library (no GPU needed to load it).  Raises if absent."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(str(path)))
+    if _lib is None:
+        if not LIBRARY.exists():
+            raise RuntimeError(f"{LIBRARY} is not built; run __graft_entry__.build() "
+                               "(or python -m sparse_top_mla_amd.build)")
+        _lib = _declare(ctypes.CDLL(str(LIBRARY)))
+    return _lib
+
+
+def _declare(lib):
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.sparse_mla_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                   vp, vp, vp, vp]
+    lib.sparse_mla_fwd.restype = ctypes.c_int
+    lib.sparse_mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, vp, vp, vp, vp]
+    lib.sparse_mla_decode_fwd.restype = ctypes.c_int
+    lib.sparse_mla_row_lengths.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.sparse_mla_row_lengths.restype = ctypes.c_int
+    lib.sparse_mla_last_error.argtypes = []
+    lib.sparse_mla_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def _check(lib, status):
+    if status != 0:
+        raise SparseMLAError(status, lib.sparse_mla_last_error().decode())
+
+
+def _dev(t, name, dtype, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd(q, kv, indices, sm_scale, d_v=512, attn_sink=None, topk_length=None, *, out=None,
+        lse=None, max_logits=None, stream=None):
+    """Sparse prefill forward.  q [s_q, h_q, d_qk] bf16, kv [s_kv, 1, d_qk]
+    bf16, indices [s_q, 1, topk] int32, topk_length [s_q] int32 or None,
+    attn_sink [h_q] fp32 or None.  Returns (out, lse, max_logits)."""
+    lib = load_library()
+    dev = q.device
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16, dev)
+    _dev(indices, "indices", torch.int32, dev)
+    _dev(topk_length, "topk_length", torch.int32, dev)
+    _dev(attn_sink, "attn_sink", torch.float32, dev)
+    if q.dim() != 3 or kv.dim() != 3 or indices.dim() != 3:
+        raise ValueError("q, kv and indices must be 3-d ([s_q,h_q,d_qk], [s_kv,h_kv,d_qk], [s_q,h_kv,topk])")
+    s_q, h_q, d_qk = q.shape
+    s_kv, h_kv = kv.shape[0], kv.shape[1]
+    topk = indices.shape[-1]
+    if kv.shape[2] != d_qk or indices.shape[0] != s_q or indices.shape[1] != h_kv:
+        raise ValueError("inconsistent shapes of q, kv and indices")
+    if topk_length is not None and tuple(topk_length.shape) != (s_q,):
+        raise ValueError("topk_length must have shape [s_q]")
+    if attn_sink is not None and tuple(attn_sink.shape) != (h_q,):
+        raise ValueError("attn_sink must have shape [h_q]")
+    out = torch.empty((s_q, h_q, d_v), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((s_q, h_q), dtype=torch.float32, device=dev) if lse is None else lse
+    max_logits = torch.empty((s_q, h_q), dtype=torch.float32, device=dev) if max_logits is None else max_logits
+    _dev(out, "out", torch.bfloat16, dev)
+    _dev(lse, "lse", torch.float32, dev)
+    _dev(max_logits, "max_logits", torch.float32, dev)
+    if out.numel() != s_q * h_q * d_v or lse.numel() != s_q * h_q or max_logits.numel() != s_q * h_q:
+        raise ValueError("output buffers have the wrong size")
+    st = lib.sparse_mla_fwd(_p(q), _p(kv), _p(indices), _p(topk_length), _p(attn_sink), s_q, s_kv,
+                            h_q, h_kv, d_qk, d_v, topk, float(sm_scale), _p(out), _p(lse),
+                            _p(max_logits), _stream(dev, stream))
+    _check(lib, st)
+    return out, lse, max_logits
+
+
+def decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, d_v=512,
+               attn_sink=None, topk_length=None, *, out=None, lse=None, max_logits=None,
+               stream=None):
+    """Paged sparse decode forward.  q [B, s_q, h_q, d_qk] bf16,
+    kv_cache [num_blocks, page_size, 1, d_qk] bf16, block_table [B, mbps]
+    int32, cache_seqlens [B] int32, indices [B, s_q, topk] int32,
+    topk_length [B, s_q] (or [B], broadcast over s_q) int32 or None,
+    attn_sink [h_q] fp32 or None.  Returns (out, lse, max_logits)."""
+    lib = load_library()
+    dev = q.device
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv_cache, "kv_cache", torch.bfloat16, dev)
+    _dev(block_table, "block_table", torch.int32, dev)
+    _dev(cache_seqlens, "cache_seqlens", torch.int32, dev)
+    _dev(indices, "indices", torch.int32, dev)
+    _dev(attn_sink, "attn_sink", torch.float32, dev)
+    if q.dim() != 4 or kv_cache.dim() != 4 or indices.dim() != 3 or block_table.dim() != 2:
+        raise ValueError("q [B,s_q,h_q,d_qk], kv_cache [blocks,page,h_kv,d_qk], indices [B,s_q,topk], "
+                         "block_table [B,mbps] expected")
+    B, s_q, h_q, d_qk = q.shape
+    num_blocks, page_size, h_kv = kv_cache.shape[0], kv_cache.shape[1], kv_cache.shape[2]
+    topk = indices.shape[-1]
+    if (kv_cache.shape[3] != d_qk or tuple(indices.shape[:2]) != (B, s_q) or block_table.shape[0] != B
+            or tuple(cache_seqlens.shape) != (B,)):
+        raise ValueError("inconsistent decode shapes")
+    if topk_length is not None:
+        _dev(topk_length, "topk_length", torch.int32, dev)
+        if tuple(topk_length.shape) == (B,):
+            topk_length = topk_length.view(B, 1).expand(B, s_q).contiguous()
+        elif tuple(topk_length.shape) != (B, s_q):
+            raise ValueError("topk_length must have shape [B] or [B, s_q]")
+    if attn_sink is not None and tuple(attn_sink.shape) != (h_q,):
+        raise ValueError("attn_sink must have shape [h_q]")
+    out = torch.empty((B, s_q, h_q, d_v), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev) if lse is None else lse
+    max_logits = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev) if max_logits is None else max_logits
+    _dev(out, "out", torch.bfloat16, dev)
+    _dev(lse, "lse", torch.float32, dev)
+    _dev(max_logits, "max_logits", torch.float32, dev)
+    if out.numel() != B * s_q * h_q * d_v or lse.numel() != B * s_q * h_q or max_logits.numel() != B * s_q * h_q:
+        raise ValueError("output buffers have the wrong size")
+    st = lib.sparse_mla_decode_fwd(_p(q), _p(kv_cache), _p(block_table), _p(cache_seqlens),
+                                   _p(indices), _p(topk_length), _p(attn_sink), B, s_q, h_q, h_kv,
+                                   d_qk, d_v, topk, num_blocks, page_size, block_table.shape[1],
+                                   float(sm_scale), _p(out), _p(lse), _p(max_logits),
+                                   _stream(dev, stream))
+    _check(lib, st)
+    return out, lse, max_logits
+
+
+def row_lengths(indices, topk_length=None, cache_seqlens=None, *, s_kv=0, rows_per_seq=1,
+                max_blocks_per_seq=0, stream=None):
+    """Row lengths L as the kernels use them.  indices [..., topk] int32."""
+    lib = load_library()
+    dev = indices.device
+    _dev(indices, "indices", torch.int32)
+    _dev(topk_length, "topk_length", torch.int32, dev)
+    _dev(cache_seqlens, "cache_seqlens", torch.int32, dev)
+    topk = indices.shape[-1]
+    rows = indices.numel() // topk
+    if topk_length is not None and topk_length.numel() != rows:
+        raise ValueError("topk_length must hold one entry per row")
+    out = torch.empty(rows, dtype=torch.int32, device=dev)
+    st = lib.sparse_mla_row_lengths(_p(indices), _p(topk_length), _p(cache_seqlens), rows,
+                                    rows_per_seq, topk, s_kv, max_blocks_per_seq, _p(out),
+                                    _stream(dev, stream))
+    _check(lib, st)
+    return out

@@ -1,0 +1,49 @@
+"""Build libsparse_mla.so in-tree with hipcc for gfx950.
+
+    python -m sparse_top_mla_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+SOURCES = [PKG / "csrc" / "sparse_mla.hip"]
+OUTPUT = PKG / "libsparse_mla.so"
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-shared",
+    "-fPIC",
+    f"-I{ROOT / 'include'}",
+    # packed fp32 VALU forms are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    path = Path(rocm) / "bin" / "hipcc"
+    return str(path) if path.exists() else "hipcc"
+
+
+def build(verbose: bool = False, extra=()) -> Path:
+    tmp = OUTPUT.with_suffix(".so.tmp")
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *map(str, SOURCES), "-o", str(tmp)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed")
+    os.replace(tmp, OUTPUT)
+    return OUTPUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

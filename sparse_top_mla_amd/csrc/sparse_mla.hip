@@ -1,0 +1,525 @@
+// Sparse top-k MLA attention forward for MI355X (gfx950 / CDNA4).
+//
+// What is computed (FlashMLA PR #196, "Problem", "Fix", "Correctness notes";
+// PR #216, "Summary"; PR #198, "Summary" for the sink): every query row
+// attends, with all of its heads sharing one latent KV head, to the KV rows
+// its index vector names.  Entries outside [0, K) are masked; the row length
+// L (explicit topk_length, else one past the last valid entry found by a tail
+// scan) bounds the 64-key block loop; positions >= L never address KV; an
+// optional per-head sink joins the softmax denominator; a row without keys
+// gives out = 0, lse = +inf, max_logits = -inf.
+//
+// Kernel shape (one design for prefill and paged decode):
+//   * one workgroup per (query row, group of up to 64 heads); each wave owns 16
+//     heads.  With two head groups per row (h_q = 128) the two workgroups of
+//     a row get ids that are equal modulo 8, so round-robin dispatch puts
+//     both on the same XCD and the second gather of the row's KV hits that
+//     XCD's L2.
+//   * the row's query slice stays in VGPRs for the whole row (B operand of
+//     S^T = K Q^T).
+//   * per 64-key block: the index vector is loaded one entry per lane and the
+//     validity of every key becomes a 64-bit wave ballot.  A block without a
+//     valid key is skipped outright (no gather, no MFMA): masked keys add
+//     exactly nothing to the online softmax, so skipping is exact.
+//   * valid KV rows are copied global -> LDS directly (global_load_lds, 16 B
+//     per lane, one 1 KiB instruction per row plus a 128 B one for the rope
+//     part at d_qk = 576); masked rows are zero-filled in LDS without touching
+//     memory, so a NaN payload behind a masked index never reaches P*V.
+//   * S^T [64 keys x 16 heads] per wave on v_mfma_f32_16x16x32_bf16 (K rows
+//     from LDS as the A operand), online exp2 softmax in registers (row max /
+//     row sum over the 4 lane groups of a head with two xor shuffles), then
+//     O^T [512 x 16] += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T
+//     taken straight from the S^T accumulators: the keys of the two operands
+//     are paired in a permuted order that makes each lane's P values exactly
+//     the ones it already holds, so P never goes through LDS.
+//   * every lane owns one head for the whole softmax, so the rescale of O and
+//     the final 1/denominator are per-lane scalars.
+//
+// The presence of topk_length, of attn_sink, paging and d_qk are template
+// parameters chosen on the host (FlashMLA PR #216, "Why template"): the fixed
+// path carries no length load, no tail predicate and no sink code.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "sparse_mla.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kBlockKeys = 64;    // keys per block (one per lane of a wave)
+constexpr int kHeadsPerWave = 16; // MFMA N dimension
+constexpr int kDV = 512;          // value width
+constexpr int kPage = 64;         // tokens per KV page (decode)
+constexpr int kMaxThreads = 512;  // up to 8 waves (h_q = 112 runs 7 in one group)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i supplies the address
+// of 4 consecutive 16-bit values; the 16 addresses describe a 4 x 16 tile
+// (row TR_ROW(i), columns 4*TR_COL(i) .. +3) and lane n receives column n of
+// the four rows.
+#define TR_ROW(i) ((i) >> 2)
+#define TR_COL(i) ((i) & 3)
+
+template <int D_QK>
+struct Tile {
+  static constexpr int kRowBytes = D_QK * 2;        // one KV row in HBM
+  static constexpr int kLdsRow = kRowBytes + 16;    // padded LDS row (bank spread)
+  static constexpr int kLdsBytes = kBlockKeys * kLdsRow;
+  static constexpr int kDSteps = D_QK / 32;         // MFMA K steps over d_qk
+  static constexpr int kRopeLanes = (kRowBytes - 1024) / 16;
+  static_assert(D_QK == 512 || D_QK == 576, "d_qk");
+};
+
+struct FwdArgs {
+  const __bf16* q;
+  const uint8_t* kv;
+  const int32_t* indices;
+  const int32_t* topk_length;
+  const float* attn_sink;
+  const int32_t* block_table;
+  const int32_t* cache_seqlens;
+  __bf16* out;
+  float* lse;
+  float* max_logits;
+  int32_t rows;          // query rows (prefill s_q; decode B * s_q)
+  int32_t rows_per_seq;  // decode s_q (row r belongs to request r / rows_per_seq)
+  int32_t h_q;
+  int32_t topk;
+  int32_t s_kv;          // prefill validity bound
+  int32_t num_blocks;    // decode page pool size
+  int32_t mbps;          // decode max_blocks_per_seq
+  int32_t head_groups;   // workgroups per row (1 or 2)
+  float scale_log2;      // sm_scale * log2(e)
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Validity bound K of a row: s_kv for prefill; for paged decode the request's
+// cache length, cut to what its block table can address.
+__device__ __forceinline__ int row_bound(bool paged, const int32_t* cache_seqlens, int seq,
+                                         int s_kv, int mbps) {
+  if (!paged) return s_kv;
+  const long long cs = cache_seqlens[seq];
+  const long long addressable = (long long)mbps * kPage;
+  return (int)(cs < addressable ? cs : addressable);
+}
+
+// Tail scan (FlashMLA PR #196, "Fix"): one round inspects the trailing 256
+// positions of [0, end) with 4 coalesced loads per lane; the loads of the
+// first round are issued before the rest of the prologue and consumed after.
+struct TailRound {
+  int v[4];
+};
+
+__device__ __forceinline__ TailRound load_tail_round(const int32_t* idx_row, int end) {
+  TailRound t;
+  const int lane = lane_id();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int p = end - 256 + e * 64 + lane;
+    t.v[e] = p >= 0 ? idx_row[p] : -1;
+  }
+  return t;
+}
+
+// Highest valid position of the round plus one, or 0 if it holds none.
+__device__ __forceinline__ int resolve_tail_round(const TailRound& t, int end, int bound) {
+#pragma unroll
+  for (int e = 3; e >= 0; --e) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(t.v[e] >= 0 && t.v[e] < bound);
+    if (m) return end - 256 + e * 64 + (63 - __builtin_clzll(m)) + 1;
+  }
+  return 0;
+}
+
+__device__ __forceinline__ int finish_tail_scan(const TailRound& first, const int32_t* idx_row,
+                                                int topk, int bound) {
+  int L = resolve_tail_round(first, topk, bound);
+  for (int end = topk - 256; L == 0 && end > 0; end -= 256)
+    L = resolve_tail_round(load_tail_round(idx_row, end), end, bound);
+  return L;
+}
+
+__device__ __forceinline__ int clamp_length(int t, int topk) {
+  return t < 0 ? 0 : (t > topk ? topk : t);
+}
+
+// Copy the block's KV rows into LDS: valid rows by direct global->LDS loads,
+// masked rows as zeros (no memory access).  Wave w handles rows w, w+nw, ...
+template <int D_QK>
+__device__ __forceinline__ void stage_block(LDS_AS uint8_t* lds, const uint8_t* kv, uint64_t mask,
+                                            int phys, int wave, int nwaves) {
+  using T = Tile<D_QK>;
+  const int lane = lane_id();
+  for (int j = wave; j < kBlockKeys; j += nwaves) {
+    LDS_AS uint8_t* dst = lds + j * T::kLdsRow;
+    if ((mask >> j) & 1ull) {
+      const int r = __builtin_amdgcn_readlane(phys, j);
+      const uint8_t* src = kv + (size_t)(uint32_t)r * T::kRowBytes;
+      __builtin_amdgcn_global_load_lds((const void*)(src + lane * 16), (LDS_AS void*)dst, 16, 0, 0);
+      if (T::kRopeLanes > 0 && lane < T::kRopeLanes)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 1024 + lane * 16),
+                                         (LDS_AS void*)(dst + 1024), 16, 0, 0);
+    } else {
+      *reinterpret_cast<LDS_AS u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      if (T::kRopeLanes > 0 && lane < T::kRopeLanes)
+        *reinterpret_cast<LDS_AS u32x4*>(dst + 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
+__global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) {
+  using T = Tile<D_QK>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[T::kLdsBytes];
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int g = lane >> 4;    // lane group: 4 keys (S^T) / 4 value columns (O^T)
+  const int hl = lane & 15;   // head within the wave (S^T / O^T column)
+
+  int row, grp;
+  if (a.head_groups == 1) {
+    row = blockIdx.x;
+    grp = 0;
+  } else {  // ids 16*t + u and 16*t + u + 8 share row 8*t + u (same XCD)
+    const int t = blockIdx.x >> 4, u = blockIdx.x & 15;
+    grp = u >> 3;
+    row = t * 8 + (u & 7);
+  }
+  if (row >= a.rows) return;
+  const int seq = row / a.rows_per_seq;
+  const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
+  const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+
+  TailRound first;
+  int tl = 0;
+  if (DYNAMIC)
+    tl = a.topk_length[row];
+  else
+    first = load_tail_round(idx_row, a.topk);
+
+  // Query slice of this wave's 16 heads: lane (g, hl) holds q[head hl][32s + 8g .. +8].
+  const int head0 = grp * nwaves * kHeadsPerWave + wave * kHeadsPerWave;
+  const __bf16* qp = a.q + ((size_t)row * a.h_q + head0 + hl) * D_QK + g * 8;
+  bf16x8 qreg[T::kDSteps];
+#pragma unroll
+  for (int s = 0; s < T::kDSteps; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + s * 32);
+
+  const int L = DYNAMIC ? clamp_length(tl, a.topk) : finish_tail_scan(first, idx_row, a.topk, bound);
+
+  f32x4 acc[kDV / 16];
+#pragma unroll
+  for (int ct = 0; ct < kDV / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max of the log2-scaled logits
+  float l_run = 0.f;        // running sum of exp2(logit - m_run)
+
+  const int nblk = (L + kBlockKeys - 1) / kBlockKeys;
+  for (int kb = 0; kb < nblk; ++kb) {
+    // a2/a3: index, validity (positions >= L are masked before any use), page.
+    const int pos = kb * kBlockKeys + lane;
+    const int idx = pos < L ? idx_row[pos] : -1;
+    bool ok = idx >= 0 && idx < bound;
+    int phys = idx;
+    if (PAGED) {
+      const int page = ok ? a.block_table[(size_t)seq * a.mbps + (idx >> 6)] : -1;
+      ok = ok && page >= 0 && page < a.num_blocks;
+      phys = page * kPage + (idx & (kPage - 1));
+    }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(ok);
+    if (mask == 0) continue;  // identical in every wave of the workgroup
+
+    // a4: gather into LDS.
+    __syncthreads();  // every wave is done reading the previous block
+    stage_block<D_QK>(lds, a.kv, mask, phys, wave, nwaves);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // a5: S^T = K Q^T; lane (g, hl) gets keys kt*16 + 4g + r of head hl.
+    f32x4 st[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < T::kDSteps; ++s) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const bf16x8 kfrag = *reinterpret_cast<const LDS_AS bf16x8*>(
+            lds + (kt * 16 + hl) * T::kLdsRow + s * 64 + g * 16);
+        st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag, qreg[s], st[kt], 0, 0, 0);
+      }
+    }
+
+    // a6: mask, online softmax in log2 units.
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint32_t bits = (uint32_t)(mask >> (kt * 16 + g * 4)) & 0xFu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = ((bits >> r) & 1u) ? st[kt][r] * a.scale_log2 : -INFINITY;
+        st[kt][r] = x;
+        rmax = fmaxf(rmax, x);
+      }
+    }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float m_new = fmaxf(m_run, rmax);  // finite: the block has a valid key
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float rsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(st[kt][r] - m_new);
+        st[kt][r] = p;
+        rsum += p;
+      }
+    }
+    rsum += __shfl_xor(rsum, 16);
+    rsum += __shfl_xor(rsum, 32);
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+#pragma unroll
+    for (int ct = 0; ct < kDV / 16; ++ct) acc[ct] *= alpha;
+
+    // P^T operand of key step s2: element e <-> key 32*s2 + 16*(e/4) + 4g + e%4.
+    bf16x8 pfrag[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pfrag[s2][e] = (__bf16)st[2 * s2 + (e >> 2)][e & 3];
+
+    // a7: O^T += V^T P^T; V^T element e of lane (g, c) is V[same key][c].
+#pragma unroll
+    for (int ct = 0; ct < kDV / 16; ++ct) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const LDS_AS uint8_t* base =
+            lds + (32 * s2 + 4 * g + TR_ROW(hl)) * T::kLdsRow + (ct * 16 + 4 * TR_COL(hl)) * 2;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)base);
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(base + 16 * T::kLdsRow));
+        const bf16x8 vfrag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfrag, pfrag[s2], acc[ct], 0, 0, 0);
+      }
+    }
+  }
+
+  // a8: finalize.  acc[ct][r] = O[head hl][value column ct*16 + 4g + r].
+  const int h = head0 + hl;
+  float inv = 0.f, lse_v = INFINITY, ml_v = -INFINITY;
+  if (l_run > 0.f) {
+    float denom = l_run;
+    if (SINK) denom += __builtin_amdgcn_exp2f(a.attn_sink[h] * kLog2e - m_run);
+    inv = 1.f / denom;
+    ml_v = m_run * kLn2;
+    lse_v = (m_run + __log2f(l_run)) * kLn2;
+  }
+  __bf16* op = a.out + ((size_t)row * a.h_q + h) * kDV + g * 4;
+#pragma unroll
+  for (int ct = 0; ct < kDV / 16; ++ct) {
+    const bf16x4 o4 = {(__bf16)(acc[ct][0] * inv), (__bf16)(acc[ct][1] * inv),
+                       (__bf16)(acc[ct][2] * inv), (__bf16)(acc[ct][3] * inv)};
+    *reinterpret_cast<bf16x4*>(op + ct * 16) = o4;
+  }
+  if (g == 0) {
+    a.lse[(size_t)row * a.h_q + h] = lse_v;
+    a.max_logits[(size_t)row * a.h_q + h] = ml_v;
+  }
+}
+
+// Row lengths from the same routines the attention kernels use; one wave per row.
+__global__ void __launch_bounds__(256) row_lengths_kernel(const int32_t* indices,
+                                                          const int32_t* topk_length,
+                                                          const int32_t* cache_seqlens, int rows,
+                                                          int rows_per_seq, int topk, int s_kv,
+                                                          int mbps, int32_t* row_len) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  int L;
+  if (topk_length != nullptr) {
+    L = clamp_length(topk_length[row], topk);
+  } else {
+    const int bound = row_bound(cache_seqlens != nullptr, cache_seqlens, row / rows_per_seq, s_kv, mbps);
+    const int32_t* idx_row = indices + (size_t)row * topk;
+    L = finish_tail_scan(load_tail_round(idx_row, topk), idx_row, topk, bound);
+  }
+  if (lane_id() == 0) row_len[row] = L;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+thread_local std::string g_last_error;
+
+smla_status fail(smla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+smla_status check_common(int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk) {
+  if (h_q <= 0 || topk <= 0 || d_qk <= 0 || d_v <= 0)
+    return fail(SMLA_ERR_BAD_SHAPE, "non-positive size (h_q=%d topk=%d d_qk=%d d_v=%d)", h_q, topk,
+                d_qk, d_v);
+  if (d_v > d_qk) return fail(SMLA_ERR_BAD_SHAPE, "d_v=%d exceeds d_qk=%d", d_v, d_qk);
+  if (h_kv != 1) return fail(SMLA_ERR_UNSUPPORTED, "h_kv=%d (only 1 is supported)", h_kv);
+  if (d_qk != 512 && d_qk != 576)
+    return fail(SMLA_ERR_UNSUPPORTED, "d_qk=%d (supported: 512, 576)", d_qk);
+  if (d_v != kDV) return fail(SMLA_ERR_UNSUPPORTED, "d_v=%d (supported: 512)", d_v);
+  if (h_q % kHeadsPerWave != 0 || h_q > 128)
+    return fail(SMLA_ERR_UNSUPPORTED, "h_q=%d (supported: multiples of 16 up to 128)", h_q);
+  return SMLA_OK;
+}
+
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
+smla_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
+  const int waves_total = args.h_q / kHeadsPerWave;
+  const int nwaves = waves_total / args.head_groups;
+  const int grid = args.head_groups == 1 ? args.rows : ((args.rows + 7) / 8) * 16;
+  hipLaunchKernelGGL((sparse_mla_fwd_kernel<D_QK, PAGED, DYNAMIC, SINK>), dim3(grid),
+                     dim3(nwaves * 64), 0, stream, args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+template <bool PAGED>
+smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
+  const int waves_total = args.h_q / kHeadsPerWave;
+  args.head_groups = (waves_total > 4 && waves_total % 2 == 0) ? 2 : 1;
+  const bool dyn = args.topk_length != nullptr;
+  const bool sink = args.attn_sink != nullptr;
+#define SMLA_CASE(D, DYN, SNK)                                                     \
+  if (d_qk == D && dyn == DYN && sink == SNK) return launch_fwd<D, PAGED, DYN, SNK>(args, stream);
+  SMLA_CASE(512, false, false)
+  SMLA_CASE(512, false, true)
+  SMLA_CASE(512, true, false)
+  SMLA_CASE(512, true, true)
+  SMLA_CASE(576, false, false)
+  SMLA_CASE(576, false, true)
+  SMLA_CASE(576, true, false)
+  SMLA_CASE(576, true, true)
+#undef SMLA_CASE
+  return fail(SMLA_ERR_UNSUPPORTED, "no kernel instance for d_qk=%d", d_qk);
+}
+
+}  // namespace
+
+extern "C" smla_status sparse_mla_fwd(const void* q, const void* kv, const int32_t* indices,
+                                      const int32_t* topk_length, const float* attn_sink,
+                                      int32_t s_q, int32_t s_kv, int32_t h_q, int32_t h_kv,
+                                      int32_t d_qk, int32_t d_v, int32_t topk, float sm_scale,
+                                      void* out, float* lse, float* max_logits,
+                                      smla_stream_t stream) {
+  g_last_error.clear();
+  if (s_q < 0 || s_kv < 0) return fail(SMLA_ERR_BAD_SHAPE, "negative s_q=%d or s_kv=%d", s_q, s_kv);
+  smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk);
+  if (st != SMLA_OK) return st;
+  if (s_q == 0) return SMLA_OK;
+  if (!q || (!kv && s_kv > 0) || !indices || !out || !lse || !max_logits)
+    return fail(SMLA_ERR_NULL_ARG,
+                "sparse_mla_fwd: q, kv (unless s_kv = 0), indices, out, lse and max_logits are required");
+  FwdArgs args{};
+  args.q = static_cast<const __bf16*>(q);
+  args.kv = static_cast<const uint8_t*>(kv);
+  args.indices = indices;
+  args.topk_length = topk_length;
+  args.attn_sink = attn_sink;
+  args.out = static_cast<__bf16*>(out);
+  args.lse = lse;
+  args.max_logits = max_logits;
+  args.rows = s_q;
+  args.rows_per_seq = 1;
+  args.h_q = h_q;
+  args.topk = topk;
+  args.s_kv = s_kv;
+  args.scale_log2 = sm_scale * kLog2e;
+  return dispatch_fwd<false>(d_qk, args, static_cast<hipStream_t>(stream));
+}
+
+extern "C" smla_status sparse_mla_decode_fwd(
+    const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+    const int32_t* indices, const int32_t* topk_length, const float* attn_sink, int32_t B,
+    int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+    int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale, void* out,
+    float* lse, float* max_logits, smla_stream_t stream) {
+  g_last_error.clear();
+  if (B < 0 || s_q <= 0 || num_blocks < 0 || max_blocks_per_seq <= 0)
+    return fail(SMLA_ERR_BAD_SHAPE, "bad sizes (B=%d s_q=%d num_blocks=%d max_blocks_per_seq=%d)",
+                B, s_q, num_blocks, max_blocks_per_seq);
+  smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk);
+  if (st != SMLA_OK) return st;
+  if (page_size != kPage) return fail(SMLA_ERR_UNSUPPORTED, "page_size=%d (supported: 64)", page_size);
+  if ((long long)num_blocks * kPage > 0x7fffffffLL)
+    return fail(SMLA_ERR_UNSUPPORTED, "num_blocks=%d exceeds 2^31 tokens", num_blocks);
+  if ((long long)B * s_q > 0x7fffffffLL) return fail(SMLA_ERR_BAD_SHAPE, "B*s_q overflows int32");
+  if (B == 0) return SMLA_OK;
+  if (!q || (!kv_cache && num_blocks > 0) || !block_table || !cache_seqlens || !indices || !out ||
+      !lse || !max_logits)
+    return fail(SMLA_ERR_NULL_ARG,
+                "sparse_mla_decode_fwd: q, kv_cache (unless num_blocks = 0), block_table, "
+                "cache_seqlens, indices, out, lse and max_logits are required");
+  FwdArgs args{};
+  args.q = static_cast<const __bf16*>(q);
+  args.kv = static_cast<const uint8_t*>(kv_cache);
+  args.indices = indices;
+  args.topk_length = topk_length;
+  args.attn_sink = attn_sink;
+  args.block_table = block_table;
+  args.cache_seqlens = cache_seqlens;
+  args.out = static_cast<__bf16*>(out);
+  args.lse = lse;
+  args.max_logits = max_logits;
+  args.rows = B * s_q;
+  args.rows_per_seq = s_q;
+  args.h_q = h_q;
+  args.topk = topk;
+  args.num_blocks = num_blocks;
+  args.mbps = max_blocks_per_seq;
+  args.scale_log2 = sm_scale * kLog2e;
+  return dispatch_fwd<true>(d_qk, args, static_cast<hipStream_t>(stream));
+}
+
+extern "C" smla_status sparse_mla_row_lengths(const int32_t* indices, const int32_t* topk_length,
+                                              const int32_t* cache_seqlens, int32_t rows,
+                                              int32_t rows_per_seq, int32_t topk, int32_t s_kv,
+                                              int32_t max_blocks_per_seq, int32_t* row_len,
+                                              smla_stream_t stream) {
+  g_last_error.clear();
+  if (rows < 0 || topk <= 0 || rows_per_seq <= 0 || s_kv < 0)
+    return fail(SMLA_ERR_BAD_SHAPE, "bad sizes (rows=%d topk=%d rows_per_seq=%d s_kv=%d)", rows,
+                topk, rows_per_seq, s_kv);
+  if (cache_seqlens != nullptr && max_blocks_per_seq <= 0)
+    return fail(SMLA_ERR_BAD_SHAPE, "max_blocks_per_seq=%d with cache_seqlens", max_blocks_per_seq);
+  if (rows == 0) return SMLA_OK;
+  if (!indices || !row_len)
+    return fail(SMLA_ERR_NULL_ARG, "sparse_mla_row_lengths: indices and row_len are required");
+  hipLaunchKernelGGL(row_lengths_kernel, dim3((rows + 3) / 4), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), indices, topk_length, cache_seqlens, rows,
+                     rows_per_seq, topk, s_kv, max_blocks_per_seq, row_len);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+extern "C" const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }

@@ -1,0 +1,118 @@
+"""The C-ABI library: it loads, exports every function include/sparse_mla.h
+declares, and rejects bad arguments on the host before anything is launched
+(CPU only: every call here returns before touching the GPU)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "sparse_mla.h"
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_mla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_top_mla_amd import _binding, build
+    if not _binding.LIBRARY.exists():
+        build.build()
+    return _binding.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["sparse_mla_decode_fwd", "sparse_mla_fwd",
+                                     "sparse_mla_last_error", "sparse_mla_row_lengths"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import sparse_top_mla_amd
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(sparse_top_mla_amd.EXPORTS) == set(_declared_functions())
+
+
+def test_library_holds_gfx950_code_only():
+    from sparse_top_mla_amd import _binding
+    data = _binding.LIBRARY.read_bytes()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_90"):
+        assert other not in data
+
+
+NULL = None
+P = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, **kw):
+    a = dict(q=P, kv=P, indices=P, topk_length=NULL, attn_sink=NULL, s_q=4, s_kv=64, h_q=64,
+             h_kv=1, d_qk=576, d_v=512, topk=64, sm_scale=0.1, out=P, lse=P, max_logits=P,
+             stream=NULL)
+    a.update(kw)
+    return lib.sparse_mla_fwd(*a.values())
+
+
+def _dec(lib, **kw):
+    a = dict(q=P, kv_cache=P, block_table=P, cache_seqlens=P, indices=P, topk_length=NULL,
+             attn_sink=NULL, B=2, s_q=1, h_q=128, h_kv=1, d_qk=576, d_v=512, topk=64,
+             num_blocks=8, page_size=64, max_blocks_per_seq=4, sm_scale=0.1, out=P, lse=P,
+             max_logits=P, stream=NULL)
+    a.update(kw)
+    return lib.sparse_mla_decode_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), 1), (dict(kv=NULL), 1), (dict(indices=NULL), 1), (dict(out=NULL), 1),
+    (dict(kv=NULL, s_kv=-1), 2),
+    (dict(lse=NULL), 1), (dict(max_logits=NULL), 1),
+    (dict(s_q=-1), 2), (dict(s_kv=-1), 2), (dict(topk=0), 2), (dict(h_q=0), 2),
+    (dict(d_v=640), 2),
+    (dict(h_kv=2), 3), (dict(d_qk=128, d_v=128), 3), (dict(d_v=256), 3), (dict(h_q=24), 3),
+    (dict(h_q=144), 3),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.sparse_mla_last_error().decode()
+
+
+def test_fwd_empty_batch_is_noop(lib):
+    assert _fwd(lib, s_q=0) == 0
+    assert _fwd(lib, s_q=0, q=NULL, indices=NULL, out=NULL, lse=NULL, max_logits=NULL) == 0
+    assert lib.sparse_mla_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_table=NULL), 1), (dict(cache_seqlens=NULL), 1), (dict(kv_cache=NULL), 1),
+    (dict(B=-1), 2), (dict(s_q=0), 2), (dict(max_blocks_per_seq=0), 2), (dict(num_blocks=-1), 2),
+    (dict(page_size=32), 3), (dict(num_blocks=1 << 26), 3), (dict(d_qk=512, d_v=512, h_kv=3), 3),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _dec(lib, **kw) == status
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _dec(lib, B=0) == 0
+    assert _dec(lib, B=0, q=NULL, indices=NULL, out=NULL, block_table=NULL) == 0
+
+
+def test_row_lengths_rejects(lib):
+    f = lib.sparse_mla_row_lengths
+    assert f(NULL, NULL, NULL, 4, 1, 64, 10, 0, P, NULL) == 1
+    assert f(P, NULL, NULL, 4, 1, 0, 10, 0, P, NULL) == 2
+    assert f(P, NULL, P, 4, 1, 64, 10, 0, P, NULL) == 2
+    assert f(P, NULL, NULL, 0, 1, 64, 10, 0, P, NULL) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import sparse_top_mla_amd as smla
+    q = torch.zeros(2, 16, 576, dtype=torch.bfloat16)
+    kv = torch.zeros(8, 1, 576, dtype=torch.bfloat16)
+    idx = torch.zeros(2, 1, 64, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        smla.fwd(q, kv, idx, 0.1)

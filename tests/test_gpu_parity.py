@@ -1,0 +1,348 @@
+"""HIP path vs the fp64 CPU oracle, through the C ABI (GPU only).
+
+Tolerances are those of tests/parity.py (out max-abs 2e-2 and relative L2
+1e-2; lse and max_logits 1e-3 absolute; empty rows exact; row lengths
+bit-exact).  Bitwise GPU-vs-GPU checks cover the statements of the pages:
+derived == explicit length (FlashMLA PR #196, "Numbers"), INT_MAX-poisoned
+dynamic == -1-padded fixed (PR #216, "Dynamic top-k"), any invalid encoding
+masks alike, and NaN behind an unused index never leaks.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_top_mla_amd as smla
+from sparse_top_mla_amd import workloads as W
+from parity import assert_bitwise, assert_parity, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+INT32_MAX = 2**31 - 1
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _to(case_tensors):
+    return [None if t is None else t.to(DEV) for t in case_tensors]
+
+
+def run_prefill(c, topk_length="case", sink="case"):
+    tl = c.topk_length if topk_length == "case" else topk_length
+    sk = c.attn_sink if sink == "case" else sink
+    q, kv, idx, tl_d, sk_d = _to([c.q, c.kv, c.indices, tl, sk])
+    res = smla.fwd(q, kv, idx, c.sm_scale, c.d_v, attn_sink=sk_d, topk_length=tl_d)
+    torch.cuda.synchronize()
+    return res
+
+
+def run_decode(c, topk_length="case", indices=None, kv_cache=None):
+    tl = c.topk_length if topk_length == "case" else topk_length
+    idx = c.indices if indices is None else indices
+    kvc = c.kv_cache if kv_cache is None else kv_cache
+    q, kv, bt, cs, idx_d, tl_d, sk = _to([c.q, kvc, c.block_table, c.cache_seqlens, idx, tl,
+                                          c.attn_sink])
+    res = smla.decode_fwd(q, kv, bt, cs, idx_d, c.sm_scale, c.d_v, attn_sink=sk, topk_length=tl_d)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_prefill(c, rows=None, topk_length="case"):
+    tl = c.topk_length if topk_length == "case" else topk_length
+    return oracle.sparse_mla_fwd(c.q, c.kv, c.indices, c.sm_scale, c.d_v, attn_sink=c.attn_sink,
+                                 topk_length=tl, rows=rows)
+
+
+def oracle_decode(c, rows=None, topk_length="case"):
+    tl = c.topk_length if topk_length == "case" else topk_length
+    return oracle.sparse_mla_decode_fwd(c.q, c.kv_cache, c.block_table, c.cache_seqlens, c.indices,
+                                        c.sm_scale, c.d_v, attn_sink=c.attn_sink, topk_length=tl,
+                                        rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# small cases: every row checked
+# ---------------------------------------------------------------------------
+
+def test_tiny_prefill():
+    c = W.tiny_prefill()
+    _say(c.name)
+    assert_parity(run_prefill(c), oracle_prefill(c), c.name)
+
+
+@pytest.mark.parametrize("with_length", [False, True])
+def test_prefill_h64_ramp_window(with_length):
+    # rows 996..1043 and 0..23 of the 1027-capped causal ramp, width 1152
+    for off, n in ((996, 48), (0, 24)):
+        c = W.prefill_h64(with_length=with_length, s_q=n, s_kv=8192, row_offset=off)
+        _say(f"{c.name} rows {off}..{off + n - 1}")
+        assert_parity(run_prefill(c), oracle_prefill(c), c.name)
+
+
+def test_prefill_h128_scattered_sink():
+    c = W.make_prefill("h128_scatter_small", s_q=24, s_kv=4096, h_q=128, d_qk=576, d_v=512,
+                       topk=2048, layout="scattered", invalid_frac=0.1, empty_frac=0.125,
+                       with_sink=True, seed=3)
+    _say(c.name)
+    assert len(c.meta["empty_rows"]) == 3
+    assert_parity(run_prefill(c), oracle_prefill(c), c.name)
+
+
+@pytest.mark.parametrize("h_q", [16, 32, 48, 64, 80, 96, 112, 128])
+@pytest.mark.parametrize("d_qk", [512, 576])
+def test_prefill_head_counts(h_q, d_qk):
+    c = W.make_prefill(f"heads{h_q}_d{d_qk}", s_q=9, s_kv=300, h_q=h_q, d_qk=d_qk, d_v=512,
+                       topk=200, layout="scattered", invalid_frac=0.3, empty_frac=0.12,
+                       with_sink=(h_q % 32 == 0), seed=h_q + d_qk)
+    _say(c.name)
+    assert_parity(run_prefill(c), oracle_prefill(c), c.name)
+
+
+@pytest.mark.parametrize("topk", [1, 7, 63, 64, 65, 100, 129, 300])
+def test_prefill_ragged_topk(topk):
+    c = W.make_prefill(f"topk{topk}", s_q=11, s_kv=5000, h_q=64, d_qk=576, d_v=512, topk=topk,
+                       layout="scattered", invalid_frac=0.25, seed=topk)
+    _say(c.name)
+    assert_parity(run_prefill(c), oracle_prefill(c), c.name)
+    lens = torch.tensor(oracle.row_lengths(c.indices, s_kv=c.s_kv), dtype=torch.int32)
+    got = run_prefill(c, topk_length=lens)
+    assert_bitwise(run_prefill(c), got, f"{c.name} derived vs explicit")
+
+
+def _tail_rows(topk=192, s_kv=1000, seed=0):
+    """Rows whose last valid entry sits at each boundary length of FlashMLA
+    PR #216, "Correctness" (0, 1, 17, 63, 64, 65, 127, 128) and a few more,
+    with -1 interior holes."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = [0, 1, 17, 63, 64, 65, 127, 128, 129, 191, 192]
+    idx = torch.full((len(lens), topk), -1, dtype=torch.int64)
+    for r, n in enumerate(lens):
+        if n:
+            idx[r, :n] = torch.randint(0, s_kv, (n,), generator=gen)
+            holes = torch.rand(n, generator=gen) < 0.2
+            holes[n - 1] = False
+            idx[r, :n][holes] = -1
+    return lens, idx.to(torch.int32)
+
+
+@pytest.mark.parametrize("d_qk", [512, 576])
+def test_tail_lengths_and_bitwise_equivalences(d_qk):
+    lens, idx = _tail_rows()
+    n = len(lens)
+    c = W.make_prefill("tails", s_q=n, s_kv=1000, h_q=64, d_qk=d_qk, d_v=512, topk=192,
+                       layout="full", seed=9, with_sink=True)
+    c.indices = idx.view(n, 1, 192).contiguous()
+    c.topk_length = None
+    _say(f"tail lengths d{d_qk}")
+    base = run_prefill(c)
+    assert_parity(base, oracle_prefill(c), "tails derived")
+    # the kernel's row lengths are the oracle's, bit for bit
+    rl = smla.row_lengths(c.indices.to(DEV), s_kv=1000).cpu()
+    assert rl.tolist() == lens
+    assert rl.tolist() == oracle.row_lengths(c.indices, s_kv=1000).tolist()
+    # derived == explicit (bitwise)
+    explicit = torch.tensor(lens, dtype=torch.int32)
+    assert_bitwise(base, run_prefill(c, topk_length=explicit), "derived vs explicit")
+    # -1 padding without a length == INT_MAX poisoning with a length (bitwise)
+    poisoned = idx.clone()
+    for r, L in enumerate(lens):
+        poisoned[r, L:] = INT32_MAX
+    c2 = W.PrefillCase("tails_dyn", c.q, c.kv, poisoned.view(n, 1, 192).contiguous(), explicit,
+                       c.attn_sink, c.sm_scale, c.d_v)
+    assert_bitwise(base, run_prefill(c2), "fixed vs dynamic")
+    # any invalid encoding at the same positions (bitwise)
+    for enc in (-2, -(2**31), 1000, 1001, INT32_MAX):
+        alt = torch.where(idx < 0, torch.full_like(idx, enc), idx)
+        c3 = W.PrefillCase("enc", c.q, c.kv, alt.view(n, 1, 192).contiguous(), None, c.attn_sink,
+                           c.sm_scale, c.d_v)
+        assert_bitwise(base, run_prefill(c3), f"encoding {enc}")
+
+
+def test_nan_behind_unused_indices_never_leaks():
+    c = W.make_prefill("nan_guard", s_q=16, s_kv=2048, h_q=64, d_qk=576, d_v=512, topk=256,
+                       layout="scattered", invalid_frac=0.3, empty_frac=0.0, seed=17)
+    idx = c.indices.view(16, 256).clone()
+    used = torch.zeros(2048, dtype=torch.bool)
+    lens = torch.full((16,), 200, dtype=torch.int32)
+    for r in range(16):
+        row = idx[r, :200]
+        used[row[(row >= 0) & (row < 2048)].long()] = True
+    _say("nan guard")
+    base = run_prefill(c, topk_length=lens)
+    poisoned = c.kv.clone()
+    poisoned[~used] = float("nan")
+    c2 = W.PrefillCase("nan", c.q, poisoned, c.indices, lens, None, c.sm_scale, c.d_v)
+    got = run_prefill(c2, topk_length=lens)
+    assert_bitwise(base, got, "NaN in unused rows")
+    assert torch.isfinite(got[0].float()).all()
+
+
+def test_prefill_no_kv_rows():
+    c = W.make_prefill("s_kv0", s_q=5, s_kv=64, h_q=16, d_qk=576, d_v=512, topk=64,
+                       layout="full", seed=2)
+    kv0 = c.kv[:0]
+    out, lse, ml = smla.fwd(c.q.to(DEV), kv0.to(DEV).contiguous(), c.indices.to(DEV), c.sm_scale)
+    torch.cuda.synchronize()
+    assert (out == 0).all() and (lse == math.inf).all() and (ml == -math.inf).all()
+
+
+def test_empty_batch():
+    q = torch.zeros(0, 64, 512, dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros(10, 1, 512, dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros(0, 1, 64, dtype=torch.int32, device=DEV)
+    out, lse, ml = smla.fwd(q, kv, idx, 0.1)
+    assert out.shape == (0, 64, 512)
+
+
+def test_decode_dynamic_small():
+    c = W.decode_dynamic(with_length=True, batch=8)
+    _say(c.name)
+    dyn = run_decode(c)
+    assert_parity(dyn, oracle_decode(c), c.name)
+    fixed = W.decode_dynamic(with_length=False, batch=8)
+    assert_bitwise(dyn, run_decode(fixed), "decode fixed vs dynamic")
+    # [B]-shaped lengths broadcast over s_q
+    assert_bitwise(dyn, run_decode(c, topk_length=c.topk_length[:, 0].contiguous()), "[B] length")
+
+
+def test_decode_fixed_small():
+    c = W.decode_fixed(batch=4)
+    _say(c.name)
+    assert_parity(run_decode(c), oracle_decode(c), c.name)
+
+
+def test_decode_edge_tables():
+    """Cache lengths past the table's reach, bad page entries, short caches,
+    a sink and explicit lengths, against the oracle's reading of each."""
+    c = W.make_decode("decode_edges", batch=5, s_q=3, h_q=64, d_qk=576, d_v=512, topk=160,
+                      seqlens=torch.tensor([700, 64, 1, 333, 129]), seed=4, effective=1,
+                      with_sink=True, spare_pages=16)
+    # indices: mix of valid, invalid and out-of-range
+    gen = torch.Generator().manual_seed(11)
+    c.indices = torch.randint(-3, 800, c.indices.shape, generator=gen).to(torch.int32)
+    bt = c.block_table.clone()
+    bt[0, 3] = -1                      # a hole in the table
+    bt[3, 2] = c.kv_cache.shape[0]     # an entry past the pool
+    c.block_table = bt
+    cs = c.cache_seqlens.clone()
+    cs[4] = 100000                     # beyond max_blocks_per_seq * 64
+    c.cache_seqlens = cs
+    # request 4 now reaches past its old length: make its last page finite
+    kvc = c.kv_cache.clone()
+    kvc[int(bt[4, 2])] = torch.randn(kvc.shape[1:], generator=gen).to(torch.bfloat16)
+    c.kv_cache = kvc
+    _say(c.name)
+    assert_parity(run_decode(c), oracle_decode(c), c.name)
+    tl = torch.randint(-5, 200, (5, 3), generator=gen).to(torch.int32)
+    assert_parity(run_decode(c, topk_length=tl), oracle_decode(c, topk_length=tl), c.name + " len")
+    rl = smla.row_lengths(c.indices.to(DEV), None, c.cache_seqlens.to(DEV), rows_per_seq=3,
+                          max_blocks_per_seq=c.block_table.shape[1]).cpu().numpy()
+    ref = oracle.row_lengths(c.indices, None, c.cache_seqlens, rows_per_seq=3,
+                             addressable=c.block_table.shape[1] * 64)
+    assert np.array_equal(rl, ref)
+
+
+def test_decode_nan_pages_never_leak():
+    c = W.decode_fixed(batch=3, min_len=2100, max_len=5000)
+    _say("decode NaN guard")
+    base = run_decode(c)
+    # spare pages and tails are already NaN; additionally poison every token
+    # that no row names
+    kvc = c.kv_cache.clone().view(-1, 576)
+    used = torch.zeros(kvc.shape[0], dtype=torch.bool)
+    for b in range(c.batch):
+        pos = c.indices[b].reshape(-1).long()
+        pos = pos[(pos >= 0) & (pos < int(c.cache_seqlens[b]))]
+        phys = c.block_table[b].long()[pos // 64] * 64 + pos % 64
+        used[phys] = True
+    kvc[~used] = float("nan")
+    got = run_decode(c, kv_cache=kvc.view_as(c.kv_cache))
+    assert_bitwise(base, got, "decode NaN poisoning")
+
+
+def test_row_lengths_fixtures_on_gpu():
+    from oracle_pins import _golden_rows
+    for name, row, s_kv, explicit, exp_len, _ in _golden_rows():
+        idx = torch.from_numpy(row).view(1, -1).to(DEV)
+        tl = None if explicit is None else torch.tensor([explicit], dtype=torch.int32, device=DEV)
+        got = int(smla.row_lengths(idx, tl, s_kv=s_kv).item())
+        assert got == exp_len, name
+
+
+def test_row_lengths_random_bitexact():
+    gen = torch.Generator().manual_seed(1)
+    for topk in (1, 5, 64, 255, 256, 257, 700, 2048):
+        idx = torch.randint(-2, 60, (300, topk), generator=gen).to(torch.int32)
+        idx[::3, topk // 2:] = -1
+        idx[1::5, :] = INT32_MAX
+        got = smla.row_lengths(idx.to(DEV), s_kv=50).cpu().numpy()
+        assert np.array_equal(got, oracle.row_lengths(idx, s_kv=50)), topk
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times:
+# sampled rows against the oracle, properties on every row
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def h64_full():
+    c_nolen = W.prefill_h64(with_length=False)
+    c_len = W.prefill_h64(with_length=True)
+    assert torch.equal(c_nolen.indices, c_len.indices) and torch.equal(c_nolen.q, c_len.q)
+    return c_nolen, c_len
+
+
+def test_full_prefill_h64(h64_full):
+    c_nolen, c_len = h64_full
+    _say(c_nolen.name + " (full)")
+    a = run_prefill(c_nolen)
+    b = run_prefill(c_len)
+    assert_bitwise(a, b, "full h64: derived vs explicit length")
+    rows = sample_rows(c_nolen.s_q, 20, seed=0, must=(1, 63, 64, 1025, 1026, 1027, 4095))
+    assert_parity(a, oracle_prefill(c_nolen, rows=rows), c_nolen.name, rows=rows)
+    rl = smla.row_lengths(c_nolen.indices.to(DEV), s_kv=c_nolen.s_kv).cpu()
+    assert torch.equal(rl, c_len.topk_length)
+    assert torch.isfinite(a[1]).all() and torch.isfinite(a[0].float()).all()
+
+
+def test_full_prefill_h128():
+    c = W.prefill_h128()
+    _say(c.name + " (full)")
+    res = run_prefill(c)
+    empty = c.meta["empty_rows"]
+    rows = sample_rows(c.s_q, 14, seed=1, must=empty[:3])
+    assert_parity(res, oracle_prefill(c, rows=rows), c.name, rows=rows)
+    # every empty row of the workload is exact; every other row is finite
+    lse = res[1].cpu()
+    is_empty = torch.zeros(c.s_q, dtype=torch.bool)
+    is_empty[empty] = True
+    assert (lse[is_empty] == math.inf).all() and (res[0].cpu()[is_empty] == 0).all()
+    assert torch.isfinite(lse[~is_empty]).all()
+    rl = smla.row_lengths(c.indices.to(DEV), s_kv=c.s_kv).cpu().numpy()
+    assert np.array_equal(rl, oracle.row_lengths(c.indices, s_kv=c.s_kv))
+
+
+def test_full_decode_dynamic():
+    c = W.decode_dynamic(with_length=True)
+    _say(c.name + " (full)")
+    dyn = run_decode(c)
+    rows = sample_rows(c.batch, 12, seed=2)
+    assert_parity(dyn, oracle_decode(c, rows=rows), c.name, rows=rows)
+    fixed = W.decode_dynamic(with_length=False)
+    assert_bitwise(dyn, run_decode(fixed), "full decode: fixed vs dynamic")
+
+
+def test_full_decode_fixed():
+    c = W.decode_fixed()
+    _say(c.name + " (full)")
+    res = run_decode(c)
+    rows = sample_rows(c.batch * c.s_q, 12, seed=3)
+    assert_parity(res, oracle_decode(c, rows=rows), c.name, rows=rows)
+    assert torch.isfinite(res[0].float()).all() and torch.isfinite(res[1]).all()
