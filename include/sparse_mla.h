@@ -34,7 +34,8 @@
  *              thread-local text for the last non-OK status.
  *   Threading: stateless apart from the thread-local error text.
  *   Support:   h_kv = 1; d_qk in {512, 576}; d_v = 512; h_q a multiple of 16
- *              in [16, 128]; page_size = 64 for decode.
+ *              in [16, 128]; page_size = 64 for decode; sm_scale positive
+ *              and finite.
  */
 #ifndef SPARSE_MLA_H
 #define SPARSE_MLA_H

@@ -342,6 +342,478 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel: 32 heads per wave (h_q a multiple of 32).
+//
+// LDS read bandwidth (128 B/clk per CU), not the matrix cores, bounds the
+// 16-head kernel above: every wave re-reads the whole K and V block for 16
+// heads.  Here a wave owns 32 heads, so each K/V byte read from LDS feeds
+// twice the MFMA work (v_mfma_f32_32x32x16_bf16 with N = 32 heads), and LDS
+// time per block matches MFMA time.  One wave per SIMD: the 32-head O^T
+// accumulator (256 fp32 per lane) stays in AGPRs and is touched only by MFMA
+// inside the block loop; the query slice stays in VGPRs.
+//
+// Workgroup: G = h_q / 32 head groups x KS key splits (G * KS <= 4 waves).
+// With KS = 2 (h_q = 32, 64) the two waves of a head group take the lower and
+// upper 32 keys of every 64-key block and merge at the end of the row.
+//
+// Pipeline per 64-key block t (two LDS buffers; the loop is unrolled by two
+// so each half-iteration reads one buffer and fills the other):
+//   wait for block t's rows + barrier
+//   issue the gather of block t+1 (its rows are known since iteration t-1)
+//   issue the page lookups of block t+2 and the index loads of block t+3
+//   S^T, masked softmax, O^T += V^T P^T for block t
+//
+// Softmax reference: each head's exp2 reference is the max of its first
+// block with a valid key and then stays fixed, so O is never rescaled in the
+// loop.  A later logit more than 2^kRefSlack above the reference would
+// overflow that scheme; it flags the row, and the workgroup recomputes the
+// row once with the true row max as the reference.  P <= 2^kRefSlack is
+// representable in bf16 (fp32 exponent range) and the sums stay below 2^90.
+// max_logits is the true max.
+// ---------------------------------------------------------------------------
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr float kRefSlack = 64.0f;  // log2 units
+
+template <int D_QK>
+struct WideTile {
+  // LDS block layout: the first 512 columns ("nope" part, also V) of each of
+  // the 64 rows in 1 KiB rows, then the remaining d_qk - 512 columns ("rope"
+  // part) in 128 B rows.  16-byte chunks are XOR-swizzled within each row so
+  // that both MFMA operand reads are bank-conflict free: the K read (16 rows,
+  // one chunk column) and the transposed V read (4 rows, 4 adjacent chunks).
+  static constexpr int kRowBytes = D_QK * 2;
+  static constexpr int kNopeBytes = 1024;
+  static constexpr int kRopeBytes = kRowBytes - kNopeBytes;  // 0 or 128
+  static constexpr int kRopeBase = kBlockKeys * kNopeBytes;
+  static constexpr int kBufBytes = kBlockKeys * kRowBytes;
+  static constexpr int kDSteps = D_QK / 16;        // 32x32x16 K steps over d_qk
+  static constexpr int kRopeLanes = kRopeBytes / 16;
+  static_assert(kRopeBytes == 0 || kRopeBytes == 128, "d_qk");
+  static_assert(32 * kDV * 4 <= kBufBytes, "merge area");
+};
+
+// Chunk swizzles: nope rows permute the 16 chunks of each 256 B group by
+// r -> 4(r%4) + (r/4)%4; rope rows (8 chunks) by (r/2)%8.
+__device__ __forceinline__ int nope_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
+
+struct BlockMeta {
+  uint64_t mask;  // bit j: key j of the block is used
+  int phys;       // lane j: KV row of key j (prefill index or paged slot)
+};
+
+__device__ __forceinline__ int load_index(const int32_t* idx_row, int blk, int topk) {
+  const int pos = blk * kBlockKeys + lane_id();
+  return pos < topk ? idx_row[pos] : -1;
+}
+
+__device__ __forceinline__ bool index_ok(int idx, int blk, int L, int bound) {
+  const int pos = blk * kBlockKeys + lane_id();
+  return pos < L && idx >= 0 && idx < bound;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ int page_lookup(const FwdArgs& a, int seq, bool ok, int idx) {
+  if (!PAGED) return 0;
+  return ok ? a.block_table[(size_t)seq * a.mbps + (idx >> 6)] : -1;
+}
+
+template <bool PAGED>
+__device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int idx, int page) {
+  BlockMeta m;
+  int phys = idx;
+  if (PAGED) {
+    ok = ok && page >= 0 && page < a.num_blocks;
+    phys = page * kPage + (idx & (kPage - 1));
+  }
+  m.mask = __builtin_amdgcn_ballot_w64(ok);
+  m.phys = phys;
+  return m;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane L writes LDS bytes [ldst + 16L, ldst + 16L + 16).  Issued as inline
+// assembly: a direct-to-LDS load the compiler can see makes it wait for all
+// outstanding LDS reads (lgkmcnt(0)) before every LDS read while the load is
+// in flight, which would serialise the MFMA operand stream against the
+// prefetch of the next block.  Completion is tracked with the explicit
+// vmcnt(0) wait at the top of every pipeline step.  M0 needs one wait state
+// before the load reads it.
+__device__ __forceinline__ void dma16(const void* gptr, LDS_AS void* ldst) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(gptr)
+               : "memory", "m0");
+}
+
+template <int D_QK>
+__device__ __forceinline__ void stage_wide(LDS_AS uint8_t* buf, const uint8_t* kv, uint64_t mask,
+                                           int phys, int wave, int nwaves) {
+  using T = WideTile<D_QK>;
+  const int lane = lane_id();
+  // Zero-fill first: an LDS store issued after a direct-to-LDS load makes the
+  // compiler wait for that load.
+  for (int j = wave; j < kBlockKeys; j += nwaves) {
+    if (!((mask >> j) & 1ull)) {
+      *reinterpret_cast<LDS_AS u32x4*>(buf + j * T::kNopeBytes + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      if (T::kRopeLanes > 0 && lane < T::kRopeLanes)
+        *reinterpret_cast<LDS_AS u32x4*>(buf + T::kRopeBase + j * T::kRopeBytes + lane * 16) =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // Lane L of a row's load fills LDS chunk L, so it fetches source chunk
+  // L ^ swizzle(row).
+  for (int j = wave; j < kBlockKeys; j += nwaves) {
+    if ((mask >> j) & 1ull) {
+      const int r = __builtin_amdgcn_readlane(phys, j);
+      const uint8_t* src = kv + (size_t)(uint32_t)r * T::kRowBytes;
+      const int c = (lane & 48) | ((lane & 15) ^ nope_swz(j));
+      dma16(src + c * 16, buf + j * T::kNopeBytes);
+      if (T::kRopeLanes > 0 && lane < T::kRopeLanes)
+        dma16(src + T::kNopeBytes + ((lane ^ rope_swz(j)) * 16),
+              buf + T::kRopeBase + j * T::kRopeBytes);
+    }
+  }
+}
+
+// Running softmax state of one lane's head (log2 units); both halves of the
+// wave hold identical copies.
+struct SoftmaxState {
+  float m_ref;  // exp2 reference (fixed once set)
+  float l_sum;  // sum of exp2(s - m_ref)
+  float m_max;  // true max (max_logits)
+  bool overflow;
+};
+
+// Max / sum of a value over lanes l and l ^ 32 with v_permlane32_swap (VALU;
+// a ds_bpermute shuffle would queue behind outstanding LDS reads).  The swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, so with both operands holding x every lane ends up with its own
+// value and its partner's.  The second copy goes through an identity DPP
+// move: given one value twice, the compiler folds the pair into a single
+// copy and drops the partner.
+__device__ __forceinline__ uint2 pair32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const unsigned v = (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0xE4, 0xF, 0xF, false);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+  return uint2{r[0], r[1]};
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const uint2 r = pair32(x);
+  return fmaxf(__builtin_bit_cast(float, r.x), __builtin_bit_cast(float, r.y));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const uint2 r = pair32(x);
+  return __builtin_bit_cast(float, r.x) + __builtin_bit_cast(float, r.y);
+}
+
+// Hides a value from loop-invariant code motion: the per-lane LDS offsets
+// below are the same in every block, but their sums with the two buffer bases
+// would otherwise each be hoisted into a register of its own.
+__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
+
+// One 32-key tile for one wave: keys [r0, r0 + 32) of the block (r0 = koff +
+// 32kt), with validity bits `bits` (bit i <-> key r0 + i).
+template <int D_QK>
+__device__ __forceinline__ void wide_tile(const LDS_AS uint8_t* buf, uint32_t bits, int r0,
+                                          const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
+                                          f32x16 (&acc)[kDV / 32], SoftmaxState& st,
+                                          float scale_log2) {
+  using T = WideTile<D_QK>;
+  constexpr int kPrefetch = D_QK == 512 ? 5 : 4;
+  const int lane = lane_id();
+  const int hl = lane & 31, half = lane >> 5;
+
+  // S^T[key][head] = K Q^T.  Lane (half, hl) reads chunk 2d + half of key row
+  // r0 + hl; r0 is a multiple of 16, so the swizzle depends on hl only and a
+  // lane needs one base offset per value of d % 8 (plus 4 for the rope
+  // chunks); everything else is an immediate offset.  K fragments are read
+  // kPrefetch MFMAs ahead of their use.
+  // Chunk 2d + half of a row sits at chunk (2d ^ half ^ swz) of its 256 B
+  // group, so each address is a row base plus (32(d%8) ^ w) with one per-lane
+  // w; the rope part likewise with its own swizzle.
+  int krow = (r0 + hl) * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
+  int rrow = T::kRopeBase + (r0 + hl) * T::kRopeBytes, rw = (half ^ rope_swz(hl)) << 4;
+  opaque(krow);
+  opaque(kw);
+  opaque(rrow);
+  opaque(rw);
+  auto kaddr = [&](int d) {
+    if (d < 32) return buf + krow + (d >> 3) * 256 + ((32 * (d & 7)) ^ kw);
+    return buf + rrow + ((32 * (d - 32)) ^ rw);
+  };
+  f32x16 s = f32x16{};
+  bf16x8 kring[kPrefetch];
+#pragma unroll
+  for (int n = 0; n < kPrefetch; ++n) kring[n] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(n));
+#pragma unroll
+  for (int d = 0; d < T::kDSteps; ++d) {
+    const bf16x8 kf = kring[d % kPrefetch];
+    if (d + kPrefetch < T::kDSteps)
+      kring[d % kPrefetch] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(d + kPrefetch));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[d], s, 0, 0, 0);
+  }
+
+  // O^T[c][head] += V^T P^T; its operands are set up and its first reads
+  // issued before the softmax so their LDS latency overlaps it.  Lane
+  // (16-group grp, i16) reads 8 B of key row r0 + 16u + 4half + TR_ROW(i16)
+  // (+8 for the upper four keys) at value chunk 4ct + 2(grp&1) + TR_COL(i16)/2
+  // with ds_read_b64_tr_b16.  MFMA n covers value tile ct = n/2, step u = n%2.
+  const int i16 = lane & 15, cb = (lane >> 4) & 1;
+  const int vrow = r0 + 4 * half + TR_ROW(i16);
+  // Value chunk 4ct + vc of row vrow (+8) sits at chunk (4ct ^ vc ^ swz) of
+  // its 256 B group: a row base plus (64(ct%4) ^ w) with one w per row half.
+  const int vc = 2 * cb + (TR_COL(i16) >> 1);
+  int vrow_lo = vrow * T::kNopeBytes + 8 * (TR_COL(i16) & 1);
+  int vrow_hi = vrow_lo + 8 * T::kNopeBytes;
+  int vw_lo = (vc ^ nope_swz(vrow)) << 4, vw_hi = (vc ^ nope_swz(vrow + 8)) << 4;
+  opaque(vrow_lo);
+  opaque(vrow_hi);
+  opaque(vw_lo);
+  opaque(vw_hi);
+  constexpr int kNP = (kDV / 32) * 2;
+  auto vaddr = [&](int n, int hi) {
+    const int ct = n >> 1, u = n & 1;
+    return buf + (hi ? vrow_hi : vrow_lo) + (ct >> 2) * 256 + 16 * u * T::kNopeBytes +
+           ((64 * (ct & 3)) ^ (hi ? vw_hi : vw_lo));
+  };
+  bf16x4 vlo[kPrefetch], vhi[kPrefetch];
+#pragma unroll
+  for (int n = 0; n < kPrefetch; ++n) {
+    vlo[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, 0));
+    vhi[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, 1));
+  }
+  // Mask (lane holds keys 8(i/4) + 4half + i%4 of the tile) and softmax
+  // against the fixed reference.  The scale is positive, so the max is taken
+  // on the raw dot products and each probability is exp2(fma(s, scale, -m)).
+  // The masking stays branch-free: a branch here makes the scheduler
+  // serialise the LDS reads of the S loop above.
+  float rmax = -INFINITY;
+  {
+    const uint32_t mlane = bits >> (4 * half);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[i]);
+  rmax = pair_max32(rmax) * scale_log2;  // finite: the tile holds a valid key
+  st.m_max = fmaxf(st.m_max, rmax);
+  if (st.m_ref == -INFINITY) st.m_ref = rmax;
+  st.overflow |= rmax > st.m_ref + kRefSlack;  // this attempt is then discarded
+  const float neg_ref = -st.m_ref;
+  float rsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, neg_ref));
+    s[i] = p;
+    rsum += p;
+  }
+  st.l_sum += pair_sum32(rsum);
+
+  // P^T of 16-key step u: element e <-> key 16u + 8(e/4) + 4half + e%4,
+  // which is s[8u + e] of this lane.
+  bf16x8 pf[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[u][e] = (__bf16)s[8 * u + e];
+
+#pragma unroll
+  for (int n = 0; n < kNP; ++n) {
+    const bf16x4 lo = vlo[n % kPrefetch], hi = vhi[n % kPrefetch];
+    if (n + kPrefetch < kNP) {
+      vlo[n % kPrefetch] =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n + kPrefetch, 0));
+      vhi[n % kPrefetch] =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n + kPrefetch, 1));
+    }
+    const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    acc[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[n & 1], acc[n >> 1], 0, 0, 0);
+  }
+}
+
+// One 64-key block for one wave: its 32-key tiles in [koff, koff + 64/KS);
+// tiles without a valid key are skipped.
+template <int D_QK, int KS>
+__device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t mask, int koff,
+                                           const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
+                                           f32x16 (&acc)[kDV / 32], SoftmaxState& st,
+                                           float scale_log2) {
+#pragma unroll
+  for (int kt = 0; kt < kBlockKeys / KS / 32; ++kt) {
+    const int r0 = koff + 32 * kt;
+    const uint32_t bits = (uint32_t)(mask >> r0);
+    if (bits != 0u) wide_tile<D_QK>(buf, bits, r0, qf, acc, st, scale_log2);
+  }
+}
+
+template <int D_QK, int KS, bool PAGED>
+struct WidePipe {
+  using T = WideTile<D_QK>;
+  // One half-iteration: block t lives in `cur` (already gathered); gather
+  // block t+1 into `nxt`, look ahead for t+2 / t+3, then compute block t.
+  static __device__ __forceinline__ void step(const FwdArgs& a, const LDS_AS uint8_t* cur,
+                                              LDS_AS uint8_t* nxt, int t, int nblk, int L,
+                                              int bound, int seq, const int32_t* idx_row,
+                                              int wave, int nwaves, int koff,
+                                              uint64_t& mask_cur, BlockMeta& meta_nxt,
+                                              int& idx_nn, const bf16x8 (&qf)[T::kDSteps],
+                                              f32x16 (&acc)[kDV / 32], SoftmaxState& st) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < nblk) stage_wide<D_QK>(nxt, a.kv, meta_nxt.mask, meta_nxt.phys, wave, nwaves);
+    const bool ok_nn = index_ok(idx_nn, t + 2, L, bound);
+    const int page_nn = page_lookup<PAGED>(a, seq, ok_nn, idx_nn);
+    const int idx_nnn = load_index(idx_row, t + 3, a.topk);
+    const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
+    if (wmask != 0) wide_block<D_QK, KS>(cur, mask_cur, koff, qf, acc, st, a.scale_log2);
+    mask_cur = meta_nxt.mask;
+    meta_nxt = block_meta<PAGED>(a, ok_nn, idx_nn, page_nn);
+    idx_nn = idx_nnn;
+  }
+};
+
+template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sparse_mla_fwd_wide_kernel(FwdArgs a) {
+  using T = WideTile<D_QK>;
+  __shared__ __attribute__((aligned(16))) uint8_t buf0_raw[T::kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1_raw[T::kBufBytes];
+  LDS_AS uint8_t* buf0 = (LDS_AS uint8_t*)buf0_raw;
+  LDS_AS uint8_t* buf1 = (LDS_AS uint8_t*)buf1_raw;
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int G = nwaves / KS;
+  const int hg = wave % G, ks = wave / G;
+  const int hl = lane & 31, half = lane >> 5;
+  const int koff = ks * (kBlockKeys / KS);
+
+  // Heavy rows of a causal prefill come last; start them first.
+  const int row = PAGED ? (int)blockIdx.x : a.rows - 1 - (int)blockIdx.x;
+  const int seq = row / a.rows_per_seq;
+  const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
+  const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+
+  // Prologue: tail-scan round (or explicit length) and query slice; the
+  // length is resolved after the query loads are in flight.
+  TailRound first;
+  int tl = 0;
+  if (DYNAMIC)
+    tl = a.topk_length[row];
+  else
+    first = load_tail_round(idx_row, a.topk);
+  const int head = hg * 32 + hl;
+  const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * D_QK + half * 8;
+  bf16x8 qf[T::kDSteps];
+#pragma unroll
+  for (int d = 0; d < T::kDSteps; ++d) qf[d] = *reinterpret_cast<const bf16x8*>(qp + d * 16);
+  const int L = DYNAMIC ? clamp_length(tl, a.topk) : finish_tail_scan(first, idx_row, a.topk, bound);
+  const int nblk = (L + kBlockKeys - 1) / kBlockKeys;
+
+  f32x16 acc[kDV / 32];
+  SoftmaxState st;
+  float m_preset = -INFINITY;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+    for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
+    st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
+    if (nblk > 0) {
+      const int idx0 = load_index(idx_row, 0, a.topk);
+      const int idx1 = load_index(idx_row, 1, a.topk);
+      int idx_nn = load_index(idx_row, 2, a.topk);
+      const bool ok0 = index_ok(idx0, 0, L, bound);
+      const bool ok1 = index_ok(idx1, 1, L, bound);
+      const int pg0 = page_lookup<PAGED>(a, seq, ok0, idx0);
+      const int pg1 = page_lookup<PAGED>(a, seq, ok1, idx1);
+      const BlockMeta m0 = block_meta<PAGED>(a, ok0, idx0, pg0);
+      BlockMeta meta_nxt = block_meta<PAGED>(a, ok1, idx1, pg1);
+      uint64_t mask_cur = m0.mask;
+      __syncthreads();  // a previous attempt may still read the buffers
+      stage_wide<D_QK>(buf0, a.kv, m0.mask, m0.phys, wave, nwaves);
+      using P = WidePipe<D_QK, KS, PAGED>;
+      for (int t = 0; t < nblk; t += 2) {
+        P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, nwaves, koff, mask_cur,
+                meta_nxt, idx_nn, qf, acc, st);
+        if (t + 1 < nblk)
+          P::step(a, buf1, buf0, t + 1, nblk, L, bound, seq, idx_row, wave, nwaves, koff, mask_cur,
+                  meta_nxt, idx_nn, qf, acc, st);
+      }
+    }
+    // Workgroup-uniform: recompute once if any head outgrew its reference.
+    if (!__syncthreads_or(st.overflow) || attempt == 1) break;
+    m_preset = st.m_max;
+  }
+
+  // Combine, normalise, store.  acc[ct][i] = O[head][c = 32ct + 8(i/4) + 4half + i%4].
+  float m_fin = st.m_ref, l_fin = st.l_sum, mx_fin = st.m_max, a_self = 1.f;
+  LDS_AS float* part = (LDS_AS float*)(hg == 0 ? buf0 : buf1);
+  if (KS == 2) {
+    __shared__ float stats_raw[2 * 2 * 32 * 3];
+    LDS_AS float* sx = (LDS_AS float*)stats_raw + hg * (2 * 32 * 3);
+    __syncthreads();  // every wave is done with the block buffers
+    if (half == 0) {
+      sx[(ks * 32 + hl) * 3 + 0] = st.m_ref;
+      sx[(ks * 32 + hl) * 3 + 1] = st.l_sum;
+      sx[(ks * 32 + hl) * 3 + 2] = st.m_max;
+    }
+    __syncthreads();
+    const int other = (1 - ks) * 32 + hl;
+    const float mo = sx[other * 3 + 0], lo = sx[other * 3 + 1], xo = sx[other * 3 + 2];
+    const float m = fmaxf(st.m_ref, mo);
+    float a_other = 0.f;
+    a_self = 0.f;
+    if (m != -INFINITY) {
+      a_self = __builtin_amdgcn_exp2f(st.m_ref - m);
+      a_other = __builtin_amdgcn_exp2f(mo - m);
+    }
+    l_fin = a_self * st.l_sum + a_other * lo;
+    m_fin = m;
+    mx_fin = fmaxf(st.m_max, xo);
+  }
+  float scale = 0.f, lse_v = INFINITY, ml_v = -INFINITY;
+  if (l_fin > 0.f) {
+    float denom = l_fin;
+    if (SINK) denom += __builtin_amdgcn_exp2f(a.attn_sink[head] * kLog2e - m_fin);
+    scale = a_self / denom;
+    ml_v = mx_fin * kLn2;
+    lse_v = (m_fin + __log2f(l_fin)) * kLn2;
+  }
+  if (KS == 2) {
+    if (ks == 1) {
+#pragma unroll
+      for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<LDS_AS f32x4*>(part + ((ct * 4 + j) * 64 + lane) * 4) =
+              f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
+                    acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale};
+    }
+    __syncthreads();
+    if (ks == 1) return;
+  }
+  __bf16* op = a.out + ((size_t)row * a.h_q + head) * kDV + 4 * half;
+#pragma unroll
+  for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 v = {acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale, acc[ct][4 * j + 2] * scale,
+                 acc[ct][4 * j + 3] * scale};
+      if (KS == 2) v += *reinterpret_cast<const LDS_AS f32x4*>(part + ((ct * 4 + j) * 64 + lane) * 4);
+      const bf16x4 o4 = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      *reinterpret_cast<bf16x4*>(op + 32 * ct + 8 * j) = o4;
+    }
+  if (half == 0) {
+    a.lse[(size_t)row * a.h_q + head] = lse_v;
+    a.max_logits[(size_t)row * a.h_q + head] = ml_v;
+  }
+}
+
 // Row lengths from the same routines the attention kernels use; one wave per row.
 __global__ void __launch_bounds__(256) row_lengths_kernel(const int32_t* indices,
                                                           const int32_t* topk_length,
@@ -377,7 +849,10 @@ smla_status fail(smla_status s, const char* fmt, ...) {
   return s;
 }
 
-smla_status check_common(int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk) {
+smla_status check_common(int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+                         float sm_scale) {
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(SMLA_ERR_UNSUPPORTED, "sm_scale=%g (must be positive and finite)", (double)sm_scale);
   if (h_q <= 0 || topk <= 0 || d_qk <= 0 || d_v <= 0)
     return fail(SMLA_ERR_BAD_SHAPE, "non-positive size (h_q=%d topk=%d d_qk=%d d_v=%d)", h_q, topk,
                 d_qk, d_v);
@@ -403,8 +878,48 @@ smla_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   return SMLA_OK;
 }
 
+template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
+smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
+  const int nwaves = (args.h_q / 32) * KS;
+  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, KS, PAGED, DYNAMIC, SINK>), dim3(args.rows),
+                     dim3(nwaves * 64), 0, stream, args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+template <bool PAGED>
+smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
+  const int ks = args.h_q / 32 <= 2 ? 2 : 1;
+  const bool dyn = args.topk_length != nullptr;
+  const bool sink = args.attn_sink != nullptr;
+  args.head_groups = 1;
+#define SMLA_WIDE(D, K, DYN, SNK)                                        \
+  if (d_qk == D && ks == K && dyn == DYN && sink == SNK)                 \
+    return launch_wide<D, K, PAGED, DYN, SNK>(args, stream);
+  SMLA_WIDE(512, 1, false, false)
+  SMLA_WIDE(512, 1, false, true)
+  SMLA_WIDE(512, 1, true, false)
+  SMLA_WIDE(512, 1, true, true)
+  SMLA_WIDE(512, 2, false, false)
+  SMLA_WIDE(512, 2, false, true)
+  SMLA_WIDE(512, 2, true, false)
+  SMLA_WIDE(512, 2, true, true)
+  SMLA_WIDE(576, 1, false, false)
+  SMLA_WIDE(576, 1, false, true)
+  SMLA_WIDE(576, 1, true, false)
+  SMLA_WIDE(576, 1, true, true)
+  SMLA_WIDE(576, 2, false, false)
+  SMLA_WIDE(576, 2, false, true)
+  SMLA_WIDE(576, 2, true, false)
+  SMLA_WIDE(576, 2, true, true)
+#undef SMLA_WIDE
+  return fail(SMLA_ERR_UNSUPPORTED, "no wide kernel instance for d_qk=%d", d_qk);
+}
+
 template <bool PAGED>
 smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
+  if (args.h_q % 32 == 0) return dispatch_wide<PAGED>(d_qk, args, stream);
   const int waves_total = args.h_q / kHeadsPerWave;
   args.head_groups = (waves_total > 4 && waves_total % 2 == 0) ? 2 : 1;
   const bool dyn = args.topk_length != nullptr;
@@ -433,7 +948,7 @@ extern "C" smla_status sparse_mla_fwd(const void* q, const void* kv, const int32
                                       smla_stream_t stream) {
   g_last_error.clear();
   if (s_q < 0 || s_kv < 0) return fail(SMLA_ERR_BAD_SHAPE, "negative s_q=%d or s_kv=%d", s_q, s_kv);
-  smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk);
+  smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk, sm_scale);
   if (st != SMLA_OK) return st;
   if (s_q == 0) return SMLA_OK;
   if (!q || (!kv && s_kv > 0) || !indices || !out || !lse || !max_logits)
@@ -467,7 +982,7 @@ extern "C" smla_status sparse_mla_decode_fwd(
   if (B < 0 || s_q <= 0 || num_blocks < 0 || max_blocks_per_seq <= 0)
     return fail(SMLA_ERR_BAD_SHAPE, "bad sizes (B=%d s_q=%d num_blocks=%d max_blocks_per_seq=%d)",
                 B, s_q, num_blocks, max_blocks_per_seq);
-  smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk);
+  smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk, sm_scale);
   if (st != SMLA_OK) return st;
   if (page_size != kPage) return fail(SMLA_ERR_UNSUPPORTED, "page_size=%d (supported: 64)", page_size);
   if ((long long)num_blocks * kPage > 0x7fffffffLL)

@@ -73,7 +73,8 @@ def _dec(lib, **kw):
     (dict(s_q=-1), 2), (dict(s_kv=-1), 2), (dict(topk=0), 2), (dict(h_q=0), 2),
     (dict(d_v=640), 2),
     (dict(h_kv=2), 3), (dict(d_qk=128, d_v=128), 3), (dict(d_v=256), 3), (dict(h_q=24), 3),
-    (dict(h_q=144), 3),
+    (dict(h_q=144), 3), (dict(sm_scale=0.0), 3), (dict(sm_scale=-0.5), 3),
+    (dict(sm_scale=float("inf")), 3), (dict(sm_scale=float("nan")), 3),
 ])
 def test_fwd_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
@@ -90,6 +91,7 @@ def test_fwd_empty_batch_is_noop(lib):
     (dict(block_table=NULL), 1), (dict(cache_seqlens=NULL), 1), (dict(kv_cache=NULL), 1),
     (dict(B=-1), 2), (dict(s_q=0), 2), (dict(max_blocks_per_seq=0), 2), (dict(num_blocks=-1), 2),
     (dict(page_size=32), 3), (dict(num_blocks=1 << 26), 3), (dict(d_qk=512, d_v=512, h_kv=3), 3),
+    (dict(sm_scale=-1.0), 3),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _dec(lib, **kw) == status
