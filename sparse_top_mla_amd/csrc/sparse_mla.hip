@@ -360,9 +360,12 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
 // Pipeline per 64-key block t (two LDS buffers; the loop is unrolled by two
 // so each half-iteration reads one buffer and fills the other):
 //   wait for block t's rows + barrier
-//   issue the gather of block t+1 (its rows are known since iteration t-1)
+//   rows of block t+1 from the index and page loaded one step earlier; its
+//   rope part is copied at once
 //   issue the page lookups of block t+2 and the index loads of block t+3
-//   S^T, masked softmax, O^T += V^T P^T for block t
+//   S^T, masked softmax, O^T += V^T P^T for block t, with the copies of
+//   block t+1's 1 KiB rows issued one at a time between the MFMAs (a wave
+//   that issues many copies at once stalls until the memory pipeline drains)
 //
 // Softmax reference: each head's exp2 reference is the max of its first
 // block with a valid key and then stays fixed, so O is never rescaled in the
@@ -433,14 +436,16 @@ __device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int i
   return m;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane L writes LDS bytes [ldst + 16L, ldst + 16L + 16).  Issued as inline
-// assembly: a direct-to-LDS load the compiler can see makes it wait for all
-// outstanding LDS reads (lgkmcnt(0)) before every LDS read while the load is
-// in flight, which would serialise the MFMA operand stream against the
-// prefetch of the next block.  Completion is tracked with the explicit
-// vmcnt(0) wait at the top of every pipeline step.  M0 needs one wait state
-// before the load reads it.
+// The gather copies KV rows global -> LDS directly (no VGPR round trip).
+// Both forms are inline assembly: a direct-to-LDS load the compiler can see
+// makes it wait for all outstanding LDS reads (lgkmcnt(0)) before every LDS
+// read while the load is in flight, which would serialise the MFMA operand
+// stream the loads are interleaved with.  Completion is tracked with the
+// explicit vmcnt(0) wait at the top of every pipeline step.  M0 (the LDS
+// destination) needs one wait state before the load reads it.  Lane L writes
+// LDS bytes [M0 + 16L, M0 + 16L + 16).
+
+// global_load_lds_dwordx4: one 64-bit source address per lane.
 __device__ __forceinline__ void dma16(const void* gptr, LDS_AS void* ldst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -449,35 +454,83 @@ __device__ __forceinline__ void dma16(const void* gptr, LDS_AS void* ldst) {
                : "memory", "m0");
 }
 
+// buffer_load_dwordx4 ... lds through a buffer resource of `bytes` bytes at
+// `base` (raw, stride 0); lane L reads base + voff.  Offsets outside the
+// resource read nothing and write zeros to LDS, so bytes = 0 zero-fills the
+// destination without touching memory and without a branch or an EXEC change
+// inside the MFMA stream.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void dma_rsrc16(const void* base, uint32_t bytes, uint32_t voff,
+                                           LDS_AS void* ldst) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  u32x4s rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;  // stride 0
+  rs[2] = __builtin_amdgcn_readfirstlane(bytes);
+  rs[3] = 0x00020000u;  // 32-bit data format, no swizzle
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+
+// Source of the rope chunks of masked rows (zeros; 8 lanes x 16 B).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_rope[128];
+
+// Rope part (d_qk = 576) of a block: 8 rows of 128 B per load, wave w taking
+// row groups w, w+nw, ...  Lane L handles row 8g + L/8, LDS chunk L%8, which
+// holds source chunk (L%8) ^ swizzle(row); masked rows read zeros.
 template <int D_QK>
-__device__ __forceinline__ void stage_wide(LDS_AS uint8_t* buf, const uint8_t* kv, uint64_t mask,
+__device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const uint8_t* kv, uint64_t mask,
                                            int phys, int wave, int nwaves) {
   using T = WideTile<D_QK>;
+  if (T::kRopeLanes == 0) return;
   const int lane = lane_id();
-  // Zero-fill first: an LDS store issued after a direct-to-LDS load makes the
-  // compiler wait for that load.
-  for (int j = wave; j < kBlockKeys; j += nwaves) {
-    if (!((mask >> j) & 1ull)) {
-      *reinterpret_cast<LDS_AS u32x4*>(buf + j * T::kNopeBytes + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-      if (T::kRopeLanes > 0 && lane < T::kRopeLanes)
-        *reinterpret_cast<LDS_AS u32x4*>(buf + T::kRopeBase + j * T::kRopeBytes + lane * 16) =
-            u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // Lane L of a row's load fills LDS chunk L, so it fetches source chunk
-  // L ^ swizzle(row).
-  for (int j = wave; j < kBlockKeys; j += nwaves) {
-    if ((mask >> j) & 1ull) {
-      const int r = __builtin_amdgcn_readlane(phys, j);
-      const uint8_t* src = kv + (size_t)(uint32_t)r * T::kRowBytes;
-      const int c = (lane & 48) | ((lane & 15) ^ nope_swz(j));
-      dma16(src + c * 16, buf + j * T::kNopeBytes);
-      if (T::kRopeLanes > 0 && lane < T::kRopeLanes)
-        dma16(src + T::kNopeBytes + ((lane ^ rope_swz(j)) * 16),
-              buf + T::kRopeBase + j * T::kRopeBytes);
-    }
+  for (int g = wave; g < kBlockKeys / 8; g += nwaves) {
+    const int jj = 8 * g + (lane >> 3);
+    const int r = __shfl(phys, jj);
+    const int c = (lane & 7) ^ rope_swz(jj);
+    const uint8_t* src = ((mask >> jj) & 1ull)
+                             ? kv + (size_t)(uint32_t)r * T::kRowBytes + T::kNopeBytes + c * 16
+                             : g_zero_rope + (lane & 7) * 16;
+    dma16(src, buf + T::kRopeBase + g * 8 * T::kRopeBytes);
   }
 }
+
+// Nope part (the first 512 columns, also V) of a block, one 1 KiB row per
+// call, so that the copies can be spread over the MFMA work of the previous
+// block: the issuing wave stalls while the memory pipeline is full, and a
+// whole block issued at once would stall it for the full gather time.  Wave w
+// issues rows w, w+nw, ...; a masked row is zero-filled; calls past the last
+// row write zeros to a 1 KiB dummy area.  Lane L fills LDS chunk L of the
+// row, so it fetches source chunk L ^ swizzle(row).
+template <int D_QK>
+struct GatherPump {
+  using T = WideTile<D_QK>;
+  const uint8_t* kv;
+  LDS_AS uint8_t* buf;
+  LDS_AS uint8_t* dummy;
+  uint64_t mask;
+  int phys;    // lane j: KV row of key j
+  int next;    // next row to issue (>= 64: done); wave-uniform
+  int stride;  // waves per workgroup
+
+  __device__ __forceinline__ void pump() {
+    const int j = next & (kBlockKeys - 1);
+    const bool live = next < kBlockKeys;
+    const bool on = live && ((mask >> j) & 1ull);
+    const int lane = lane_id();
+    const int r = __builtin_amdgcn_readlane(phys, j);
+    const uint8_t* row = on ? kv + (size_t)(uint32_t)r * T::kRowBytes : kv;
+    const uint32_t voff = (uint32_t)(((lane & 48) | ((lane & 15) ^ nope_swz(j))) * 16);
+    dma_rsrc16(row, on ? T::kNopeBytes : 0u, voff, live ? buf + j * T::kNopeBytes : dummy);
+    next += stride;
+  }
+  __device__ __forceinline__ void finish() {
+    while (next < kBlockKeys) pump();
+  }
+};
 
 // Running softmax state of one lane's head (log2 units); both halves of the
 // wave hold identical copies.
@@ -515,26 +568,27 @@ __device__ __forceinline__ float pair_sum32(float x) {
 // would otherwise each be hoisted into a register of its own.
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
-// One 32-key tile for one wave: keys [r0, r0 + 32) of the block (r0 = koff +
-// 32kt), with validity bits `bits` (bit i <-> key r0 + i).
-template <int D_QK>
-__device__ __forceinline__ void wide_tile(const LDS_AS uint8_t* buf, uint32_t bits, int r0,
-                                          const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
-                                          f32x16 (&acc)[kDV / 32], SoftmaxState& st,
-                                          float scale_log2) {
+// A wave works on 32-key tiles: keys [r0, r0 + 32) of the block in LDS, with
+// validity bits `bits` (bit i <-> key r0 + i).  Every function below that
+// issues MFMAs calls `pump` (one row of the next block's gather) after every
+// EVERY-th of them.  In the S^T accumulator layout a lane holds keys
+// 8(i/4) + 4half + i%4 (i = 0..15) of the tile for its head hl.
+
+// S^T[key][head] = K Q^T of one tile.  Lane (half, hl) reads chunk 2d + half of key row r0 + hl; r0 is a multiple
+// of 16, so the swizzle depends on hl only and a lane needs one base offset
+// per value of d % 8 (plus 4 for the rope chunks); everything else is an
+// immediate offset.  Chunk 2d + half of a row sits at chunk (2d ^ half ^ swz)
+// of its 256 B group, so each address is a row base plus (32(d%8) ^ w) with
+// one per-lane w; the rope part likewise with its own swizzle.  K fragments
+// are read kPrefetch MFMAs ahead.
+template <int D_QK, int EVERY>
+__device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
+                                              const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
+                                              GatherPump<D_QK>& pump) {
   using T = WideTile<D_QK>;
-  constexpr int kPrefetch = D_QK == 512 ? 5 : 4;
+  constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
   const int lane = lane_id();
   const int hl = lane & 31, half = lane >> 5;
-
-  // S^T[key][head] = K Q^T.  Lane (half, hl) reads chunk 2d + half of key row
-  // r0 + hl; r0 is a multiple of 16, so the swizzle depends on hl only and a
-  // lane needs one base offset per value of d % 8 (plus 4 for the rope
-  // chunks); everything else is an immediate offset.  K fragments are read
-  // kPrefetch MFMAs ahead of their use.
-  // Chunk 2d + half of a row sits at chunk (2d ^ half ^ swz) of its 256 B
-  // group, so each address is a row base plus (32(d%8) ^ w) with one per-lane
-  // w; the rope part likewise with its own swizzle.
   int krow = (r0 + hl) * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
   int rrow = T::kRopeBase + (r0 + hl) * T::kRopeBytes, rw = (half ^ rope_swz(hl)) << 4;
   opaque(krow);
@@ -555,125 +609,176 @@ __device__ __forceinline__ void wide_tile(const LDS_AS uint8_t* buf, uint32_t bi
     if (d + kPrefetch < T::kDSteps)
       kring[d % kPrefetch] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(d + kPrefetch));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[d], s, 0, 0, 0);
+    if (d % EVERY == EVERY - 1) pump.pump();
+    __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
   }
+  return s;
+}
 
-  // O^T[c][head] += V^T P^T; its operands are set up and its first reads
-  // issued before the softmax so their LDS latency overlaps it.  Lane
-  // (16-group grp, i16) reads 8 B of key row r0 + 16u + 4half + TR_ROW(i16)
-  // (+8 for the upper four keys) at value chunk 4ct + 2(grp&1) + TR_COL(i16)/2
-  // with ds_read_b64_tr_b16.  MFMA n covers value tile ct = n/2, step u = n%2.
-  const int i16 = lane & 15, cb = (lane >> 4) & 1;
-  const int vrow = r0 + 4 * half + TR_ROW(i16);
-  // Value chunk 4ct + vc of row vrow (+8) sits at chunk (4ct ^ vc ^ swz) of
-  // its 256 B group: a row base plus (64(ct%4) ^ w) with one w per row half.
-  const int vc = 2 * cb + (TR_COL(i16) >> 1);
-  int vrow_lo = vrow * T::kNopeBytes + 8 * (TR_COL(i16) & 1);
-  int vrow_hi = vrow_lo + 8 * T::kNopeBytes;
-  int vw_lo = (vc ^ nope_swz(vrow)) << 4, vw_hi = (vc ^ nope_swz(vrow + 8)) << 4;
-  opaque(vrow_lo);
-  opaque(vrow_hi);
-  opaque(vw_lo);
-  opaque(vw_hi);
-  constexpr int kNP = (kDV / 32) * 2;
-  auto vaddr = [&](int n, int hi) {
-    const int ct = n >> 1, u = n & 1;
-    return buf + (hi ? vrow_hi : vrow_lo) + (ct >> 2) * 256 + 16 * u * T::kNopeBytes +
-           ((64 * (ct & 3)) ^ (hi ? vw_hi : vw_lo));
-  };
-  bf16x4 vlo[kPrefetch], vhi[kPrefetch];
-#pragma unroll
-  for (int n = 0; n < kPrefetch; ++n) {
-    vlo[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, 0));
-    vhi[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, 1));
-  }
-  // Mask (lane holds keys 8(i/4) + 4half + i%4 of the tile) and softmax
-  // against the fixed reference.  The scale is positive, so the max is taken
-  // on the raw dot products and each probability is exp2(fma(s, scale, -m)).
-  // The masking stays branch-free: a branch here makes the scheduler
-  // serialise the LDS reads of the S loop above.
-  float rmax = -INFINITY;
+// Masks the tile (masked logits become -inf) and takes its row max against
+// the softmax state; returns the exp2 offset -m_ref (0 while no reference is
+// set, when every logit seen is -inf).  The scale is positive, so the max is
+// taken on the raw dot products and each probability is
+// exp2(fma(s, scale, -m_ref)).  Branch-free: a branch here would split the
+// MFMA streams this code is scheduled into.
+__device__ __forceinline__ float tile_max(f32x16& s, uint32_t bits, SoftmaxState& st,
+                                          float scale_log2) {
   {
-    const uint32_t mlane = bits >> (4 * half);
+    const uint32_t mlane = bits >> (4 * (lane_id() >> 5));
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
   }
+  float rmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[i]);
-  rmax = pair_max32(rmax) * scale_log2;  // finite: the tile holds a valid key
+  rmax = pair_max32(rmax) * scale_log2;  // -inf only for a tile without a valid key
   st.m_max = fmaxf(st.m_max, rmax);
   if (st.m_ref == -INFINITY) st.m_ref = rmax;
   st.overflow |= rmax > st.m_ref + kRefSlack;  // this attempt is then discarded
-  const float neg_ref = -st.m_ref;
-  float rsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, neg_ref));
-    s[i] = p;
-    rsum += p;
-  }
-  st.l_sum += pair_sum32(rsum);
-
-  // P^T of 16-key step u: element e <-> key 16u + 8(e/4) + 4half + e%4,
-  // which is s[8u + e] of this lane.
-  bf16x8 pf[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf[u][e] = (__bf16)s[8 * u + e];
-
-#pragma unroll
-  for (int n = 0; n < kNP; ++n) {
-    const bf16x4 lo = vlo[n % kPrefetch], hi = vhi[n % kPrefetch];
-    if (n + kPrefetch < kNP) {
-      vlo[n % kPrefetch] =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n + kPrefetch, 0));
-      vhi[n % kPrefetch] =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n + kPrefetch, 1));
-    }
-    const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    acc[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[n & 1], acc[n >> 1], 0, 0, 0);
-  }
+  return st.m_ref == -INFINITY ? 0.f : -st.m_ref;
 }
 
-// One 64-key block for one wave: its 32-key tiles in [koff, koff + 64/KS);
-// tiles without a valid key are skipped.
-template <int D_QK, int KS>
+// Probability of logit s (log2 units after scaling) against the reference.
+__device__ __forceinline__ float prob(float s, float neg_ref, float scale_log2) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(s, scale_log2, neg_ref));
+}
+
+// O^T[c][head] += V^T P^T of one tile, key step u = 0 for every value tile
+// first, so that the probabilities of step 1 are computed under the MFMAs of
+// step 0.  The P^T operand of step u holds, as element e, key
+// 16u + 8(e/4) + 4half + e%4, which is s[8u + e] of this lane.  Lane (16-group grp, i16) reads 8 B of key row r0 + 16u + 4half +
+// TR_ROW(i16) (+8 for the upper four keys) at value chunk 4ct + 2(grp&1) +
+// TR_COL(i16)/2 with ds_read_b64_tr_b16.  Value chunk 4ct + vc of row vrow
+// (+8) sits at chunk (4ct ^ vc ^ swz) of its 256 B group: a row base plus
+// (64(ct%4) ^ w) with one w per row half.  MFMA n covers value tile
+// ct = n % 16, step u = n / 16.
+template <int D_QK, int EVERY>
+__device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r0, f32x16 s,
+                                                uint32_t bits,
+                                                f32x16 (&acc)[kDV / 32], SoftmaxState& st,
+                                                float scale_log2, GatherPump<D_QK>& pump) {
+  using T = WideTile<D_QK>;
+  constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
+  constexpr int kTiles = kDV / 32;
+  const int lane = lane_id();
+  const int i16 = lane & 15, cb = (lane >> 4) & 1, half = lane >> 5;
+  const int vrow = r0 + 4 * half + TR_ROW(i16);
+  const int vc = 2 * cb + (TR_COL(i16) >> 1);
+  int row_lo = vrow * T::kNopeBytes + 8 * (TR_COL(i16) & 1);
+  int row_hi = row_lo + 8 * T::kNopeBytes;
+  int w_lo = (vc ^ nope_swz(vrow)) << 4, w_hi = (vc ^ nope_swz(vrow + 8)) << 4;
+  opaque(row_lo);
+  opaque(row_hi);
+  opaque(w_lo);
+  opaque(w_hi);
+  auto vaddr = [&](int n, bool upper) {
+    const int ct = n % kTiles, u = n / kTiles;
+    return buf + (upper ? row_hi : row_lo) + (ct >> 2) * 256 + 16 * u * T::kNopeBytes +
+           ((64 * (ct & 3)) ^ (upper ? w_hi : w_lo));
+  };
+  bf16x4 lo[kPrefetch], hi[kPrefetch];
+#pragma unroll
+  for (int n = 0; n < kPrefetch; ++n) {
+    lo[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, false));
+    hi[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, true));
+  }
+  const float neg_ref = tile_max(s, bits, st, scale_log2);
+  float rsum = 0.f;
+  bf16x8 pf[2];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = prob(s[e], neg_ref, scale_log2);
+    rsum += p;
+    pf[0][e] = (__bf16)p;
+  }
+  // Step 1's probabilities, two per MFMA of step 0 (sched barriers below keep
+  // them there).
+  float p1[8];
+#pragma unroll
+  for (int n = 0; n < 2 * kTiles; ++n) {
+    const bf16x4 l = lo[n % kPrefetch], h = hi[n % kPrefetch];
+    if (n + kPrefetch < 2 * kTiles) {
+      lo[n % kPrefetch] =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n + kPrefetch, false));
+      hi[n % kPrefetch] =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n + kPrefetch, true));
+    }
+    const bf16x8 vf = {l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+    acc[n % kTiles] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[n / kTiles], acc[n % kTiles], 0, 0, 0);
+    if (n < 4) {
+      p1[2 * n] = prob(s[8 + 2 * n], neg_ref, scale_log2);
+      p1[2 * n + 1] = prob(s[9 + 2 * n], neg_ref, scale_log2);
+    } else if (n == 4) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rsum += p1[e];
+        pf[1][e] = (__bf16)p1[e];
+      }
+    }
+    if (n % EVERY == EVERY - 1) pump.pump();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l_sum += pair_sum32(rsum);
+}
+
+// One 64-key block with a valid key for one wave: its 32-key tiles in
+// [koff, koff + 64/KS); tiles without a valid key are skipped.
+template <int D_QK, int KS, int EVERY>
 __device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t mask, int koff,
                                            const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                            f32x16 (&acc)[kDV / 32], SoftmaxState& st,
-                                           float scale_log2) {
+                                           float scale_log2, GatherPump<D_QK>& pump) {
 #pragma unroll
   for (int kt = 0; kt < kBlockKeys / KS / 32; ++kt) {
     const int r0 = koff + 32 * kt;
     const uint32_t bits = (uint32_t)(mask >> r0);
-    if (bits != 0u) wide_tile<D_QK>(buf, bits, r0, qf, acc, st, scale_log2);
+    if (bits != 0u) {
+      const f32x16 s = tile_scores<D_QK, EVERY>(buf, r0, qf, pump);
+      tile_softmax_pv<D_QK, EVERY>(buf, r0, s, bits, acc, st, scale_log2, pump);
+    }
   }
 }
+
+// Look-ahead state of the pipeline at the top of step t: index and page of
+// block t+1, index of block t+2.  Every load is consumed only after the next
+// step's vmcnt(0) wait, so no wait inside a step covers the gather loads.
+struct Ahead {
+  int idx1, page1, idx2;
+};
 
 template <int D_QK, int KS, bool PAGED>
 struct WidePipe {
   using T = WideTile<D_QK>;
+  // One gather row per this many MFMAs: 16 rows per wave and block against
+  // 64 (KS = 2) or 136 (KS = 1, d_qk = 576) MFMAs per wave and block.
+  static constexpr int kEvery = KS == 2 ? 4 : 8;
   // One half-iteration: block t lives in `cur` (already gathered); gather
-  // block t+1 into `nxt`, look ahead for t+2 / t+3, then compute block t.
+  // block t+1 into `nxt` while computing block t.
   static __device__ __forceinline__ void step(const FwdArgs& a, const LDS_AS uint8_t* cur,
                                               LDS_AS uint8_t* nxt, int t, int nblk, int L,
                                               int bound, int seq, const int32_t* idx_row,
-                                              int wave, int nwaves, int koff,
-                                              uint64_t& mask_cur, BlockMeta& meta_nxt,
-                                              int& idx_nn, const bf16x8 (&qf)[T::kDSteps],
+                                              LDS_AS uint8_t* dummy, int wave, int nwaves,
+                                              int koff, uint64_t& mask_cur, Ahead& ah,
+                                              const bf16x8 (&qf)[T::kDSteps],
                                               f32x16 (&acc)[kDV / 32], SoftmaxState& st) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < nblk) stage_wide<D_QK>(nxt, a.kv, meta_nxt.mask, meta_nxt.phys, wave, nwaves);
-    const bool ok_nn = index_ok(idx_nn, t + 2, L, bound);
-    const int page_nn = page_lookup<PAGED>(a, seq, ok_nn, idx_nn);
-    const int idx_nnn = load_index(idx_row, t + 3, a.topk);
+    const bool have_nxt = t + 1 < nblk;
+    const BlockMeta mn =
+        block_meta<PAGED>(a, index_ok(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
+    if (have_nxt) stage_rope<D_QK>(nxt, a.kv, mn.mask, mn.phys, wave, nwaves);
+    const bool ok2 = index_ok(ah.idx2, t + 2, L, bound);
+    const int page2 = page_lookup<PAGED>(a, seq, ok2, ah.idx2);
+    const int idx3 = load_index(idx_row, t + 3, a.topk);
+    GatherPump<D_QK> pump{a.kv, nxt, dummy, mn.mask, mn.phys, have_nxt ? wave : kBlockKeys, nwaves};
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
-    if (wmask != 0) wide_block<D_QK, KS>(cur, mask_cur, koff, qf, acc, st, a.scale_log2);
-    mask_cur = meta_nxt.mask;
-    meta_nxt = block_meta<PAGED>(a, ok_nn, idx_nn, page_nn);
-    idx_nn = idx_nnn;
+    if (wmask != 0)
+      wide_block<D_QK, KS, kEvery>(cur, mask_cur, koff, qf, acc, st, a.scale_log2, pump);
+    pump.finish();
+    mask_cur = mn.mask;
+    ah = Ahead{ah.idx2, page2, idx3};
   }
 };
 
@@ -683,8 +788,10 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   using T = WideTile<D_QK>;
   __shared__ __attribute__((aligned(16))) uint8_t buf0_raw[T::kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1_raw[T::kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t dummy_raw[T::kNopeBytes];
   LDS_AS uint8_t* buf0 = (LDS_AS uint8_t*)buf0_raw;
   LDS_AS uint8_t* buf1 = (LDS_AS uint8_t*)buf1_raw;
+  LDS_AS uint8_t* dummy = (LDS_AS uint8_t*)dummy_raw;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -726,23 +833,24 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     if (nblk > 0) {
       const int idx0 = load_index(idx_row, 0, a.topk);
       const int idx1 = load_index(idx_row, 1, a.topk);
-      int idx_nn = load_index(idx_row, 2, a.topk);
+      const int idx2 = load_index(idx_row, 2, a.topk);
       const bool ok0 = index_ok(idx0, 0, L, bound);
       const bool ok1 = index_ok(idx1, 1, L, bound);
       const int pg0 = page_lookup<PAGED>(a, seq, ok0, idx0);
       const int pg1 = page_lookup<PAGED>(a, seq, ok1, idx1);
       const BlockMeta m0 = block_meta<PAGED>(a, ok0, idx0, pg0);
-      BlockMeta meta_nxt = block_meta<PAGED>(a, ok1, idx1, pg1);
       uint64_t mask_cur = m0.mask;
+      Ahead ah{idx1, pg1, idx2};
       __syncthreads();  // a previous attempt may still read the buffers
-      stage_wide<D_QK>(buf0, a.kv, m0.mask, m0.phys, wave, nwaves);
+      stage_rope<D_QK>(buf0, a.kv, m0.mask, m0.phys, wave, nwaves);
+      GatherPump<D_QK>{a.kv, buf0, dummy, m0.mask, m0.phys, wave, nwaves}.finish();
       using P = WidePipe<D_QK, KS, PAGED>;
       for (int t = 0; t < nblk; t += 2) {
-        P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, nwaves, koff, mask_cur,
-                meta_nxt, idx_nn, qf, acc, st);
+        P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, dummy, wave, nwaves, koff,
+                mask_cur, ah, qf, acc, st);
         if (t + 1 < nblk)
-          P::step(a, buf1, buf0, t + 1, nblk, L, bound, seq, idx_row, wave, nwaves, koff, mask_cur,
-                  meta_nxt, idx_nn, qf, acc, st);
+          P::step(a, buf1, buf0, t + 1, nblk, L, bound, seq, idx_row, dummy, wave, nwaves, koff,
+                  mask_cur, ah, qf, acc, st);
       }
     }
     // Workgroup-uniform: recompute once if any head outgrew its reference.
