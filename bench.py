@@ -47,6 +47,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--ingest-counters", metavar="DIR",
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR (pmc_<workload>_<counter>/ "
+                         "and pmc_copy_<counter>/) into profiles/traffic_<workload>.json; no GPU needed")
     return ap.parse_args()
 
 
@@ -236,8 +239,14 @@ def cpu_baseline(case, counts, target_s):
 # ---------------------------------------------------------------------------
 
 def kernel_source_digest():
-    src = (ROOT / "sparse_top_mla_amd" / "csrc" / "sparse_mla.hip").read_bytes()
-    return hashlib.sha256(src).hexdigest()[:16]
+    """Digest of the kernel source without comments and blank lines, so that
+    stored counter figures stay attached to the code they were taken on."""
+    import re
+    src = (ROOT / "sparse_top_mla_amd" / "csrc" / "sparse_mla.hip").read_text()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def stored_traffic(workload):
@@ -262,6 +271,59 @@ def roofline(workload, case, counts, kernel_ms):
             "frac": achieved / PEAK_BF16_TFLOPS, "traffic": stored_traffic(workload)}
 
 
+def _counter_values(csv_path, kernel_substr):
+    """Counter values of the dispatches of the first kernel whose name holds
+    kernel_substr (the default prefill run also times a second variant)."""
+    import csv
+    vals, name = [], None
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if kernel_substr in r["Kernel_Name"]:
+                name = name or r["Kernel_Name"]
+                if r["Kernel_Name"] == name:
+                    vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def ingest_counters(d):
+    """HBM bytes per launch of the attention kernel from rocprofv3 counter runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the
+    same counter reads for a plain 1 GiB device copy (reads 1 GiB, writes
+    1 GiB); the factors are stored with the result."""
+    d = Path(d)
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = _counter_values(d / f"pmc_copy_{c}" / "run_counter_collection.csv", "copyBuffer")
+        if not v:
+            raise SystemExit(f"no copy kernel in pmc_copy_{c}")
+        cal[c] = (1 << 30) / (statistics.fmean(v) * 1024.0)
+    digest = kernel_source_digest()
+    for sub in sorted(d.glob("pmc_*_FETCH_SIZE")):
+        w = sub.name[len("pmc_"):-len("_FETCH_SIZE")]
+        if w == "copy":
+            continue
+        f = _counter_values(sub / "run_counter_collection.csv", "sparse_mla_fwd")
+        wr = _counter_values(d / f"pmc_{w}_WRITE_SIZE" / "run_counter_collection.csv", "sparse_mla_fwd")
+        if not f or not wr:
+            continue
+        fetch = statistics.fmean(f) * 1024.0 * cal["FETCH_SIZE"]
+        write = statistics.fmean(wr) * 1024.0 * cal["WRITE_SIZE"]
+        rec = {"workload": w, "hbm_bytes_per_launch": fetch + write,
+               "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+               "fetch_kib_raw_mean": statistics.fmean(f), "write_kib_raw_mean": statistics.fmean(wr),
+               "dispatches": [len(f), len(wr)],
+               "copy_calibration_factor": {"FETCH_SIZE": cal["FETCH_SIZE"], "WRITE_SIZE": cal["WRITE_SIZE"]},
+               "command": f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -o run --output-format csv -- "
+                          f"python3 -u bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0; "
+                          f"calibration: ... -- python3 -u bench.py --calibrate-copy",
+               "kernel_source_sha256_16": digest}
+        PROFILES.mkdir(exist_ok=True)
+        (PROFILES / f"traffic_{w}.json").write_text(json.dumps(rec, indent=1) + "\n")
+        print(f"{w}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch "
+              f"(fetch {fetch / 1e6:.1f}, write {write / 1e6:.1f})")
+
+
 def calibrate_copy():
     """A plain device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -276,6 +338,9 @@ def calibrate_copy():
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path; run with --gpus 1)", file=sys.stderr)

@@ -9,31 +9,30 @@
 // optional per-head sink joins the softmax denominator; a row without keys
 // gives out = 0, lse = +inf, max_logits = -inf.
 //
-// Kernel shape (one design for prefill and paged decode):
-//   * one workgroup per (query row, group of up to 64 heads); each wave owns 16
-//     heads.  With two head groups per row (h_q = 128) the two workgroups of
-//     a row get ids that are equal modulo 8, so round-robin dispatch puts
-//     both on the same XCD and the second gather of the row's KV hits that
-//     XCD's L2.
+// Two kernels share the index, validity, tail-scan and paging routines:
+//   * the wide kernel (h_q a multiple of 32, every benchmarked shape): one
+//     workgroup per query row, one wave per SIMD, 32 heads per wave on
+//     v_mfma_f32_32x32x16_bf16; see the block comment above it.
+//   * the 16-head kernel below (other multiples of 16): one workgroup per
+//     (query row, group of up to 64 heads), 16 heads per wave on
+//     v_mfma_f32_16x16x32_bf16.
+// Common to both:
 //   * the row's query slice stays in VGPRs for the whole row (B operand of
 //     S^T = K Q^T).
 //   * per 64-key block: the index vector is loaded one entry per lane and the
 //     validity of every key becomes a 64-bit wave ballot.  A block without a
 //     valid key is skipped outright (no gather, no MFMA): masked keys add
-//     exactly nothing to the online softmax, so skipping is exact.
-//   * valid KV rows are copied global -> LDS directly (global_load_lds, 16 B
-//     per lane, one 1 KiB instruction per row plus a 128 B one for the rope
-//     part at d_qk = 576); masked rows are zero-filled in LDS without touching
-//     memory, so a NaN payload behind a masked index never reaches P*V.
-//   * S^T [64 keys x 16 heads] per wave on v_mfma_f32_16x16x32_bf16 (K rows
-//     from LDS as the A operand), online exp2 softmax in registers (row max /
-//     row sum over the 4 lane groups of a head with two xor shuffles), then
-//     O^T [512 x 16] += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T
-//     taken straight from the S^T accumulators: the keys of the two operands
-//     are paired in a permuted order that makes each lane's P values exactly
-//     the ones it already holds, so P never goes through LDS.
-//   * every lane owns one head for the whole softmax, so the rescale of O and
-//     the final 1/denominator are per-lane scalars.
+//     exactly nothing to the softmax, so skipping is exact.
+//   * valid KV rows are copied global -> LDS directly (16 B per lane, one
+//     1 KiB instruction per row plus the 128 B rope part at d_qk = 576);
+//     masked rows become zeros in LDS without touching memory, so a NaN
+//     payload behind a masked index never reaches P*V.
+//   * P^T is taken straight from the S^T accumulators: the keys of the two
+//     MFMA operands are paired in a permuted order that makes each lane's P
+//     values exactly the ones it already holds, so P never goes through LDS;
+//     V^T is read with ds_read_b64_tr_b16.
+//   * every lane owns one head for the whole softmax, so the softmax state
+//     and the final 1/denominator are per-lane scalars.
 //
 // The presence of topk_length, of attn_sink, paging and d_qk are template
 // parameters chosen on the host (FlashMLA PR #216, "Why template"): the fixed
@@ -581,10 +580,10 @@ __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 // of its 256 B group, so each address is a row base plus (32(d%8) ^ w) with
 // one per-lane w; the rope part likewise with its own swizzle.  K fragments
 // are read kPrefetch MFMAs ahead.
-template <int D_QK, int EVERY>
+template <int D_QK, int EVERY, class Pump>
 __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
                                               const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
-                                              GatherPump<D_QK>& pump) {
+                                              Pump& pump) {
   using T = WideTile<D_QK>;
   constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
   const int lane = lane_id();
@@ -653,11 +652,10 @@ __device__ __forceinline__ float prob(float s, float neg_ref, float scale_log2) 
 // (+8) sits at chunk (4ct ^ vc ^ swz) of its 256 B group: a row base plus
 // (64(ct%4) ^ w) with one w per row half.  MFMA n covers value tile
 // ct = n % 16, step u = n / 16.
-template <int D_QK, int EVERY>
+template <int D_QK, int EVERY, class Pump>
 __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r0, f32x16 s,
-                                                uint32_t bits,
-                                                f32x16 (&acc)[kDV / 32], SoftmaxState& st,
-                                                float scale_log2, GatherPump<D_QK>& pump) {
+                                                uint32_t bits, f32x16 (&acc)[kDV / 32],
+                                                SoftmaxState& st, float scale_log2, Pump& pump) {
   using T = WideTile<D_QK>;
   constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
   constexpr int kTiles = kDV / 32;
