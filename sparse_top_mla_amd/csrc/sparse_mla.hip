@@ -903,17 +903,39 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     __syncthreads();
     if (ks == 1) return;
   }
-  __bf16* op = a.out + ((size_t)row * a.h_q + head) * kDV + 4 * half;
+  // The output goes through LDS so that every global store writes one head's
+  // whole 1 KiB row: stored straight from the accumulator layout, a store
+  // instruction would touch 32 rows with 16 bytes each.  The wave's bf16
+  // tile takes 32 KiB of a block buffer that no other wave uses any more
+  // (KS = 2: its own merge area, once every partial value has been read).
+  // Chunk c (16 B) of head row h sits at chunk c ^ h of the row.
+  LDS_AS uint8_t* tile = KS == 2 ? (LDS_AS uint8_t*)part
+                                 : (wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * kDV * 2);
+  f32x4 o[kDV / 32][4];
 #pragma unroll
   for (int ct = 0; ct < kDV / 32; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 v = {acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale, acc[ct][4 * j + 2] * scale,
-                 acc[ct][4 * j + 3] * scale};
-      if (KS == 2) v += *reinterpret_cast<const LDS_AS f32x4*>(part + ((ct * 4 + j) * 64 + lane) * 4);
-      const bf16x4 o4 = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-      *reinterpret_cast<bf16x4*>(op + 32 * ct + 8 * j) = o4;
+      o[ct][j] = f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
+                       acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale};
+      if (KS == 2) o[ct][j] += *reinterpret_cast<const LDS_AS f32x4*>(part + ((ct * 4 + j) * 64 + lane) * 4);
     }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // partials read before the tile overwrites them
+#pragma unroll
+  for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x4 o4 = {(__bf16)o[ct][j][0], (__bf16)o[ct][j][1], (__bf16)o[ct][j][2],
+                         (__bf16)o[ct][j][3]};
+      *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * (kDV * 2) + (((4 * ct + j) ^ hl) << 4) + 8 * half) = o4;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is complete for every lane
+  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out + ((size_t)row * a.h_q + hg * 32) * kDV) + lane * 16;
+#pragma unroll 4
+  for (int h = 0; h < 32; ++h) {
+    const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(tile + h * (kDV * 2) + ((lane ^ h) << 4));
+    *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
+  }
   if (half == 0) {
     a.lse[(size_t)row * a.h_q + head] = lse_v;
     a.max_logits[(size_t)row * a.h_q + head] = ml_v;
