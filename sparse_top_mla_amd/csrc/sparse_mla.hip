@@ -805,15 +805,20 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
   const int32_t* idx_row = a.indices + (size_t)row * a.topk;
 
-  // Prologue: tail-scan round (or explicit length) and query slice; the
-  // length is resolved after the query loads are in flight.
+  // Prologue: tail-scan round (or explicit length), the first index blocks,
+  // then the query slice; the length is resolved and block 0 is gathered
+  // while the query loads are still in flight.
   TailRound first;
   int tl = 0;
   if (DYNAMIC)
     tl = a.topk_length[row];
   else
     first = load_tail_round(idx_row, a.topk);
+  int idx0 = load_index(idx_row, 0, a.topk);
+  int idx1 = load_index(idx_row, 1, a.topk);
+  int idx2 = load_index(idx_row, 2, a.topk);
   const int head = hg * 32 + hl;
+  const float sink = SINK ? a.attn_sink[head] : 0.f;  // read here, not in the epilogue
   const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * D_QK + half * 8;
   bf16x8 qf[T::kDSteps];
 #pragma unroll
@@ -829,9 +834,11 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
     st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
     if (nblk > 0) {
-      const int idx0 = load_index(idx_row, 0, a.topk);
-      const int idx1 = load_index(idx_row, 1, a.topk);
-      const int idx2 = load_index(idx_row, 2, a.topk);
+      if (attempt > 0) {
+        idx0 = load_index(idx_row, 0, a.topk);
+        idx1 = load_index(idx_row, 1, a.topk);
+        idx2 = load_index(idx_row, 2, a.topk);
+      }
       const bool ok0 = index_ok(idx0, 0, L, bound);
       const bool ok1 = index_ok(idx1, 1, L, bound);
       const int pg0 = page_lookup<PAGED>(a, seq, ok0, idx0);
@@ -885,7 +892,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   float scale = 0.f, lse_v = INFINITY, ml_v = -INFINITY;
   if (l_fin > 0.f) {
     float denom = l_fin;
-    if (SINK) denom += __builtin_amdgcn_exp2f(a.attn_sink[head] * kLog2e - m_fin);
+    if (SINK) denom += __builtin_amdgcn_exp2f(sink * kLog2e - m_fin);
     scale = a_self / denom;
     ml_v = mx_fin * kLn2;
     lse_v = (m_fin + __log2f(l_fin)) * kLn2;
