@@ -10,9 +10,9 @@
 // gives out = 0, lse = +inf, max_logits = -inf.
 //
 // Two kernels share the index, validity, tail-scan and paging routines:
-//   * the wide kernel (h_q a multiple of 32, every benchmarked shape): one
-//     workgroup per query row, one wave per SIMD, 32 heads per wave on
-//     v_mfma_f32_32x32x16_bf16; see the block comment above it.
+//   * the wide kernel (h_q = 64 or 128, every benchmarked shape): one
+//     workgroup of four waves per query row, one wave per SIMD, 32 heads per
+//     wave on v_mfma_f32_32x32x16_bf16; see the block comment above it.
 //   * the 16-head kernel below (other multiples of 16): one workgroup per
 //     (query row, group of up to 64 heads), 16 heads per wave on
 //     v_mfma_f32_16x16x32_bf16.
@@ -352,7 +352,7 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
 // accumulator (256 fp32 per lane) stays in AGPRs and is touched only by MFMA
 // inside the block loop; the query slice stays in VGPRs.
 //
-// Workgroup: G = h_q / 32 head groups x KS key splits (G * KS <= 4 waves).
+// Workgroup: G = h_q / 32 head groups x KS key splits, G * KS = 4 waves.
 // With KS = 2 (h_q = 32, 64) the two waves of a head group take the lower and
 // upper 32 keys of every 64-key block and merge at the end of the row.
 //
@@ -377,6 +377,7 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kRefSlack = 64.0f;  // log2 units
+constexpr int kWideWaves = 4;       // waves per workgroup (h_q = 64: 2 x 2 key halves; 128: 4)
 
 template <int D_QK>
 struct WideTile {
@@ -444,35 +445,43 @@ __device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int i
 // destination) needs one wait state before the load reads it.  Lane L writes
 // LDS bytes [M0 + 16L, M0 + 16L + 16).
 
+// M0 is an operand of both forms ("{m0}"), so the compiler writes it only
+// when its value changes; the s_nop is the wait state an LDS DMA needs after
+// an M0 write.
+
 // global_load_lds_dwordx4: one 64-bit source address per lane.
 __device__ __forceinline__ void dma16(const void* gptr, LDS_AS void* ldst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0v), "v"(gptr)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0v) : "memory");
 }
 
-// buffer_load_dwordx4 ... lds through a buffer resource of `bytes` bytes at
-// `base` (raw, stride 0); lane L reads base + voff.  Offsets outside the
-// resource read nothing and write zeros to LDS, so bytes = 0 zero-fills the
-// destination without touching memory and without a branch or an EXEC change
-// inside the MFMA stream.
+// buffer_load_dwordx4 ... offset:OFF lds through a raw buffer resource of
+// `bytes` bytes at `base`: lane L reads base + voff + OFF and writes LDS
+// bytes [M0 + OFF + 16L, +16).  The range check covers voff + OFF; offsets
+// outside the resource read nothing and write zeros to LDS, so bytes = 0
+// zero-fills the destination without touching memory and without a branch or
+// an EXEC change inside the MFMA stream.
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+template <int OFF>
 __device__ __forceinline__ void dma_rsrc16(const void* base, uint32_t bytes, uint32_t voff,
-                                           LDS_AS void* ldst) {
+                                           uint32_t m0v) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   u32x4s rs;
   rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
   rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;  // stride 0
   rs[2] = __builtin_amdgcn_readfirstlane(bytes);
   rs[3] = 0x00020000u;  // 32-bit data format, no swizzle
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds"
                :
-               : "s"(m0v), "v"(voff), "s"(rs)
-               : "memory", "m0");
+               : "v"(voff), "s"(rs), "i"(OFF), "{m0}"(__builtin_amdgcn_readfirstlane(m0v))
+               : "memory");
 }
+
+// Hides a value from loop-invariant code motion: per-lane offsets that are
+// the same in every block would otherwise each be hoisted into a register of
+// their own (LDS operand offsets summed with the two buffer bases, the gather
+// lane offsets of the sixteen copy slots).
+__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
 // Source of the rope chunks of masked rows (zeros; 8 lanes x 16 B).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_rope[128];
@@ -501,33 +510,62 @@ __device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const uint8_t* k
 // call, so that the copies can be spread over the MFMA work of the previous
 // block: the issuing wave stalls while the memory pipeline is full, and a
 // whole block issued at once would stall it for the full gather time.  Wave w
-// issues rows w, w+nw, ...; a masked row is zero-filled; calls past the last
-// row write zeros to a 1 KiB dummy area.  Lane L fills LDS chunk L of the
-// row, so it fetches source chunk L ^ swizzle(row).
+// copies rows 16w .. 16w + 15; slot s (a constant once the caller's loop is
+// unrolled) is row 16w + s.  M0 points at the four-row window 16w + 4(s/4)
+// and the instruction offset (s % 4) KiB selects the row within it, with the
+// buffer base moved down by the same offset, so M0 changes once every four
+// copies (an M0 write costs the issuing wave time).  A masked row, or any row
+// of a block past the end of the query row, reads nothing and is zero-filled.
+// Lane L fills LDS chunk L of the row, so it fetches source chunk
+// L ^ swizzle(row); the swizzle depends on the row's low four bits only, i.e.
+// on s.
 template <int D_QK>
 struct GatherPump {
   using T = WideTile<D_QK>;
+  static constexpr int kSlots = kBlockKeys / kWideWaves;
   const uint8_t* kv;
   LDS_AS uint8_t* buf;
-  LDS_AS uint8_t* dummy;
-  uint64_t mask;
-  int phys;    // lane j: KV row of key j
-  int next;    // next row to issue (>= 64: done); wave-uniform
-  int stride;  // waves per workgroup
+  uint64_t mask;     // bit j: key j is valid
+  int phys;          // lane j: KV row of key j
+  int row0;          // first row of this wave (wave-uniform)
+  uint32_t issued;   // slots copied so far (wave-uniform)
+  uint32_t win;      // M0 of the current four-row window
 
-  __device__ __forceinline__ void pump() {
-    const int j = next & (kBlockKeys - 1);
-    const bool live = next < kBlockKeys;
-    const bool on = live && ((mask >> j) & 1ull);
-    const int lane = lane_id();
-    const int r = __builtin_amdgcn_readlane(phys, j);
-    const uint8_t* row = on ? kv + (size_t)(uint32_t)r * T::kRowBytes : kv;
-    const uint32_t voff = (uint32_t)(((lane & 48) | ((lane & 15) ^ nope_swz(j))) * 16);
-    dma_rsrc16(row, on ? T::kNopeBytes : 0u, voff, live ? buf + j * T::kNopeBytes : dummy);
-    next += stride;
+  // fresh: compute the window here (finish, where slots may be skipped);
+  // otherwise slot s % 4 == 0 opens the window and the next three reuse it,
+  // so the compiler sees one M0 value per window and writes M0 once.
+  __device__ __forceinline__ void copy(int s, bool fresh = false) {
+    int r0 = row0;
+    asm volatile("" : "+s"(r0));  // recompute per copy (no hoisted SGPRs)
+    const int j = r0 + s;
+    if (fresh || (s & 3) == 0) win = (uint32_t)(uintptr_t)(buf + (r0 + (s & ~3)) * T::kNopeBytes);
+    // Branch-free: a masked row reads from the table base with an empty range.
+    const uint32_t on = (uint32_t)(mask >> j) & 1u;
+    const uint32_t r = (uint32_t)__builtin_amdgcn_readlane(phys, j) & (0u - on);
+    const uint8_t* row = kv + (size_t)r * T::kRowBytes;
+    int lane = lane_id();
+    opaque(lane);  // one VALU op per copy instead of 16 offsets hoisted into registers
+    const uint32_t voff = (uint32_t)(((lane & 48) | ((lane & 15) ^ nope_swz(s))) * 16);
+    const uint32_t bytes = (((uint32_t)(s & 3) + 1u) * T::kNopeBytes) & (0u - on);
+    switch (s & 3) {
+      case 0: dma_rsrc16<0 * T::kNopeBytes>(row - 0 * T::kNopeBytes, bytes, voff, win); break;
+      case 1: dma_rsrc16<1 * T::kNopeBytes>(row - 1 * T::kNopeBytes, bytes, voff, win); break;
+      case 2: dma_rsrc16<2 * T::kNopeBytes>(row - 2 * T::kNopeBytes, bytes, voff, win); break;
+      default: dma_rsrc16<3 * T::kNopeBytes>(row - 3 * T::kNopeBytes, bytes, voff, win); break;
+    }
+    issued |= 1u << s;
   }
+  // Copies every slot in order (a block gathered outside the MFMA stream).
+  __device__ __forceinline__ void copy_all() {
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) copy(s);
+  }
+  // Copies the slots that were not copied in the MFMA stream (all of them for
+  // a block whose tiles this wave skipped).
   __device__ __forceinline__ void finish() {
-    while (next < kBlockKeys) pump();
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s)
+      if (!((issued >> s) & 1u)) copy(s, true);
   }
 };
 
@@ -562,15 +600,11 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __builtin_bit_cast(float, r.x) + __builtin_bit_cast(float, r.y);
 }
 
-// Hides a value from loop-invariant code motion: the per-lane LDS offsets
-// below are the same in every block, but their sums with the two buffer bases
-// would otherwise each be hoisted into a register of its own.
-__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
 // A wave works on 32-key tiles: keys [r0, r0 + 32) of the block in LDS, with
 // validity bits `bits` (bit i <-> key r0 + i).  Every function below that
-// issues MFMAs calls `pump` (one row of the next block's gather) after every
-// EVERY-th of them.  In the S^T accumulator layout a lane holds keys
+// issues MFMAs copies one row of the next block's gather (gather slots
+// slot0, slot0 + 1, ..., at most NP of them) after every EVERY-th of them.  In the S^T accumulator layout a lane holds keys
 // 8(i/4) + 4half + i%4 (i = 0..15) of the tile for its head hl.
 
 // S^T[key][head] = K Q^T of one tile.  Lane (half, hl) reads chunk 2d + half of key row r0 + hl; r0 is a multiple
@@ -580,10 +614,10 @@ __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 // of its 256 B group, so each address is a row base plus (32(d%8) ^ w) with
 // one per-lane w; the rope part likewise with its own swizzle.  K fragments
 // are read kPrefetch MFMAs ahead.
-template <int D_QK, int EVERY, class Pump>
+template <int D_QK, int EVERY, int NP, class Pump>
 __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
                                               const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
-                                              Pump& pump) {
+                                              Pump& pump, int slot0) {
   using T = WideTile<D_QK>;
   constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
   const int lane = lane_id();
@@ -608,7 +642,7 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
     if (d + kPrefetch < T::kDSteps)
       kring[d % kPrefetch] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(d + kPrefetch));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[d], s, 0, 0, 0);
-    if (d % EVERY == EVERY - 1) pump.pump();
+    if (d % EVERY == EVERY - 1 && d / EVERY < NP) pump.copy(slot0 + d / EVERY);
     __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
   }
   return s;
@@ -655,7 +689,8 @@ __device__ __forceinline__ float prob(float s, float neg_ref, float scale_log2) 
 template <int D_QK, int EVERY, class Pump>
 __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r0, f32x16 s,
                                                 uint32_t bits, f32x16 (&acc)[kDV / 32],
-                                                SoftmaxState& st, float scale_log2, Pump& pump) {
+                                                SoftmaxState& st, float scale_log2, Pump& pump,
+                                                int slot0) {
   using T = WideTile<D_QK>;
   constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
   constexpr int kTiles = kDV / 32;
@@ -715,26 +750,32 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
         pf[1][e] = (__bf16)p1[e];
       }
     }
-    if (n % EVERY == EVERY - 1) pump.pump();
+    if (n % EVERY == EVERY - 1) pump.copy(slot0 + n / EVERY);
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l_sum += pair_sum32(rsum);
 }
 
 // One 64-key block with a valid key for one wave: its 32-key tiles in
-// [koff, koff + 64/KS); tiles without a valid key are skipped.
+// [koff, koff + 64/KS); tiles without a valid key are skipped (their gather
+// slots are then copied by GatherPump::finish).  Each tile owns an equal
+// share of the wave's gather slots, half under S^T and half under P*V.
 template <int D_QK, int KS, int EVERY>
 __device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t mask, int koff,
                                            const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                            f32x16 (&acc)[kDV / 32], SoftmaxState& st,
                                            float scale_log2, GatherPump<D_QK>& pump) {
+  constexpr int kTiles = kBlockKeys / KS / 32;
+  constexpr int kPerTile = GatherPump<D_QK>::kSlots / kTiles;
+  static_assert(kPerTile / 2 == 2 * kDV / 32 / EVERY, "gather slots per P*V pass");
 #pragma unroll
-  for (int kt = 0; kt < kBlockKeys / KS / 32; ++kt) {
+  for (int kt = 0; kt < kTiles; ++kt) {
     const int r0 = koff + 32 * kt;
     const uint32_t bits = (uint32_t)(mask >> r0);
     if (bits != 0u) {
-      const f32x16 s = tile_scores<D_QK, EVERY>(buf, r0, qf, pump);
-      tile_softmax_pv<D_QK, EVERY>(buf, r0, s, bits, acc, st, scale_log2, pump);
+      const f32x16 s = tile_scores<D_QK, EVERY, kPerTile / 2>(buf, r0, qf, pump, kt * kPerTile);
+      tile_softmax_pv<D_QK, EVERY>(buf, r0, s, bits, acc, st, scale_log2, pump,
+                                   kt * kPerTile + kPerTile / 2);
     }
   }
 }
@@ -757,8 +798,7 @@ struct WidePipe {
   static __device__ __forceinline__ void step(const FwdArgs& a, const LDS_AS uint8_t* cur,
                                               LDS_AS uint8_t* nxt, int t, int nblk, int L,
                                               int bound, int seq, const int32_t* idx_row,
-                                              LDS_AS uint8_t* dummy, int wave, int nwaves,
-                                              int koff, uint64_t& mask_cur, Ahead& ah,
+                                              int wave, int koff, uint64_t& mask_cur, Ahead& ah,
                                               const bf16x8 (&qf)[T::kDSteps],
                                               f32x16 (&acc)[kDV / 32], SoftmaxState& st) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -766,11 +806,13 @@ struct WidePipe {
     const bool have_nxt = t + 1 < nblk;
     const BlockMeta mn =
         block_meta<PAGED>(a, index_ok(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
-    if (have_nxt) stage_rope<D_QK>(nxt, a.kv, mn.mask, mn.phys, wave, nwaves);
+    if (have_nxt) stage_rope<D_QK>(nxt, a.kv, mn.mask, mn.phys, wave, kWideWaves);
     const bool ok2 = index_ok(ah.idx2, t + 2, L, bound);
     const int page2 = page_lookup<PAGED>(a, seq, ok2, ah.idx2);
     const int idx3 = load_index(idx_row, t + 3, a.topk);
-    GatherPump<D_QK> pump{a.kv, nxt, dummy, mn.mask, mn.phys, have_nxt ? wave : kBlockKeys, nwaves};
+    // Past the last block the mask is empty: the copies zero-fill `nxt`,
+    // which nothing reads any more.
+    GatherPump<D_QK> pump{a.kv, nxt, mn.mask, mn.phys, GatherPump<D_QK>::kSlots * wave, 0u, 0u};
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
     if (wmask != 0)
       wide_block<D_QK, KS, kEvery>(cur, mask_cur, koff, qf, acc, st, a.scale_log2, pump);
@@ -786,15 +828,12 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   using T = WideTile<D_QK>;
   __shared__ __attribute__((aligned(16))) uint8_t buf0_raw[T::kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1_raw[T::kBufBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t dummy_raw[T::kNopeBytes];
   LDS_AS uint8_t* buf0 = (LDS_AS uint8_t*)buf0_raw;
   LDS_AS uint8_t* buf1 = (LDS_AS uint8_t*)buf1_raw;
-  LDS_AS uint8_t* dummy = (LDS_AS uint8_t*)dummy_raw;
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int G = nwaves / KS;
+  constexpr int G = kWideWaves / KS;
   const int hg = wave % G, ks = wave / G;
   const int hl = lane & 31, half = lane >> 5;
   const int koff = ks * (kBlockKeys / KS);
@@ -847,16 +886,19 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       uint64_t mask_cur = m0.mask;
       Ahead ah{idx1, pg1, idx2};
       __syncthreads();  // a previous attempt may still read the buffers
-      stage_rope<D_QK>(buf0, a.kv, m0.mask, m0.phys, wave, nwaves);
-      GatherPump<D_QK>{a.kv, buf0, dummy, m0.mask, m0.phys, wave, nwaves}.finish();
+      stage_rope<D_QK>(buf0, a.kv, m0.mask, m0.phys, wave, kWideWaves);
+      GatherPump<D_QK>{a.kv, buf0, m0.mask, m0.phys, GatherPump<D_QK>::kSlots * wave, 0u, 0u}.copy_all();
       using P = WidePipe<D_QK, KS, PAGED>;
       for (int t = 0; t < nblk; t += 2) {
-        P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, dummy, wave, nwaves, koff,
-                mask_cur, ah, qf, acc, st);
+        P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf, acc,
+                st);
         if (t + 1 < nblk)
-          P::step(a, buf1, buf0, t + 1, nblk, L, bound, seq, idx_row, dummy, wave, nwaves, koff,
-                  mask_cur, ah, qf, acc, st);
+          P::step(a, buf1, buf0, t + 1, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf,
+                  acc, st);
       }
+      // The last step's zero-fill copies may still be landing in a buffer
+      // that the next attempt or the epilogue writes.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     // Workgroup-uniform: recompute once if any head outgrew its reference.
     if (!__syncthreads_or(st.overflow) || attempt == 1) break;
@@ -1015,9 +1057,10 @@ smla_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
 
 template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
 smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
-  const int nwaves = (args.h_q / 32) * KS;
+  if ((args.h_q / 32) * KS != kWideWaves)
+    return fail(SMLA_ERR_UNSUPPORTED, "wide kernel needs h_q=%d (KS=%d)", 32 * kWideWaves / KS, KS);
   hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, KS, PAGED, DYNAMIC, SINK>), dim3(args.rows),
-                     dim3(nwaves * 64), 0, stream, args);
+                     dim3(kWideWaves * 64), 0, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
@@ -1025,7 +1068,7 @@ smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
 
 template <bool PAGED>
 smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
-  const int ks = args.h_q / 32 <= 2 ? 2 : 1;
+  const int ks = args.h_q == 64 ? 2 : 1;
   const bool dyn = args.topk_length != nullptr;
   const bool sink = args.attn_sink != nullptr;
   args.head_groups = 1;
@@ -1054,7 +1097,9 @@ smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
 
 template <bool PAGED>
 smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
-  if (args.h_q % 32 == 0) return dispatch_wide<PAGED>(d_qk, args, stream);
+  // The wide kernel runs four waves: 64 heads as two head groups times two
+  // key halves, or 128 heads as four head groups.
+  if (args.h_q == 64 || args.h_q == 128) return dispatch_wide<PAGED>(d_qk, args, stream);
   const int waves_total = args.h_q / kHeadsPerWave;
   args.head_groups = (waves_total > 4 && waves_total % 2 == 0) ? 2 : 1;
   const bool dyn = args.topk_length != nullptr;
