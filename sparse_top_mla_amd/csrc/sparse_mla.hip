@@ -105,6 +105,14 @@ struct FwdArgs {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// s_waitcnt vmcnt(0) through the builtin rather than inline assembly, so that
+// the compiler's own wait insertion knows every earlier vector-memory load
+// has completed (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15).  Behind an
+// inline-asm wait it would still consider, say, the query loads in flight
+// and wait for them again inside the block loop, where the count also covers
+// the gather copies just issued.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Validity bound K of a row: s_kv for prefill; for paged decode the request's
 // cache length, cut to what its block table can address.
 __device__ __forceinline__ int row_bound(bool paged, const int32_t* cache_seqlens, int seq,
@@ -245,7 +253,7 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
     // a4: gather into LDS.
     __syncthreads();  // every wave is done reading the previous block
     stage_block<D_QK>(lds, a.kv, mask, phys, wave, nwaves);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_all();
     __syncthreads();
 
     // a5: S^T = K Q^T; lane (g, hl) gets keys kt*16 + 4g + r of head hl.
@@ -801,7 +809,7 @@ struct WidePipe {
                                               int wave, int koff, uint64_t& mask_cur, Ahead& ah,
                                               const bf16x8 (&qf)[T::kDSteps],
                                               f32x16 (&acc)[kDV / 32], SoftmaxState& st) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm_all();
     __syncthreads();
     const bool have_nxt = t + 1 < nblk;
     const BlockMeta mn =
@@ -853,9 +861,11 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     tl = a.topk_length[row];
   else
     first = load_tail_round(idx_row, a.topk);
-  int idx0 = load_index(idx_row, 0, a.topk);
-  int idx1 = load_index(idx_row, 1, a.topk);
-  int idx2 = load_index(idx_row, 2, a.topk);
+  // Kept for a recompute: loading them again there would make the compiler
+  // wait for every outstanding load (the query rows included) at the join.
+  const int idx0 = load_index(idx_row, 0, a.topk);
+  const int idx1 = load_index(idx_row, 1, a.topk);
+  const int idx2 = load_index(idx_row, 2, a.topk);
   const int head = hg * 32 + hl;
   const float sink = SINK ? a.attn_sink[head] : 0.f;  // read here, not in the epilogue
   const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * D_QK + half * 8;
@@ -873,11 +883,6 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
     st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
     if (nblk > 0) {
-      if (attempt > 0) {
-        idx0 = load_index(idx_row, 0, a.topk);
-        idx1 = load_index(idx_row, 1, a.topk);
-        idx2 = load_index(idx_row, 2, a.topk);
-      }
       const bool ok0 = index_ok(idx0, 0, L, bound);
       const bool ok1 = index_ok(idx1, 1, L, bound);
       const int pg0 = page_lookup<PAGED>(a, seq, ok0, idx0);
@@ -898,7 +903,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       }
       // The last step's zero-fill copies may still be landing in a buffer
       // that the next attempt or the epilogue writes.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vm_all();
     }
     // Workgroup-uniform: recompute once if any head outgrew its reference.
     if (!__syncthreads_or(st.overflow) || attempt == 1) break;
