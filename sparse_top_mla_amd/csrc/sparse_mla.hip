@@ -45,6 +45,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <type_traits>
 
 #include "sparse_mla.h"
 
@@ -945,50 +946,88 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     lse_v = (m_fin + __log2f(l_fin)) * kLn2;
   }
   if (KS == 2) {
-    if (ks == 1) {
+    // Each wave of a head group finishes one half of the value columns
+    // (wave ks: columns 256ks .. 256ks + 255, i.e. ct in [8ks, 8ks + 8)).  It
+    // hands its scaled partial of the other half to the partner through the
+    // partner's 32 KiB region of the group's block buffer, adds the partner's
+    // partial of its own half, stages the bf16 result in its own region (only
+    // this wave reads it) and stores 512 B half rows.
+    // The half is a compile-time constant in each branch (acc is indexed
+    // with it and must stay in registers).
+    auto finish_half = [&](auto ks_c) {
+    constexpr int K = decltype(ks_c)::value;
+    constexpr int kHalf = kDV / 64;  // value tiles per half
+    LDS_AS float* mine = part + K * (32 * kDV / 2);
+    LDS_AS float* theirs = part + (1 - K) * (32 * kDV / 2);
 #pragma unroll
-      for (int ct = 0; ct < kDV / 32; ++ct)
+    for (int c = 0; c < kHalf; ++c) {
+      const int ct = (1 - K) * kHalf + c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<LDS_AS f32x4*>(part + ((ct * 4 + j) * 64 + lane) * 4) =
-              f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
-                    acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale};
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<LDS_AS f32x4*>(theirs + ((c * 4 + j) * 64 + lane) * 4) =
+            f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale, acc[ct][4 * j + 2] * scale,
+                  acc[ct][4 * j + 3] * scale};
     }
     __syncthreads();
-    if (ks == 1) return;
-  }
-  // The output goes through LDS so that every global store writes one head's
-  // whole 1 KiB row: stored straight from the accumulator layout, a store
-  // instruction would touch 32 rows with 16 bytes each.  The wave's bf16
-  // tile takes 32 KiB of a block buffer that no other wave uses any more
-  // (KS = 2: its own merge area, once every partial value has been read).
-  // Chunk c (16 B) of head row h sits at chunk c ^ h of the row.
-  LDS_AS uint8_t* tile = KS == 2 ? (LDS_AS uint8_t*)part
-                                 : (wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * kDV * 2);
-  f32x4 o[kDV / 32][4];
+    f32x4 o[kHalf][4];
 #pragma unroll
-  for (int ct = 0; ct < kDV / 32; ++ct)
+    for (int c = 0; c < kHalf; ++c) {
+      const int ct = K * kHalf + c;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[ct][j] = f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
-                       acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale};
-      if (KS == 2) o[ct][j] += *reinterpret_cast<const LDS_AS f32x4*>(part + ((ct * 4 + j) * 64 + lane) * 4);
+      for (int j = 0; j < 4; ++j)
+        o[c][j] = f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
+                        acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale} +
+                  *reinterpret_cast<const LDS_AS f32x4*>(mine + ((c * 4 + j) * 64 + lane) * 4);
     }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // partials read before the tile overwrites them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // partials read before the tile overwrites them
+    // Half row h (512 B) at h * 512; its chunk c (16 B) sits at chunk c ^ h.
+    LDS_AS uint8_t* tile = (LDS_AS uint8_t*)mine;
 #pragma unroll
-  for (int ct = 0; ct < kDV / 32; ++ct)
+    for (int c = 0; c < kHalf; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x4 o4 = {(__bf16)o[ct][j][0], (__bf16)o[ct][j][1], (__bf16)o[ct][j][2],
-                         (__bf16)o[ct][j][3]};
-      *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * (kDV * 2) + (((4 * ct + j) ^ hl) << 4) + 8 * half) = o4;
-    }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is complete for every lane
-  uint8_t* orow = reinterpret_cast<uint8_t*>(a.out + ((size_t)row * a.h_q + hg * 32) * kDV) + lane * 16;
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 o4 = {(__bf16)o[c][j][0], (__bf16)o[c][j][1], (__bf16)o[c][j][2],
+                           (__bf16)o[c][j][3]};
+        *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * kDV + (((4 * c + j) ^ hl) << 4) + 8 * half) = o4;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is complete for every lane
+    const int hsub = lane >> 5, chunk = lane & 31;
+    uint8_t* obase = reinterpret_cast<uint8_t*>(a.out + ((size_t)row * a.h_q + hg * 32) * kDV) +
+                     K * kDV + chunk * 16;
 #pragma unroll 4
-  for (int h = 0; h < 32; ++h) {
-    const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(tile + h * (kDV * 2) + ((lane ^ h) << 4));
-    *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
+    for (int k = 0; k < 16; ++k) {
+      const int h = 2 * k + hsub;
+      const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(tile + h * kDV + ((chunk ^ h) << 4));
+      *reinterpret_cast<u32x4*>(obase + (size_t)h * (kDV * 2)) = v;
+    }
+    };
+    if (ks == 0)
+      finish_half(std::integral_constant<int, 0>{});
+    else
+      finish_half(std::integral_constant<int, 1>{});
+    if (ks == 1) return;
+  } else {
+    // The output goes through LDS so that every global store writes one
+    // head's whole 1 KiB row: stored straight from the accumulator layout, a
+    // store instruction would touch 32 rows with 16 bytes each.  The wave's
+    // bf16 tile takes 32 KiB of a block buffer that no other wave uses any
+    // more.  Chunk c (16 B) of head row h sits at chunk c ^ h of the row.
+    LDS_AS uint8_t* tile = (wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * kDV * 2);
+#pragma unroll
+    for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 o4 = {(__bf16)(acc[ct][4 * j] * scale), (__bf16)(acc[ct][4 * j + 1] * scale),
+                           (__bf16)(acc[ct][4 * j + 2] * scale), (__bf16)(acc[ct][4 * j + 3] * scale)};
+        *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * (kDV * 2) + (((4 * ct + j) ^ hl) << 4) + 8 * half) = o4;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is complete for every lane
+    uint8_t* orow = reinterpret_cast<uint8_t*>(a.out + ((size_t)row * a.h_q + hg * 32) * kDV) + lane * 16;
+#pragma unroll 4
+    for (int h = 0; h < 32; ++h) {
+      const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(tile + h * (kDV * 2) + ((lane ^ h) << 4));
+      *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
+    }
   }
   if (half == 0) {
     a.lse[(size_t)row * a.h_q + head] = lse_v;
