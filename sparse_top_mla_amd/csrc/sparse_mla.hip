@@ -102,6 +102,7 @@ struct FwdArgs {
   int32_t mbps;          // decode max_blocks_per_seq
   int32_t head_groups;   // workgroups per row (1 or 2)
   float scale_log2;      // sm_scale * log2(e)
+  uint32_t kv_span;      // bytes of the KV table (wide kernel: at most kMaxKvSpan)
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -414,6 +415,7 @@ __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 struct BlockMeta {
   uint64_t mask;  // bit j: key j of the block is used
   int phys;       // lane j: KV row of key j (prefill index or paged slot)
+  bool ok;        // lane j: bit j of mask
 };
 
 __device__ __forceinline__ int load_index(const int32_t* idx_row, int blk, int topk) {
@@ -442,6 +444,7 @@ __device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int i
   }
   m.mask = __builtin_amdgcn_ballot_w64(ok);
   m.phys = phys;
+  m.ok = ok;
   return m;
 }
 
@@ -458,61 +461,39 @@ __device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int i
 // when its value changes; the s_nop is the wait state an LDS DMA needs after
 // an M0 write.
 
-// global_load_lds_dwordx4: one 64-bit source address per lane.
-__device__ __forceinline__ void dma16(const void* gptr, LDS_AS void* ldst) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0v) : "memory");
-}
+// Hides a value from loop-invariant code motion: per-lane offsets that are
+// the same in every block (LDS operand offsets summed with the two buffer
+// bases) would otherwise each be hoisted into a register of their own.
+__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
-// buffer_load_dwordx4 ... offset:OFF lds through a raw buffer resource of
-// `bytes` bytes at `base`: lane L reads base + voff + OFF and writes LDS
-// bytes [M0 + OFF + 16L, +16).  The range check covers voff + OFF; offsets
-// outside the resource read nothing and write zeros to LDS, so bytes = 0
-// zero-fills the destination without touching memory and without a branch or
-// an EXEC change inside the MFMA stream.
+// The gather reads the KV table through one raw buffer resource
+// whose base sits kSpanBias bytes below the table (records: span + bias).
+// buffer_load_dwordx4 ... offset:OFF lds reads base + voff + OFF per lane
+// and writes LDS bytes [M0 + OFF + 16L, +16) for lane L; the range check
+// covers voff + OFF, and an offset outside the records reads nothing and
+// writes zeros to LDS, so a masked row is zero-filled without touching
+// memory and without a branch or an EXEC change inside the MFMA stream.
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
-template <int OFF>
-__device__ __forceinline__ void dma_rsrc16(const void* base, uint32_t bytes, uint32_t voff,
-                                           uint32_t m0v) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
+constexpr uint32_t kSpanBias = 3 * 1024;  // room for the largest OFF below
+constexpr uint32_t kOob = 0xFFFFE000u;    // + lane chunk + OFF: outside, no wrap
+constexpr uint32_t kMaxKvSpan = kOob - kSpanBias;
+
+__device__ __forceinline__ u32x4s table_rsrc(const FwdArgs& a) {
+  const uint64_t b = (uint64_t)(uintptr_t)a.kv - kSpanBias;
   u32x4s rs;
   rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
   rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;  // stride 0
-  rs[2] = __builtin_amdgcn_readfirstlane(bytes);
+  rs[2] = __builtin_amdgcn_readfirstlane(a.kv_span + kSpanBias);
   rs[3] = 0x00020000u;  // 32-bit data format, no swizzle
+  return rs;
+}
+
+template <int OFF>
+__device__ __forceinline__ void dma_table16(const u32x4s& rs, uint32_t voff, uint32_t m0v) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds"
                :
                : "v"(voff), "s"(rs), "i"(OFF), "{m0}"(__builtin_amdgcn_readfirstlane(m0v))
                : "memory");
-}
-
-// Hides a value from loop-invariant code motion: per-lane offsets that are
-// the same in every block would otherwise each be hoisted into a register of
-// their own (LDS operand offsets summed with the two buffer bases, the gather
-// lane offsets of the sixteen copy slots).
-__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
-
-// Source of the rope chunks of masked rows (zeros; 8 lanes x 16 B).
-__device__ __attribute__((aligned(16))) uint8_t g_zero_rope[128];
-
-// Rope part (d_qk = 576) of a block: 8 rows of 128 B per load, wave w taking
-// row groups w, w+nw, ...  Lane L handles row 8g + L/8, LDS chunk L%8, which
-// holds source chunk (L%8) ^ swizzle(row); masked rows read zeros.
-template <int D_QK>
-__device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const uint8_t* kv, uint64_t mask,
-                                           int phys, int wave, int nwaves) {
-  using T = WideTile<D_QK>;
-  if (T::kRopeLanes == 0) return;
-  const int lane = lane_id();
-  for (int g = wave; g < kBlockKeys / 8; g += nwaves) {
-    const int jj = 8 * g + (lane >> 3);
-    const int r = __shfl(phys, jj);
-    const int c = (lane & 7) ^ rope_swz(jj);
-    const uint8_t* src = ((mask >> jj) & 1ull)
-                             ? kv + (size_t)(uint32_t)r * T::kRowBytes + T::kNopeBytes + c * 16
-                             : g_zero_rope + (lane & 7) * 16;
-    dma16(src, buf + T::kRopeBase + g * 8 * T::kRopeBytes);
-  }
 }
 
 // Nope part (the first 512 columns, also V) of a block, one 1 KiB row per
@@ -521,24 +502,37 @@ __device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const uint8_t* k
 // whole block issued at once would stall it for the full gather time.  Wave w
 // copies rows 16w .. 16w + 15; slot s (a constant once the caller's loop is
 // unrolled) is row 16w + s.  M0 points at the four-row window 16w + 4(s/4)
-// and the instruction offset (s % 4) KiB selects the row within it, with the
-// buffer base moved down by the same offset, so M0 changes once every four
-// copies (an M0 write costs the issuing wave time).  A masked row, or any row
-// of a block past the end of the query row, reads nothing and is zero-filled.
-// Lane L fills LDS chunk L of the row, so it fetches source chunk
-// L ^ swizzle(row); the swizzle depends on the row's low four bits only, i.e.
-// on s.
+// and the instruction offset (s % 4) KiB selects the row within it, so M0
+// changes once every four copies (an M0 write costs the issuing wave time).
+// The instruction offset is added to the memory address as well, so the
+// per-row offsets (one per lane of `offw`, built once per block) are moved
+// down by it: a copy is a readlane, two VALU ops and the load.  A masked row,
+// or any row of a block past the end of the query row, has offset kOob and
+// is zero-filled.  Lane L fills LDS chunk L of the row, so it fetches source
+// chunk L ^ swizzle(row); the swizzle depends on the row's low four bits
+// only, i.e. on s.
 template <int D_QK>
 struct GatherPump {
   using T = WideTile<D_QK>;
   static constexpr int kSlots = kBlockKeys / kWideWaves;
-  const uint8_t* kv;
+  u32x4s rsrc;       // table resource (wave-uniform)
   LDS_AS uint8_t* buf;
-  uint64_t mask;     // bit j: key j is valid
-  int phys;          // lane j: KV row of key j
   int row0;          // first row of this wave (wave-uniform)
+  int offw;          // lane s: source offset of row row0 + s (see row_offsets)
+  int lane16;        // 16 * lane
   uint32_t issued;   // slots copied so far (wave-uniform)
   uint32_t win;      // M0 of the current four-row window
+
+  // Lane j of the result: offset of key j's row for slot j % 4, or kOob.
+  static __device__ __forceinline__ int row_offsets(const BlockMeta& m) {
+    const uint32_t off = (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias -
+                         (uint32_t)(lane_id() & 3) * T::kNopeBytes;
+    return (int)(m.ok ? off : kOob);
+  }
+  // The wave's sixteen rows, moved to lanes 0..15.
+  static __device__ __forceinline__ int wave_offsets(int offs, int row0) {
+    return __shfl(offs, row0 + (lane_id() & (kSlots - 1)));
+  }
 
   // fresh: compute the window here (finish, where slots may be skipped);
   // otherwise slot s % 4 == 0 opens the window and the next three reuse it,
@@ -546,21 +540,14 @@ struct GatherPump {
   __device__ __forceinline__ void copy(int s, bool fresh = false) {
     int r0 = row0;
     asm volatile("" : "+s"(r0));  // recompute per copy (no hoisted SGPRs)
-    const int j = r0 + s;
     if (fresh || (s & 3) == 0) win = (uint32_t)(uintptr_t)(buf + (r0 + (s & ~3)) * T::kNopeBytes);
-    // Branch-free: a masked row reads from the table base with an empty range.
-    const uint32_t on = (uint32_t)(mask >> j) & 1u;
-    const uint32_t r = (uint32_t)__builtin_amdgcn_readlane(phys, j) & (0u - on);
-    const uint8_t* row = kv + (size_t)r * T::kRowBytes;
-    int lane = lane_id();
-    opaque(lane);  // one VALU op per copy instead of 16 offsets hoisted into registers
-    const uint32_t voff = (uint32_t)(((lane & 48) | ((lane & 15) ^ nope_swz(s))) * 16);
-    const uint32_t bytes = (((uint32_t)(s & 3) + 1u) * T::kNopeBytes) & (0u - on);
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readlane(offw, s);
+    const uint32_t voff = ((uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4)) + so;
     switch (s & 3) {
-      case 0: dma_rsrc16<0 * T::kNopeBytes>(row - 0 * T::kNopeBytes, bytes, voff, win); break;
-      case 1: dma_rsrc16<1 * T::kNopeBytes>(row - 1 * T::kNopeBytes, bytes, voff, win); break;
-      case 2: dma_rsrc16<2 * T::kNopeBytes>(row - 2 * T::kNopeBytes, bytes, voff, win); break;
-      default: dma_rsrc16<3 * T::kNopeBytes>(row - 3 * T::kNopeBytes, bytes, voff, win); break;
+      case 0: dma_table16<0 * T::kNopeBytes>(rsrc, voff, win); break;
+      case 1: dma_table16<1 * T::kNopeBytes>(rsrc, voff, win); break;
+      case 2: dma_table16<2 * T::kNopeBytes>(rsrc, voff, win); break;
+      default: dma_table16<3 * T::kNopeBytes>(rsrc, voff, win); break;
     }
     issued |= 1u << s;
   }
@@ -577,6 +564,28 @@ struct GatherPump {
       if (!((issued >> s) & 1u)) copy(s, true);
   }
 };
+
+// Rope part (d_qk = 576) of a block: 8 rows of 128 B per load, wave w taking
+// row groups w and w + 4.  Lane L handles row jj = 8g + L/8, LDS chunk L%8,
+// which holds source chunk (L%8) ^ swizzle(jj); `offs` are the per-key
+// offsets of GatherPump::row_offsets (moved down by (jj % 4) KiB, which is
+// added back), so masked rows stay outside the records and read zeros.
+template <int D_QK>
+__device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const u32x4s& rsrc, int offs,
+                                           int wave) {
+  using T = WideTile<D_QK>;
+  if (T::kRopeLanes == 0) return;
+  const int lane = lane_id();
+#pragma unroll
+  for (int g0 = 0; g0 < kBlockKeys / 8; g0 += kWideWaves) {
+    const int g = g0 + wave;
+    const int jj = 8 * g + (lane >> 3);
+    const uint32_t o = (uint32_t)__shfl(offs, jj);
+    const uint32_t voff = o + (uint32_t)(jj & 3) * T::kNopeBytes + T::kNopeBytes +
+                          (uint32_t)(((lane & 7) ^ rope_swz(jj)) << 4);
+    dma_table16<0>(rsrc, voff, (uint32_t)(uintptr_t)(buf + T::kRopeBase + g * 8 * T::kRopeBytes));
+  }
+}
 
 // Running softmax state of one lane's head (log2 units); both halves of the
 // wave hold identical copies.
@@ -815,13 +824,17 @@ struct WidePipe {
     const bool have_nxt = t + 1 < nblk;
     const BlockMeta mn =
         block_meta<PAGED>(a, index_ok(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
-    if (have_nxt) stage_rope<D_QK>(nxt, a.kv, mn.mask, mn.phys, wave, kWideWaves);
+    const u32x4s rsrc = table_rsrc(a);
+    const int offs = GatherPump<D_QK>::row_offsets(mn);
+    if (have_nxt) stage_rope<D_QK>(nxt, rsrc, offs, wave);
     const bool ok2 = index_ok(ah.idx2, t + 2, L, bound);
     const int page2 = page_lookup<PAGED>(a, seq, ok2, ah.idx2);
     const int idx3 = load_index(idx_row, t + 3, a.topk);
     // Past the last block the mask is empty: the copies zero-fill `nxt`,
     // which nothing reads any more.
-    GatherPump<D_QK> pump{a.kv, nxt, mn.mask, mn.phys, GatherPump<D_QK>::kSlots * wave, 0u, 0u};
+    const int row0 = GatherPump<D_QK>::kSlots * wave;
+    GatherPump<D_QK> pump{rsrc, nxt, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
+                          lane_id() * 16, 0u, 0u};
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
     if (wmask != 0)
       wide_block<D_QK, KS, kEvery>(cur, mask_cur, koff, qf, acc, st, a.scale_log2, pump);
@@ -892,8 +905,15 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       uint64_t mask_cur = m0.mask;
       Ahead ah{idx1, pg1, idx2};
       __syncthreads();  // a previous attempt may still read the buffers
-      stage_rope<D_QK>(buf0, a.kv, m0.mask, m0.phys, wave, kWideWaves);
-      GatherPump<D_QK>{a.kv, buf0, m0.mask, m0.phys, GatherPump<D_QK>::kSlots * wave, 0u, 0u}.copy_all();
+      {
+        const u32x4s rsrc = table_rsrc(a);
+        const int offs = GatherPump<D_QK>::row_offsets(m0);
+        const int row0 = GatherPump<D_QK>::kSlots * wave;
+        stage_rope<D_QK>(buf0, rsrc, offs, wave);
+        GatherPump<D_QK>{rsrc, buf0, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
+                         lane_id() * 16, 0u, 0u}
+            .copy_all();
+      }
       using P = WidePipe<D_QK, KS, PAGED>;
       for (int t = 0; t < nblk; t += 2) {
         P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf, acc,
@@ -1139,11 +1159,19 @@ smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
   return fail(SMLA_ERR_UNSUPPORTED, "no wide kernel instance for d_qk=%d", d_qk);
 }
 
+// KV table bytes for FwdArgs::kv_span; a table the wide kernel cannot address
+// with 32-bit offsets gets a value above kMaxKvSpan.
+uint32_t span_or_max(uint64_t bytes) {
+  return bytes <= kMaxKvSpan ? (uint32_t)bytes : 0xFFFFFFFFu;
+}
+
 template <bool PAGED>
 smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
   // The wide kernel runs four waves: 64 heads as two head groups times two
-  // key halves, or 128 heads as four head groups.
-  if (args.h_q == 64 || args.h_q == 128) return dispatch_wide<PAGED>(d_qk, args, stream);
+  // key halves, or 128 heads as four head groups; it addresses the KV table
+  // with 32-bit offsets (kv_span, set by the caller, at most kMaxKvSpan).
+  if ((args.h_q == 64 || args.h_q == 128) && args.kv_span <= kMaxKvSpan)
+    return dispatch_wide<PAGED>(d_qk, args, stream);
   const int waves_total = args.h_q / kHeadsPerWave;
   args.head_groups = (waves_total > 4 && waves_total % 2 == 0) ? 2 : 1;
   const bool dyn = args.topk_length != nullptr;
@@ -1193,6 +1221,7 @@ extern "C" smla_status sparse_mla_fwd(const void* q, const void* kv, const int32
   args.topk = topk;
   args.s_kv = s_kv;
   args.scale_log2 = sm_scale * kLog2e;
+  args.kv_span = span_or_max((uint64_t)s_kv * (uint64_t)d_qk * 2u);
   return dispatch_fwd<false>(d_qk, args, static_cast<hipStream_t>(stream));
 }
 
@@ -1236,6 +1265,7 @@ extern "C" smla_status sparse_mla_decode_fwd(
   args.num_blocks = num_blocks;
   args.mbps = max_blocks_per_seq;
   args.scale_log2 = sm_scale * kLog2e;
+  args.kv_span = span_or_max((uint64_t)num_blocks * kPage * (uint64_t)d_qk * 2u);
   return dispatch_fwd<true>(d_qk, args, static_cast<hipStream_t>(stream));
 }
 
