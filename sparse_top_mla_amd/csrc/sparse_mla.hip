@@ -488,12 +488,20 @@ __device__ __forceinline__ u32x4s table_rsrc(const FwdArgs& a) {
   return rs;
 }
 
-template <int OFF>
+// NOP: the wait state an LDS DMA needs after an M0 write (the compiler writes
+// M0 for the operand only when its value changes).
+template <int OFF, bool NOP = true>
 __device__ __forceinline__ void dma_table16(const u32x4s& rs, uint32_t voff, uint32_t m0v) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds"
-               :
-               : "v"(voff), "s"(rs), "i"(OFF), "{m0}"(__builtin_amdgcn_readfirstlane(m0v))
-               : "memory");
+  if (NOP)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds"
+                 :
+                 : "v"(voff), "s"(rs), "i"(OFF), "{m0}"(__builtin_amdgcn_readfirstlane(m0v))
+                 : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds"
+                 :
+                 : "v"(voff), "s"(rs), "i"(OFF), "{m0}"(__builtin_amdgcn_readfirstlane(m0v))
+                 : "memory");
 }
 
 // Nope part (the first 512 columns, also V) of a block, one 1 KiB row per
@@ -522,6 +530,7 @@ struct GatherPump {
   int lane16;        // 16 * lane
   uint32_t issued;   // slots copied so far (wave-uniform)
   uint32_t win;      // M0 of the current four-row window
+  uint32_t so_next;  // offset of the next slot, read one copy ahead
 
   // Lane j of the result: offset of key j's row for slot j % 4, or kOob.
   static __device__ __forceinline__ int row_offsets(const BlockMeta& m) {
@@ -537,24 +546,28 @@ struct GatherPump {
   // fresh: compute the window here (finish, where slots may be skipped);
   // otherwise slot s % 4 == 0 opens the window and the next three reuse it,
   // so the compiler sees one M0 value per window and writes M0 once.
-  __device__ __forceinline__ void copy(int s, bool fresh = false) {
-    int r0 = row0;
-    asm volatile("" : "+s"(r0));  // recompute per copy (no hoisted SGPRs)
-    if (fresh || (s & 3) == 0) win = (uint32_t)(uintptr_t)(buf + (r0 + (s & ~3)) * T::kNopeBytes);
-    const uint32_t so = (uint32_t)__builtin_amdgcn_readlane(offw, s);
+  // first: the first copy of a run of consecutive slots reads its own
+  // offset; every copy reads the next slot's offset ahead, so that the VALU
+  // use of a readlane result never follows the readlane directly.
+  __device__ __forceinline__ void copy(int s, bool fresh = false, bool first = true) {
+    const bool opens = fresh || (s & 3) == 0;
+    if (opens) win = (uint32_t)(uintptr_t)(buf + (row0 + (s & ~3)) * T::kNopeBytes);
+    const uint32_t so = first ? (uint32_t)__builtin_amdgcn_readlane(offw, s) : so_next;
+    if (s + 1 < kSlots) so_next = (uint32_t)__builtin_amdgcn_readlane(offw, s + 1);
     const uint32_t voff = ((uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4)) + so;
+    constexpr int B = T::kNopeBytes;
     switch (s & 3) {
-      case 0: dma_table16<0 * T::kNopeBytes>(rsrc, voff, win); break;
-      case 1: dma_table16<1 * T::kNopeBytes>(rsrc, voff, win); break;
-      case 2: dma_table16<2 * T::kNopeBytes>(rsrc, voff, win); break;
-      default: dma_table16<3 * T::kNopeBytes>(rsrc, voff, win); break;
+      case 0: dma_table16<0 * B>(rsrc, voff, win); break;
+      case 1: opens ? dma_table16<1 * B>(rsrc, voff, win) : dma_table16<1 * B, false>(rsrc, voff, win); break;
+      case 2: opens ? dma_table16<2 * B>(rsrc, voff, win) : dma_table16<2 * B, false>(rsrc, voff, win); break;
+      default: opens ? dma_table16<3 * B>(rsrc, voff, win) : dma_table16<3 * B, false>(rsrc, voff, win); break;
     }
     issued |= 1u << s;
   }
   // Copies every slot in order (a block gathered outside the MFMA stream).
   __device__ __forceinline__ void copy_all() {
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) copy(s);
+    for (int s = 0; s < kSlots; ++s) copy(s, false, s == 0);
   }
   // Copies the slots that were not copied in the MFMA stream (all of them for
   // a block whose tiles this wave skipped).
@@ -660,7 +673,7 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
     if (d + kPrefetch < T::kDSteps)
       kring[d % kPrefetch] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(d + kPrefetch));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[d], s, 0, 0, 0);
-    if (d % EVERY == EVERY - 1 && d / EVERY < NP) pump.copy(slot0 + d / EVERY);
+    if (d % EVERY == EVERY - 1 && d / EVERY < NP) pump.copy(slot0 + d / EVERY, false, d / EVERY == 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
   }
   return s;
@@ -672,9 +685,12 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
 // taken on the raw dot products and each probability is
 // exp2(fma(s, scale, -m_ref)).  Branch-free: a branch here would split the
 // MFMA streams this code is scheduled into.
+template <bool SKIP_FULL>
 __device__ __forceinline__ float tile_max(f32x16& s, uint32_t bits, SoftmaxState& st,
                                           float scale_log2) {
-  {
+  // SKIP_FULL: a tile of valid keys (wave-uniform test) needs no mask; the
+  // branch costs the 128-head kernel registers it does not have.
+  if (!SKIP_FULL || bits != 0xFFFFFFFFu) {
     const uint32_t mlane = bits >> (4 * (lane_id() >> 5));
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -704,7 +720,7 @@ __device__ __forceinline__ float prob(float s, float neg_ref, float scale_log2) 
 // (+8) sits at chunk (4ct ^ vc ^ swz) of its 256 B group: a row base plus
 // (64(ct%4) ^ w) with one w per row half.  MFMA n covers value tile
 // ct = n % 16, step u = n / 16.
-template <int D_QK, int EVERY, class Pump>
+template <int D_QK, int EVERY, bool SKIP_FULL, class Pump>
 __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r0, f32x16 s,
                                                 uint32_t bits, f32x16 (&acc)[kDV / 32],
                                                 SoftmaxState& st, float scale_log2, Pump& pump,
@@ -734,7 +750,7 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
     lo[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, false));
     hi[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, true));
   }
-  const float neg_ref = tile_max(s, bits, st, scale_log2);
+  const float neg_ref = tile_max<SKIP_FULL>(s, bits, st, scale_log2);
   float rsum = 0.f;
   bf16x8 pf[2];
 #pragma unroll
@@ -768,7 +784,7 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
         pf[1][e] = (__bf16)p1[e];
       }
     }
-    if (n % EVERY == EVERY - 1) pump.copy(slot0 + n / EVERY);
+    if (n % EVERY == EVERY - 1) pump.copy(slot0 + n / EVERY, false, n / EVERY == 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l_sum += pair_sum32(rsum);
@@ -792,8 +808,8 @@ __device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t m
     const uint32_t bits = (uint32_t)(mask >> r0);
     if (bits != 0u) {
       const f32x16 s = tile_scores<D_QK, EVERY, kPerTile / 2>(buf, r0, qf, pump, kt * kPerTile);
-      tile_softmax_pv<D_QK, EVERY>(buf, r0, s, bits, acc, st, scale_log2, pump,
-                                   kt * kPerTile + kPerTile / 2);
+      tile_softmax_pv<D_QK, EVERY, KS == 2 && D_QK == 512>(buf, r0, s, bits, acc, st, scale_log2,
+                                                           pump, kt * kPerTile + kPerTile / 2);
     }
   }
 }
@@ -834,7 +850,7 @@ struct WidePipe {
     // which nothing reads any more.
     const int row0 = GatherPump<D_QK>::kSlots * wave;
     GatherPump<D_QK> pump{rsrc, nxt, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
-                          lane_id() * 16, 0u, 0u};
+                          lane_id() * 16, 0u, 0u, 0u};
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
     if (wmask != 0)
       wide_block<D_QK, KS, kEvery>(cur, mask_cur, koff, qf, acc, st, a.scale_log2, pump);
@@ -911,7 +927,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
         const int row0 = GatherPump<D_QK>::kSlots * wave;
         stage_rope<D_QK>(buf0, rsrc, offs, wave);
         GatherPump<D_QK>{rsrc, buf0, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
-                         lane_id() * 16, 0u, 0u}
+                         lane_id() * 16, 0u, 0u, 0u}
             .copy_all();
       }
       using P = WidePipe<D_QK, KS, PAGED>;
