@@ -571,10 +571,32 @@ struct GatherPump {
   }
   // Copies the slots that were not copied in the MFMA stream (all of them for
   // a block whose tiles this wave skipped).
+  // LOOP: a run-time loop over the missing slots (usually none: one test
+  // instead of sixteen); otherwise one unrolled test per slot, which is what
+  // the register allocation of the 64-head kernel tolerates.
+  template <bool LOOP>
   __device__ __forceinline__ void finish() {
+    if (LOOP) {
+      for (uint32_t miss = ~issued & ((1u << kSlots) - 1); miss != 0; miss &= miss - 1)
+        copy_any(__builtin_ctz(miss));
+    } else {
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s)
-      if (!((issued >> s) & 1u)) copy(s, true);
+      for (int s = 0; s < kSlots; ++s)
+        if (!((issued >> s) & 1u)) copy(s, true);
+    }
+  }
+  // copy() for a slot known only at run time (the offset selection branches).
+  __device__ __forceinline__ void copy_any(int s) {
+    win = (uint32_t)(uintptr_t)(buf + (row0 + (s & ~3)) * T::kNopeBytes);
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readlane(offw, s);
+    const uint32_t voff = ((uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4)) + so;
+    constexpr int B = T::kNopeBytes;
+    switch (s & 3) {
+      case 0: dma_table16<0 * B>(rsrc, voff, win); break;
+      case 1: dma_table16<1 * B>(rsrc, voff, win); break;
+      case 2: dma_table16<2 * B>(rsrc, voff, win); break;
+      default: dma_table16<3 * B>(rsrc, voff, win); break;
+    }
   }
 };
 
@@ -751,14 +773,15 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
     hi[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, true));
   }
   const float neg_ref = tile_max<SKIP_FULL>(s, bits, st, scale_log2);
-  float rsum = 0.f;
+  float p0[8];
   bf16x8 pf[2];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = prob(s[e], neg_ref, scale_log2);
-    rsum += p;
-    pf[0][e] = (__bf16)p;
+    p0[e] = prob(s[e], neg_ref, scale_log2);
+    pf[0][e] = (__bf16)p0[e];
   }
+  // Pairwise sums (short dependency chains).
+  float rsum = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p0[4] + p0[5]) + (p0[6] + p0[7]));
   // Step 1's probabilities, two per MFMA of step 0 (sched barriers below keep
   // them there).
   float p1[8];
@@ -779,10 +802,8 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
       p1[2 * n + 1] = prob(s[9 + 2 * n], neg_ref, scale_log2);
     } else if (n == 4) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        rsum += p1[e];
-        pf[1][e] = (__bf16)p1[e];
-      }
+      for (int e = 0; e < 8; ++e) pf[1][e] = (__bf16)p1[e];
+      rsum += ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
     }
     if (n % EVERY == EVERY - 1) pump.copy(slot0 + n / EVERY, false, n / EVERY == 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -854,7 +875,7 @@ struct WidePipe {
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
     if (wmask != 0)
       wide_block<D_QK, KS, kEvery>(cur, mask_cur, koff, qf, acc, st, a.scale_log2, pump);
-    pump.finish();
+    pump.template finish<KS == 1>();
     mask_cur = mn.mask;
     ah = Ahead{ah.idx2, page2, idx3};
   }
