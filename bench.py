@@ -49,7 +49,14 @@ def parse():
                     help="run only a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--ingest-counters", metavar="DIR",
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR (pmc_<workload>_<counter>/ "
-                         "and pmc_copy_<counter>/) into profiles/traffic_<workload>.json; no GPU needed")
+                         "and pmc_copy_<counter>/), and the MFMA-busy runs (pmc_<workload>_MFMA/), into "
+                         "profiles/traffic_<workload>.json; no GPU needed")
+    ap.add_argument("--attainable", action="store_true",
+                    help="measure this device's attainable dense bf16 MFMA rate (an MFMA loop) and HBM "
+                         "bandwidth (a streaming copy) into profiles/attainable_peaks.json")
+    ap.add_argument("--replicas", type=int, default=3,
+                    help="decode: also time calls that rotate over this many copies of the inputs "
+                         "(cold Infinity Cache); 0 disables")
     return ap.parse_args()
 
 
@@ -249,16 +256,22 @@ def kernel_source_digest():
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def stored_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, if it was taken on the current kernel source."""
+def stored_counters(workload):
+    """The committed rocprofv3 counter record of this workload, if it was
+    taken on the current kernel source (else None)."""
     f = PROFILES / f"traffic_{workload}.json"
     if not f.exists():
         return None
     rec = json.loads(f.read_text())
     if rec.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch from the committed counter record, or None."""
+    rec = stored_counters(workload)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
 def roofline(workload, case, counts, kernel_ms):
@@ -315,13 +328,83 @@ def ingest_counters(d):
                "dispatches": [len(f), len(wr)],
                "copy_calibration_factor": {"FETCH_SIZE": cal["FETCH_SIZE"], "WRITE_SIZE": cal["WRITE_SIZE"]},
                "command": f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -o run --output-format csv -- "
-                          f"python3 -u bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0; "
+                          f"python3 -u bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0; "
                           f"calibration: ... -- python3 -u bench.py --calibrate-copy",
                "kernel_source_sha256_16": digest}
+        busy = _mfma_busy(d / f"pmc_{w}_MFMA")
+        if busy is not None:
+            rec.update(busy)
         PROFILES.mkdir(exist_ok=True)
         (PROFILES / f"traffic_{w}.json").write_text(json.dumps(rec, indent=1) + "\n")
         print(f"{w}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch "
               f"(fetch {fetch / 1e6:.1f}, write {write / 1e6:.1f})")
+
+
+def _mfma_busy(sub):
+    """MFMA-busy fraction of the attention kernel from one rocprofv3 run with
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.  The SQ counter sums busy
+    cycles over every SIMD; GRBM_GUI_ACTIVE sums the active cycles of every
+    XCD; the agent record gives the SIMD and XCD counts:
+        busy = MFMA_BUSY / ((GUI_ACTIVE / Num_Xcc) * Simd_Count)."""
+    import csv
+    f = sub / "run_counter_collection.csv"
+    a = sub / "run_agent_info.csv"
+    if not f.exists() or not a.exists():
+        return None
+    simd = xcc = None
+    with open(a) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Name", "").startswith("gfx"):
+                simd, xcc = int(r["Simd_Count"]), int(r["Num_Xcc"])
+    vals = {}
+    with open(f) as fh:
+        rows = [r for r in csv.DictReader(fh) if "sparse_mla_fwd" in r["Kernel_Name"]]
+    if not rows or not simd:
+        return None
+    name = rows[0]["Kernel_Name"]
+    for r in rows:
+        if r["Kernel_Name"] == name:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    busy = statistics.fmean(vals["SQ_VALU_MFMA_BUSY_CYCLES"])
+    gui = statistics.fmean(vals["GRBM_GUI_ACTIVE"])
+    return {"mfma_busy_frac": busy / ((gui / xcc) * simd),
+            "mfma_busy_cycles_mean": busy, "grbm_gui_active_mean": gui,
+            "mfma_busy_command": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -o run "
+                                 f"--output-format csv -- python3 -u bench.py --workload "
+                                 f"{sub.name[len('pmc_'):-len('_MFMA')]} --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0"}
+
+
+def attainable_peaks():
+    """This device's attainable dense bf16 MFMA rate (an MFMA loop on every
+    SIMD, from the benchmark's probe library) and HBM bandwidth (a streaming
+    device copy of 4 GiB: reads and writes counted)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(str(ROOT / "sparse_top_mla_amd" / "libsmla_probe.so"))
+    lib.smla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.smla_probe_mfma_count.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.smla_probe_mfma_count.restype = ctypes.c_longlong
+    props = torch.cuda.get_device_properties(0)
+    blocks, iters = props.multi_processor_count * 4, 4096
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    launch = lambda: lib.smla_probe_mfma(out.data_ptr(), blocks, iters, stream)  # noqa: E731
+    assert launch() == 0
+    _, per = time_steps(launch, 10, 3)
+    mfma_ms = statistics.median(per)
+    flops = lib.smla_probe_mfma_count(blocks, iters) * 2.0 * 32 * 32 * 16
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_()
+    dst = torch.empty_like(src)
+    _, per_c = time_steps(lambda: dst.copy_(src), 10, 3)
+    copy_ms = statistics.median(per_c)
+    return {"mfma_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "hbm_gbs": 2.0 * n / (copy_ms * 1e-3) / 1e9,
+            "mfma_probe": f"{blocks} workgroups x 8 waves x {iters} x 4 independent "
+                          f"v_mfma_f32_32x32x16_bf16, median of 10 launches: {mfma_ms:.3f} ms",
+            "copy_probe": f"torch device copy of {n >> 30} GiB (read + write), median of 10: "
+                          f"{copy_ms:.3f} ms",
+            "device": props.name, "command": "python3 bench.py --attainable"}
 
 
 def calibrate_copy():
@@ -352,6 +435,12 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.attainable:
+        rec = attainable_peaks()
+        PROFILES.mkdir(exist_ok=True)
+        (PROFILES / "attainable_peaks.json").write_text(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps(rec), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -365,6 +454,21 @@ def main():
     value = counts["flops"] / (ms_per_step * 1e-3) / 1e12
 
     variants = {}
+    if is_decode(case) and args.replicas > 1:
+        # Cold variant: rotate over copies of the inputs, so that a call does
+        # not find the previous call's KV rows in the Infinity Cache.
+        calls = [call] + [gpu_call(case, dev) for _ in range(args.replicas - 1)]
+        k = [0]
+
+        def rotating():
+            calls[k[0] % len(calls)]()
+            k[0] += 1
+        ms_cold, per_cold = time_steps(rotating, args.steps, args.warmup)
+        variants[f"cold_{args.replicas}_replicas"] = {
+            "ms_per_call": ms_cold, "kernel_ms": statistics.fmean(per_cold),
+            "kernel_ms_median": statistics.median(per_cold),
+            "hbm_gbs_algorithmic": counts["bytes"] / (statistics.fmean(per_cold) * 1e-3) / 1e9}
+        del calls
     if args.workload == "prefill_h64":
         case_len = make_case("prefill_h64_len")
         call_len = gpu_call(case_len, dev)
@@ -404,6 +508,17 @@ def main():
     }
     if variants:
         result["variants"] = variants
+    rec = stored_counters(args.workload)
+    if rec is not None and "mfma_busy_frac" in rec:
+        # The rocprof MFMA-busy fraction of this kernel (same code), beside the
+        # algorithmic fraction in roofline.frac.
+        result["rocprof_mfma_busy_frac"] = rec["mfma_busy_frac"]
+    peaks = PROFILES / "attainable_peaks.json"
+    if peaks.exists():
+        p = json.loads(peaks.read_text())
+        att = p["hbm_gbs"] if is_decode(case) else p["mfma_tflops"]
+        result["attainable"] = {"mfma_tflops": p["mfma_tflops"], "hbm_gbs": p["hbm_gbs"],
+                                "frac_of_attainable": result["roofline"]["achieved"] / att}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(case, counts, args.cpu_seconds)
     else:

@@ -1,0 +1,63 @@
+// Attainable-peak probe for the benchmark (not part of the attention path).
+//
+// smla_probe_mfma runs back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD:
+// each wave keeps four independent accumulator chains, two waves per SIMD,
+// so the matrix cores never wait on a result.  The host divides the FLOPs
+// (2 * 32 * 32 * 16 per MFMA) by the measured time to get the dense bf16
+// MFMA rate this device attains at its running clock.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChains = 4;
+
+__global__ void __launch_bounds__(512) mfma_loop(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (float)((lane + e) & 7));
+    b[e] = (__bf16)(0.002f * (float)((lane * 3 + e) & 7));
+  }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) acc[k] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < kChains; ++k)
+      acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kChains; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[k][e];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Launches `blocks` workgroups of 512 threads (8 waves), each wave issuing
+// iters * 4 MFMAs; `out` holds blocks * 512 floats.  Returns 0 on success,
+// else the HIP error code of the launch.
+int smla_probe_mfma(float* out, int blocks, int iters, void* stream) {
+  if (!out || blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream), out,
+                     iters);
+  return (int)hipGetLastError();
+}
+
+// MFMAs one launch issues.
+long long smla_probe_mfma_count(int blocks, int iters) {
+  return (long long)blocks * 8 * iters * kChains;
+}
+
+}  // extern "C"
