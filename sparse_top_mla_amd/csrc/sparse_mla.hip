@@ -572,17 +572,23 @@ struct GatherPump {
   // Copies the slots that were not copied in the MFMA stream (all of them for
   // a block whose tiles this wave skipped).
   // LOOP: a run-time loop over the missing slots (usually none: one test
-  // instead of sixteen); otherwise one unrolled test per slot, which is what
-  // the register allocation of the 64-head kernel tolerates.
+  // instead of sixteen); otherwise unrolled tests.
   template <bool LOOP>
   __device__ __forceinline__ void finish() {
     if (LOOP) {
       for (uint32_t miss = ~issued & ((1u << kSlots) - 1); miss != 0; miss &= miss - 1)
         copy_any(__builtin_ctz(miss));
     } else {
+      // A test per four slots, then per slot (tests only; the copies stay
+      // one per slot, which is what the register allocation of the 64-head
+      // kernel tolerates).
 #pragma unroll
-      for (int s = 0; s < kSlots; ++s)
-        if (!((issued >> s) & 1u)) copy(s, true);
+      for (int q = 0; q < kSlots; q += 4)
+        if (((issued >> q) & 15u) != 15u) {
+#pragma unroll
+          for (int s = q; s < q + 4; ++s)
+            if (!((issued >> s) & 1u)) copy(s, true);
+        }
     }
   }
   // copy() for a slot known only at run time (the offset selection branches).
