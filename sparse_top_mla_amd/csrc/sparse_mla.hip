@@ -748,7 +748,7 @@ __device__ __forceinline__ float prob(float s, float neg_ref, float scale_log2) 
 // (+8) sits at chunk (4ct ^ vc ^ swz) of its 256 B group: a row base plus
 // (64(ct%4) ^ w) with one w per row half.  MFMA n covers value tile
 // ct = n % 16, step u = n / 16.
-template <int D_QK, int EVERY, bool SKIP_FULL, class Pump>
+template <int D_QK, int EVERY, int NP, bool SKIP_FULL, class Pump>
 __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r0, f32x16 s,
                                                 uint32_t bits, f32x16 (&acc)[kDV / 32],
                                                 SoftmaxState& st, float scale_log2, Pump& pump,
@@ -811,7 +811,7 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
       for (int e = 0; e < 8; ++e) pf[1][e] = (__bf16)p1[e];
       rsum += ((p1[0] + p1[1]) + (p1[2] + p1[3])) + ((p1[4] + p1[5]) + (p1[6] + p1[7]));
     }
-    if (n % EVERY == EVERY - 1) pump.copy(slot0 + n / EVERY, false, n / EVERY == 0);
+    if (n % EVERY == EVERY - 1 && n / EVERY < NP) pump.copy(slot0 + n / EVERY, false, n / EVERY == 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l_sum += pair_sum32(rsum);
@@ -819,24 +819,32 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
 
 // One 64-key block with a valid key for one wave: its 32-key tiles in
 // [koff, koff + 64/KS); tiles without a valid key are skipped (their gather
-// slots are then copied by GatherPump::finish).  Each tile owns an equal
-// share of the wave's gather slots, half under S^T and half under P*V.
+// slots are then copied by GatherPump::finish).  The first tile takes every
+// gather slot of the wave, as many under S^T as its MFMAs allow at one per
+// EVERY and the rest under P*V, so that the copies leave early.
 template <int D_QK, int KS, int EVERY>
 __device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t mask, int koff,
                                            const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                            f32x16 (&acc)[kDV / 32], SoftmaxState& st,
                                            float scale_log2, GatherPump<D_QK>& pump) {
   constexpr int kTiles = kBlockKeys / KS / 32;
-  constexpr int kPerTile = GatherPump<D_QK>::kSlots / kTiles;
-  static_assert(kPerTile / 2 == 2 * kDV / 32 / EVERY, "gather slots per P*V pass");
+  constexpr int kSlots = GatherPump<D_QK>::kSlots;
+  constexpr int kSteps = WideTile<D_QK>::kDSteps;
+  constexpr int NS = kSteps / EVERY < kSlots ? kSteps / EVERY : kSlots;  // under S^T
+  constexpr int NV = kSlots - NS;                                       // under P*V
+  constexpr bool SF = KS == 2 && D_QK == 512;
+  static_assert(NV * EVERY <= 2 * kDV / 32, "gather slots per P*V pass");
 #pragma unroll
   for (int kt = 0; kt < kTiles; ++kt) {
     const int r0 = koff + 32 * kt;
     const uint32_t bits = (uint32_t)(mask >> r0);
     if (bits != 0u) {
-      const f32x16 s = tile_scores<D_QK, EVERY, kPerTile / 2>(buf, r0, qf, pump, kt * kPerTile);
-      tile_softmax_pv<D_QK, EVERY, KS == 2 && D_QK == 512>(buf, r0, s, bits, acc, st, scale_log2,
-                                                           pump, kt * kPerTile + kPerTile / 2);
+      const f32x16 s = kt == 0 ? tile_scores<D_QK, EVERY, NS>(buf, r0, qf, pump, 0)
+                               : tile_scores<D_QK, EVERY, 0>(buf, r0, qf, pump, 0);
+      if (kt == 0)
+        tile_softmax_pv<D_QK, EVERY, NV, SF>(buf, r0, s, bits, acc, st, scale_log2, pump, NS);
+      else
+        tile_softmax_pv<D_QK, EVERY, 0, SF>(buf, r0, s, bits, acc, st, scale_log2, pump, 0);
     }
   }
 }
@@ -851,9 +859,13 @@ struct Ahead {
 template <int D_QK, int KS, bool PAGED>
 struct WidePipe {
   using T = WideTile<D_QK>;
-  // One gather row per this many MFMAs: 16 rows per wave and block against
-  // 64 (KS = 2) or 136 (KS = 1, d_qk = 576) MFMAs per wave and block.
-  static constexpr int kEvery = KS == 2 ? 4 : 8;
+  // The gather of block t+1 leaves in the first tile of block t, one row
+  // per kEvery MFMAs (16 rows per wave and block), so that the rows have
+  // the rest of the block to land.  Paged rows come from HBM, and there every
+  // fourth MFMA keeps the copies' issue cost under the MFMAs; every second
+  // one suits rows that mostly hit in the caches (prefill).  Measured: both
+  // beat spreading the copies over the whole block.
+  static constexpr int kEvery = PAGED && KS == 1 ? 4 : 2;
   // One half-iteration: block t lives in `cur` (already gathered); gather
   // block t+1 into `nxt` while computing block t.
   static __device__ __forceinline__ void step(const FwdArgs& a, const LDS_AS uint8_t* cur,
