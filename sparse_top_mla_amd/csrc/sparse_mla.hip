@@ -40,6 +40,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -132,9 +133,9 @@ struct TailRound {
   int v[4];
 };
 
-__device__ __forceinline__ TailRound load_tail_round(const int32_t* idx_row, int end) {
+__device__ __forceinline__ TailRound load_tail_round(const int32_t* idx_row, int end,
+                                                     int lane = lane_id()) {
   TailRound t;
-  const int lane = lane_id();
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int p = end - 256 + e * 64 + lane;
@@ -418,8 +419,9 @@ struct BlockMeta {
   bool ok;        // lane j: bit j of mask
 };
 
-__device__ __forceinline__ int load_index(const int32_t* idx_row, int blk, int topk) {
-  const int pos = blk * kBlockKeys + lane_id();
+__device__ __forceinline__ int load_index(const int32_t* idx_row, int blk, int topk,
+                                          int lane = lane_id()) {
+  const int pos = blk * kBlockKeys + lane;
   return pos < topk ? idx_row[pos] : -1;
 }
 
@@ -465,6 +467,17 @@ __device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int i
 // the same in every block (LDS operand offsets summed with the two buffer
 // bases) would otherwise each be hoisted into a register of their own.
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
+
+// The lane index, computed where it is called: lane_id() is a pure builtin
+// that the compiler computes once and keeps (or spills) for the whole kernel.
+// Values derived from this one are computed per row of the row loop instead
+// of being hoisted out of it, where they would hold registers across every
+// block.
+__device__ __forceinline__ int lane_fresh() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
 
 // The gather reads the KV table through one raw buffer resource
 // whose base sits kSpanBias bytes below the table (records: span + bias).
@@ -899,6 +912,55 @@ struct WidePipe {
   }
 };
 
+// Row of a workgroup's turn k, or -1 once it has none left.  The grid is at
+// most one workgroup per CU; positions p = 0, 1, ... go to the workgroups in
+// snake order (0..G-1, then G-1..0, ...), so each gets an even share of long
+// and short rows.  Prefill takes its rows from the last one down (the rows
+// of a causal prefill grow with the row number).
+__device__ __forceinline__ int turn_row(const FwdArgs& a, int k, bool paged) {
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  const long long p = (long long)k * G + ((k & 1) ? G - 1 - b : b);
+  if (p >= a.rows) return -1;
+  return paged ? (int)p : a.rows - 1 - (int)p;
+}
+
+// What a row needs before its first block: the explicit length (or the last
+// round of its index list, for the tail scan) and its first three index
+// blocks.
+template <bool DYNAMIC>
+struct RowHead {
+  TailRound first;
+  int tl;
+  int idx0, idx1, idx2;
+};
+
+template <bool DYNAMIC>
+__device__ __forceinline__ RowHead<DYNAMIC> load_row_head(const FwdArgs& a, int row) {
+  RowHead<DYNAMIC> h;
+  const int lane = lane_fresh();
+  const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+  h.tl = 0;
+  if (DYNAMIC)
+    h.tl = a.topk_length[row];
+  else
+    h.first = load_tail_round(idx_row, a.topk, lane);
+  h.idx0 = load_index(idx_row, 0, a.topk, lane);
+  h.idx1 = load_index(idx_row, 1, a.topk, lane);
+  h.idx2 = load_index(idx_row, 2, a.topk, lane);
+  return h;
+}
+
+// The MFMA B operand of the row's query slice: lane (half, hl) holds
+// elements 16d + 8half .. +7 of head `head` in qf[d].
+template <int D_QK>
+__device__ __forceinline__ void load_query(bf16x8 (&qf)[WideTile<D_QK>::kDSteps], const FwdArgs& a,
+                                           int row, int head, int half) {
+  const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * D_QK + half * 8;
+#pragma unroll
+  for (int d = 0; d < WideTile<D_QK>::kDSteps; ++d)
+    qf[d] = *reinterpret_cast<const bf16x8*>(qp + d * 16);
+}
+
 template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_wide_kernel(FwdArgs a) {
@@ -915,34 +977,30 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   const int hl = lane & 31, half = lane >> 5;
   const int koff = ks * (kBlockKeys / KS);
 
-  // Heavy rows of a causal prefill come last; start them first.
-  const int row = PAGED ? (int)blockIdx.x : a.rows - 1 - (int)blockIdx.x;
+  const int head = hg * 32 + hl;
+  // The per-head sinks sit in LDS for the epilogues: a global load there
+  // would be counted behind the next row's query loads and wait for them.
+  __shared__ float sink_lds[SINK ? kWideWaves / KS * 32 : 1];
+  if (SINK && (int)threadIdx.x < kWideWaves / KS * 32) sink_lds[threadIdx.x] = a.attn_sink[threadIdx.x];
+  // (The first barrier of the row loop comes before the first epilogue.)
+
+  // The workgroup's rows (persistent grid), each started while the previous
+  // row's epilogue runs: its length, first indices and query slice are
+  // loaded before that epilogue.
+  int turn = 0;
+  int row = turn_row(a, turn, PAGED);
+  bf16x8 qf[T::kDSteps];
+  load_query<D_QK>(qf, a, row, head, half);
+  for (;;) {
+  const RowHead<DYNAMIC> rh = load_row_head<DYNAMIC>(a, row);
   const int seq = row / a.rows_per_seq;
   const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
   const int32_t* idx_row = a.indices + (size_t)row * a.topk;
-
-  // Prologue: tail-scan round (or explicit length), the first index blocks,
-  // then the query slice; the length is resolved and block 0 is gathered
-  // while the query loads are still in flight.
-  TailRound first;
-  int tl = 0;
-  if (DYNAMIC)
-    tl = a.topk_length[row];
-  else
-    first = load_tail_round(idx_row, a.topk);
+  const int L = DYNAMIC ? clamp_length(rh.tl, a.topk) : finish_tail_scan(rh.first, idx_row, a.topk, bound);
+  const int nblk = (L + kBlockKeys - 1) / kBlockKeys;
   // Kept for a recompute: loading them again there would make the compiler
   // wait for every outstanding load (the query rows included) at the join.
-  const int idx0 = load_index(idx_row, 0, a.topk);
-  const int idx1 = load_index(idx_row, 1, a.topk);
-  const int idx2 = load_index(idx_row, 2, a.topk);
-  const int head = hg * 32 + hl;
-  const float sink = SINK ? a.attn_sink[head] : 0.f;  // read here, not in the epilogue
-  const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * D_QK + half * 8;
-  bf16x8 qf[T::kDSteps];
-#pragma unroll
-  for (int d = 0; d < T::kDSteps; ++d) qf[d] = *reinterpret_cast<const bf16x8*>(qp + d * 16);
-  const int L = DYNAMIC ? clamp_length(tl, a.topk) : finish_tail_scan(first, idx_row, a.topk, bound);
-  const int nblk = (L + kBlockKeys - 1) / kBlockKeys;
+  const int idx0 = rh.idx0, idx1 = rh.idx1, idx2 = rh.idx2;
 
   f32x16 acc[kDV / 32];
   SoftmaxState st;
@@ -959,7 +1017,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       const BlockMeta m0 = block_meta<PAGED>(a, ok0, idx0, pg0);
       uint64_t mask_cur = m0.mask;
       Ahead ah{idx1, pg1, idx2};
-      __syncthreads();  // a previous attempt may still read the buffers
+      __syncthreads();  // a previous attempt or row may still read the buffers
       {
         const u32x4s rsrc = table_rsrc(a);
         const int offs = GatherPump<D_QK>::row_offsets(m0);
@@ -985,6 +1043,13 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     if (!__syncthreads_or(st.overflow) || attempt == 1) break;
     m_preset = st.m_max;
   }
+
+  // Lane values for the rest of the row (see lane_fresh), then the next
+  // row's query slice, which lands under this row's epilogue.
+  const int lane = lane_fresh(), hl = lane & 31, half = lane >> 5, head = hg * 32 + hl;
+  const float sink = SINK ? sink_lds[head] : 0.f;
+  const int next = turn_row(a, ++turn, PAGED);
+  if (next >= 0) load_query<D_QK>(qf, a, next, head, half);
 
   // Combine, normalise, store.  acc[ct][i] = O[head][c = 32ct + 8(i/4) + 4half + i%4].
   float m_fin = st.m_ref, l_fin = st.l_sum, mx_fin = st.m_max, a_self = 1.f;
@@ -1020,6 +1085,10 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     ml_v = mx_fin * kLn2;
     lse_v = (m_fin + __log2f(l_fin)) * kLn2;
   }
+  if (half == 0 && (KS == 1 || ks == 0)) {
+    a.lse[(size_t)row * a.h_q + head] = lse_v;
+    a.max_logits[(size_t)row * a.h_q + head] = ml_v;
+  }
   if (KS == 2) {
     // Each wave of a head group finishes one half of the value columns
     // (wave ks: columns 256ks .. 256ks + 255, i.e. ct in [8ks, 8ks + 8)).  It
@@ -1044,15 +1113,20 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
                   acc[ct][4 * j + 3] * scale};
     }
     __syncthreads();
-    f32x4 o[kHalf][4];
+    // Rounded to bf16 as they are combined (the next row's query slice may
+    // be in flight into half of the registers).
+    bf16x4 o[kHalf][4];
 #pragma unroll
     for (int c = 0; c < kHalf; ++c) {
       const int ct = K * kHalf + c;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[c][j] = f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
-                        acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale} +
-                  *reinterpret_cast<const LDS_AS f32x4*>(mine + ((c * 4 + j) * 64 + lane) * 4);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = f32x4{acc[ct][4 * j] * scale, acc[ct][4 * j + 1] * scale,
+                              acc[ct][4 * j + 2] * scale, acc[ct][4 * j + 3] * scale} +
+                        *reinterpret_cast<const LDS_AS f32x4*>(mine + ((c * 4 + j) * 64 + lane) * 4);
+        o[c][j] = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one value tile of partials in flight at a time
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // partials read before the tile overwrites them
     // Half row h (512 B) at h * 512; its chunk c (16 B) sits at chunk c ^ h.
@@ -1060,11 +1134,9 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < kHalf; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x4 o4 = {(__bf16)o[c][j][0], (__bf16)o[c][j][1], (__bf16)o[c][j][2],
-                           (__bf16)o[c][j][3]};
-        *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * kDV + (((4 * c + j) ^ hl) << 4) + 8 * half) = o4;
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * kDV + (((4 * c + j) ^ hl) << 4) + 8 * half) =
+            o[c][j];
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is complete for every lane
     const int hsub = lane >> 5, chunk = lane & 31;
     uint8_t* obase = reinterpret_cast<uint8_t*>(a.out + ((size_t)row * a.h_q + hg * 32) * kDV) +
@@ -1080,7 +1152,6 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       finish_half(std::integral_constant<int, 0>{});
     else
       finish_half(std::integral_constant<int, 1>{});
-    if (ks == 1) return;
   } else {
     // The output goes through LDS so that every global store writes one
     // head's whole 1 KiB row: stored straight from the accumulator layout, a
@@ -1104,11 +1175,11 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
     }
   }
-  if (half == 0) {
-    a.lse[(size_t)row * a.h_q + head] = lse_v;
-    a.max_logits[(size_t)row * a.h_q + head] = ml_v;
+  if (next < 0) break;
+  row = next;
   }
 }
+
 
 // Row lengths from the same routines the attention kernels use; one wave per row.
 __global__ void __launch_bounds__(256) row_lengths_kernel(const int32_t* indices,
@@ -1174,11 +1245,30 @@ smla_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   return SMLA_OK;
 }
 
+// Compute units of the current device (cached per device), or -1.
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
 smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
   if ((args.h_q / 32) * KS != kWideWaves)
     return fail(SMLA_ERR_UNSUPPORTED, "wide kernel needs h_q=%d (KS=%d)", 32 * kWideWaves / KS, KS);
-  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, KS, PAGED, DYNAMIC, SINK>), dim3(args.rows),
+  const int cus = cu_count();
+  if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
+  const int grid = args.rows < cus ? args.rows : cus;  // one workgroup per CU, each loops over rows
+  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, KS, PAGED, DYNAMIC, SINK>), dim3(grid),
                      dim3(kWideWaves * 64), 0, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
