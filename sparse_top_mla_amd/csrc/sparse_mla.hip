@@ -501,6 +501,18 @@ __device__ __forceinline__ u32x4s table_rsrc(const FwdArgs& a) {
   return rs;
 }
 
+// The same form of resource over one row's query slice (h_q rows of d_qk),
+// read by the gather as if it were a KV table with head j at row j.
+__device__ __forceinline__ u32x4s query_rsrc(const FwdArgs& a, int row, int row_bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)(a.q + (size_t)row * a.h_q * (row_bytes / 2)) - kSpanBias;
+  u32x4s rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;
+  rs[2] = __builtin_amdgcn_readfirstlane((uint32_t)(a.h_q * row_bytes) + kSpanBias);
+  rs[3] = 0x00020000u;
+  return rs;
+}
+
 // NOP: the wait state an LDS DMA needs after an M0 write (the compiler writes
 // M0 for the operand only when its value changes).
 template <int OFF, bool NOP = true>
@@ -886,20 +898,28 @@ struct WidePipe {
                                               int bound, int seq, const int32_t* idx_row,
                                               int wave, int koff, uint64_t& mask_cur, Ahead& ah,
                                               const bf16x8 (&qf)[T::kDSteps],
-                                              f32x16 (&acc)[kDV / 32], SoftmaxState& st) {
+                                              f32x16 (&acc)[kDV / 32], SoftmaxState& st,
+                                              int q_row) {
     wait_vm_all();
     __syncthreads();
     const bool have_nxt = t + 1 < nblk;
-    const BlockMeta mn =
-        block_meta<PAGED>(a, index_ok(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
-    const u32x4s rsrc = table_rsrc(a);
+    // The last step of a 64-head row gathers the query slice of row q_row
+    // (64 rows of d_qk: one block buffer) into `nxt` instead, head j as row j.
+    // (Wave-uniform; readfirstlane says so to the compiler, which must keep
+    // the selected resource in scalar registers.)
+    const bool q_nxt = __builtin_amdgcn_readfirstlane((int)(!have_nxt && q_row >= 0)) != 0;
+    BlockMeta mn = block_meta<PAGED>(a, index_ok(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
+    if (q_nxt) mn = BlockMeta{~0ull, lane_id(), true};
+    u32x4s rsrc = q_nxt ? query_rsrc(a, q_row, T::kRowBytes) : table_rsrc(a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
     const int offs = GatherPump<D_QK>::row_offsets(mn);
-    if (have_nxt) stage_rope<D_QK>(nxt, rsrc, offs, wave);
+    if (have_nxt || q_nxt) stage_rope<D_QK>(nxt, rsrc, offs, wave);
     const bool ok2 = index_ok(ah.idx2, t + 2, L, bound);
     const int page2 = page_lookup<PAGED>(a, seq, ok2, ah.idx2);
     const int idx3 = load_index(idx_row, t + 3, a.topk);
-    // Past the last block the mask is empty: the copies zero-fill `nxt`,
-    // which nothing reads any more.
+    // Past the last block (without a query slice to gather) the mask is
+    // empty: the copies zero-fill `nxt`, which nothing reads any more.
     const int row0 = GatherPump<D_QK>::kSlots * wave;
     GatherPump<D_QK> pump{rsrc, nxt, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
                           lane_id() * 16, 0u, 0u, 0u};
@@ -961,6 +981,23 @@ __device__ __forceinline__ void load_query(bf16x8 (&qf)[WideTile<D_QK>::kDSteps]
     qf[d] = *reinterpret_cast<const bf16x8*>(qp + d * 16);
 }
 
+// The same operand from a block buffer that the gather filled with the
+// row's 64 head rows (head j as row j, laid out like a KV block): head group
+// hg reads rows 32hg .. 32hg + 31 the way tile_scores reads key rows.
+template <int D_QK>
+__device__ __forceinline__ void load_query_lds(bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
+                                               const LDS_AS uint8_t* buf, int hg, int lane) {
+  using T = WideTile<D_QK>;
+  const int hl = lane & 31, half = lane >> 5;
+  const int krow = (32 * hg + hl) * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
+  const int rrow = T::kRopeBase + (32 * hg + hl) * T::kRopeBytes, rw = (half ^ rope_swz(hl)) << 4;
+#pragma unroll
+  for (int d = 0; d < T::kDSteps; ++d)
+    qf[d] = *reinterpret_cast<const LDS_AS bf16x8*>(
+        d < 32 ? buf + krow + (d >> 3) * 256 + ((32 * (d & 7)) ^ kw)
+               : buf + rrow + ((32 * (d - 32)) ^ rw));
+}
+
 template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_wide_kernel(FwdArgs a) {
@@ -1001,6 +1038,11 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   // Kept for a recompute: loading them again there would make the compiler
   // wait for every outstanding load (the query rows included) at the join.
   const int idx0 = rh.idx0, idx1 = rh.idx1, idx2 = rh.idx2;
+  const int next = turn_row(a, ++turn, PAGED);
+  // 64 heads: the next row's query slice fits one block buffer, and the
+  // last block step gathers it there (contiguous 1 KiB rows; loaded straight
+  // into the MFMA operand layout, each load would touch 32 head rows).
+  const int q_row = KS == 2 && nblk > 0 ? next : -1;
 
   f32x16 acc[kDV / 32];
   SoftmaxState st;
@@ -1030,10 +1072,10 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       using P = WidePipe<D_QK, KS, PAGED>;
       for (int t = 0; t < nblk; t += 2) {
         P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf, acc,
-                st);
+                st, q_row);
         if (t + 1 < nblk)
           P::step(a, buf1, buf0, t + 1, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf,
-                  acc, st);
+                  acc, st, q_row);
       }
       // The last step's zero-fill copies may still be landing in a buffer
       // that the next attempt or the epilogue writes.
@@ -1045,11 +1087,15 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   }
 
   // Lane values for the rest of the row (see lane_fresh), then the next
-  // row's query slice, which lands under this row's epilogue.
+  // row's query slice: from the last block's buffer (read before the
+  // epilogue reuses the buffers: the barrier there follows the reads), or
+  // loaded now to land under this row's epilogue.
   const int lane = lane_fresh(), hl = lane & 31, half = lane >> 5, head = hg * 32 + hl;
   const float sink = SINK ? sink_lds[head] : 0.f;
-  const int next = turn_row(a, ++turn, PAGED);
-  if (next >= 0) load_query<D_QK>(qf, a, next, head, half);
+  if (q_row >= 0)
+    load_query_lds<D_QK>(qf, (nblk - 1) & 1 ? buf0 : buf1, hg, lane);
+  else if (next >= 0)
+    load_query<D_QK>(qf, a, next, head, half);
 
   // Combine, normalise, store.  acc[ct][i] = O[head][c = 32ct + 8(i/4) + 4half + i%4].
   float m_fin = st.m_ref, l_fin = st.l_sum, mx_fin = st.m_max, a_self = 1.f;

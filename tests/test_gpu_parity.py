@@ -287,6 +287,40 @@ def test_row_lengths_random_bitexact():
 
 
 # ---------------------------------------------------------------------------
+# more rows than the grid has workgroups (one per CU, 256 on MI355X): each
+# workgroup walks several rows and prepares a row's successor under it (for
+# 64 heads the successor's query slice is gathered into the last block's
+# buffer).  Empty rows and both block-count parities sit between them.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h_q,d_qk", [(64, 512), (64, 576), (128, 512), (128, 576)])
+def test_prefill_rows_beyond_grid(h_q, d_qk):
+    c = W.make_prefill(f"rows300_h{h_q}_d{d_qk}", s_q=300, s_kv=700, h_q=h_q, d_qk=d_qk, d_v=512,
+                       topk=96, layout="scattered", invalid_frac=0.3, empty_frac=0.05,
+                       with_sink=(d_qk == 576), seed=7 + h_q + d_qk)
+    _say(c.name)
+    assert_parity(run_prefill(c), oracle_prefill(c), c.name)
+    # explicit lengths 0..96: rows of 0, 1 and 2 blocks in every order
+    gen = torch.Generator().manual_seed(h_q + d_qk)
+    tl = torch.randint(0, 97, (c.s_q,), generator=gen, dtype=torch.int32)
+    assert_parity(run_prefill(c, topk_length=tl), oracle_prefill(c, topk_length=tl),
+                  c.name + " explicit lengths")
+
+
+@pytest.mark.parametrize("h_q", [64, 128])
+def test_decode_rows_beyond_grid(h_q):
+    gen = torch.Generator().manual_seed(h_q)
+    seqlens = torch.randint(100, 900, (150,), generator=gen)
+    c = W.make_decode(f"decode_rows300_h{h_q}", batch=150, s_q=2, h_q=h_q, d_qk=576, d_v=512,
+                      topk=128, seqlens=seqlens, seed=h_q, effective=100, with_length=True,
+                      with_sink=True)
+    _say(c.name)
+    dyn = run_decode(c)
+    assert_parity(dyn, oracle_decode(c), c.name)
+    assert_bitwise(dyn, run_decode(c, topk_length=None), f"{c.name} dynamic vs fixed")
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times:
 # sampled rows against the oracle, properties on every row
 # ---------------------------------------------------------------------------
