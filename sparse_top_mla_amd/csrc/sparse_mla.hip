@@ -363,12 +363,19 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
 // accumulator (256 fp32 per lane) stays in AGPRs and is touched only by MFMA
 // inside the block loop; the query slice stays in VGPRs.
 //
-// Workgroup: G = h_q / 32 head groups x KS key splits, G * KS = 4 waves.
-// With KS = 2 (h_q = 32, 64) the two waves of a head group take the lower and
-// upper 32 keys of every 64-key block and merge at the end of the row.
+// Workgroup: NW waves (one per SIMD of the CUs it occupies) working on blocks
+// of BK = 16 NW keys (each wave copies 16 rows of a block), as NW / KS head
+// groups of 32 heads times KS key splits:
+//   128 heads:             NW = 4, KS = 1, one workgroup per CU, 64-key blocks;
+//   64 heads, d_qk = 512:  NW = 2, KS = 1, two workgroups per CU, 32-key blocks;
+//   64 heads, d_qk = 576:  NW = 4, KS = 2 (two 2-wave workgroups do not fit the
+//                          registers at d_qk = 576): the two waves of a head
+//                          group take the lower and upper 32 keys of every
+//                          64-key block and merge at the end of the row.
+// A wave computes 32 keys x 32 heads per tile in every layout.
 //
-// Pipeline per 64-key block t (two LDS buffers; the loop is unrolled by two
-// so each half-iteration reads one buffer and fills the other):
+// Pipeline per block t (two LDS buffers; the loop is unrolled by two so each
+// half-iteration reads one buffer and fills the other):
 //   wait for block t's rows + barrier
 //   rows of block t+1 from the index and page loaded one step earlier; its
 //   rope part is copied at once
@@ -388,9 +395,9 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kRefSlack = 64.0f;  // log2 units
-constexpr int kWideWaves = 4;       // waves per workgroup (h_q = 64: 2 x 2 key halves; 128: 4)
+constexpr int kWideWaves = 4;       // waves per CU: one per SIMD
 
-template <int D_QK>
+template <int D_QK, int BK = 64>
 struct WideTile {
   // LDS block layout: the first 512 columns ("nope" part, also V) of each of
   // the 64 rows in 1 KiB rows, then the remaining d_qk - 512 columns ("rope"
@@ -400,12 +407,12 @@ struct WideTile {
   static constexpr int kRowBytes = D_QK * 2;
   static constexpr int kNopeBytes = 1024;
   static constexpr int kRopeBytes = kRowBytes - kNopeBytes;  // 0 or 128
-  static constexpr int kRopeBase = kBlockKeys * kNopeBytes;
-  static constexpr int kBufBytes = kBlockKeys * kRowBytes;
+  static constexpr int kRopeBase = BK * kNopeBytes;
+  static constexpr int kBufBytes = BK * kRowBytes;
   static constexpr int kDSteps = D_QK / 16;        // 32x32x16 K steps over d_qk
   static constexpr int kRopeLanes = kRopeBytes / 16;
   static_assert(kRopeBytes == 0 || kRopeBytes == 128, "d_qk");
-  static_assert(32 * kDV * 4 <= kBufBytes, "merge area");
+  static_assert(32 * kDV * 2 <= kBufBytes, "a wave's bf16 output tile fits a buffer");
 };
 
 // Chunk swizzles: nope rows permute the 16 chunks of each 256 B group by
@@ -419,15 +426,20 @@ struct BlockMeta {
   bool ok;        // lane j: bit j of mask
 };
 
+// Blocks of BK keys: lane j < BK holds position BK blk + j; lanes >= BK
+// (BK = 32) hold no key.
+template <int BK>
 __device__ __forceinline__ int load_index(const int32_t* idx_row, int blk, int topk,
                                           int lane = lane_id()) {
-  const int pos = blk * kBlockKeys + lane;
-  return pos < topk ? idx_row[pos] : -1;
+  const int pos = blk * BK + lane;
+  return lane < BK && pos < topk ? idx_row[pos] : -1;
 }
 
+template <int BK>
 __device__ __forceinline__ bool index_ok(int idx, int blk, int L, int bound) {
-  const int pos = blk * kBlockKeys + lane_id();
-  return pos < L && idx >= 0 && idx < bound;
+  const int lane = lane_id();
+  const int pos = blk * BK + lane;
+  return lane < BK && pos < L && idx >= 0 && idx < bound;
 }
 
 template <bool PAGED>
@@ -547,7 +559,7 @@ __device__ __forceinline__ void dma_table16(const u32x4s& rs, uint32_t voff, uin
 template <int D_QK>
 struct GatherPump {
   using T = WideTile<D_QK>;
-  static constexpr int kSlots = kBlockKeys / kWideWaves;
+  static constexpr int kSlots = 16;  // rows per wave and block
   u32x4s rsrc;       // table resource (wave-uniform)
   LDS_AS uint8_t* buf;
   int row0;          // first row of this wave (wave-uniform)
@@ -631,19 +643,19 @@ struct GatherPump {
   }
 };
 
-// Rope part (d_qk = 576) of a block: 8 rows of 128 B per load, wave w taking
-// row groups w and w + 4.  Lane L handles row jj = 8g + L/8, LDS chunk L%8,
+// Rope part (d_qk = 576) of a block: 8 rows of 128 B per load, wave w of NW
+// taking row groups w, w + NW, ...  Lane L handles row jj = 8g + L/8, LDS chunk L%8,
 // which holds source chunk (L%8) ^ swizzle(jj); `offs` are the per-key
 // offsets of GatherPump::row_offsets (moved down by (jj % 4) KiB, which is
 // added back), so masked rows stay outside the records and read zeros.
-template <int D_QK>
+template <int D_QK, int BK, int NW>
 __device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const u32x4s& rsrc, int offs,
                                            int wave) {
-  using T = WideTile<D_QK>;
+  using T = WideTile<D_QK, BK>;
   if (T::kRopeLanes == 0) return;
   const int lane = lane_id();
 #pragma unroll
-  for (int g0 = 0; g0 < kBlockKeys / 8; g0 += kWideWaves) {
+  for (int g0 = 0; g0 < BK / 8; g0 += NW) {
     const int g = g0 + wave;
     const int jj = 8 * g + (lane >> 3);
     const uint32_t o = (uint32_t)__shfl(offs, jj);
@@ -697,14 +709,16 @@ __device__ __forceinline__ float pair_sum32(float x) {
 // immediate offset.  Chunk 2d + half of a row sits at chunk (2d ^ half ^ swz)
 // of its 256 B group, so each address is a row base plus (32(d%8) ^ w) with
 // one per-lane w; the rope part likewise with its own swizzle.  K fragments
-// are read kPrefetch MFMAs ahead.
-template <int D_QK, int EVERY, int NP, class Pump>
+// are read kPrefetch MFMAs ahead.  LFRESH: the lane's addresses are computed
+// here per tile (see lane_fresh) instead of once for the kernel; what the
+// register allocation of each kernel instance prefers, by measurement.
+template <int D_QK, int BK, int EVERY, int NP, bool LFRESH, class Pump>
 __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
                                               const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                               Pump& pump, int slot0) {
-  using T = WideTile<D_QK>;
+  using T = WideTile<D_QK, BK>;
   constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
-  const int lane = lane_id();
+  const int lane = LFRESH ? lane_fresh() : lane_id();
   const int hl = lane & 31, half = lane >> 5;
   int krow = (r0 + hl) * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
   int rrow = T::kRopeBase + (r0 + hl) * T::kRopeBytes, rw = (half ^ rope_swz(hl)) << 4;
@@ -738,17 +752,12 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
 // taken on the raw dot products and each probability is
 // exp2(fma(s, scale, -m_ref)).  Branch-free: a branch here would split the
 // MFMA streams this code is scheduled into.
-template <bool SKIP_FULL>
 __device__ __forceinline__ float tile_max(f32x16& s, uint32_t bits, SoftmaxState& st,
                                           float scale_log2) {
-  // SKIP_FULL: a tile of valid keys (wave-uniform test) needs no mask; the
-  // branch costs the 128-head kernel registers it does not have.
-  if (!SKIP_FULL || bits != 0xFFFFFFFFu) {
-    const uint32_t mlane = bits >> (4 * (lane_id() >> 5));
+  const uint32_t mlane = bits >> (4 * (lane_id() >> 5));
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
-  }
+  for (int i = 0; i < 16; ++i)
+    s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
   float rmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[i]);
@@ -773,7 +782,7 @@ __device__ __forceinline__ float prob(float s, float neg_ref, float scale_log2) 
 // (+8) sits at chunk (4ct ^ vc ^ swz) of its 256 B group: a row base plus
 // (64(ct%4) ^ w) with one w per row half.  MFMA n covers value tile
 // ct = n % 16, step u = n / 16.
-template <int D_QK, int EVERY, int NP, bool SKIP_FULL, class Pump>
+template <int D_QK, int EVERY, int NP, bool LFRESH, class Pump>
 __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r0, f32x16 s,
                                                 uint32_t bits, f32x16 (&acc)[kDV / 32],
                                                 SoftmaxState& st, float scale_log2, Pump& pump,
@@ -781,7 +790,7 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
   using T = WideTile<D_QK>;
   constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
   constexpr int kTiles = kDV / 32;
-  const int lane = lane_id();
+  const int lane = LFRESH ? lane_fresh() : lane_id();
   const int i16 = lane & 15, cb = (lane >> 4) & 1, half = lane >> 5;
   const int vrow = r0 + 4 * half + TR_ROW(i16);
   const int vc = 2 * cb + (TR_COL(i16) >> 1);
@@ -803,7 +812,7 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
     lo[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, false));
     hi[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)vaddr(n, true));
   }
-  const float neg_ref = tile_max<SKIP_FULL>(s, bits, st, scale_log2);
+  const float neg_ref = tile_max(s, bits, st, scale_log2);
   float p0[8];
   bf16x8 pf[2];
 #pragma unroll
@@ -842,34 +851,34 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
   st.l_sum += pair_sum32(rsum);
 }
 
-// One 64-key block with a valid key for one wave: its 32-key tiles in
-// [koff, koff + 64/KS); tiles without a valid key are skipped (their gather
-// slots are then copied by GatherPump::finish).  The first tile takes every
-// gather slot of the wave, as many under S^T as its MFMAs allow at one per
-// EVERY and the rest under P*V, so that the copies leave early.
-template <int D_QK, int KS, int EVERY>
+// One block with a valid key for one wave: the wave's 32-key tiles among
+// keys [koff, koff + BK/KS) (one or two); tiles without a valid key are
+// skipped (their gather slots are then copied by GatherPump::finish).  The
+// first tile takes every gather slot of the wave, as many under S^T as its
+// MFMAs allow at one per EVERY and the rest under P*V, so that the copies
+// leave early.
+template <int D_QK, int BK, int KS, int EVERY, bool LFRESH>
 __device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t mask, int koff,
                                            const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                            f32x16 (&acc)[kDV / 32], SoftmaxState& st,
                                            float scale_log2, GatherPump<D_QK>& pump) {
-  constexpr int kTiles = kBlockKeys / KS / 32;
+  constexpr int kTiles = BK / KS / 32;
   constexpr int kSlots = GatherPump<D_QK>::kSlots;
   constexpr int kSteps = WideTile<D_QK>::kDSteps;
   constexpr int NS = kSteps / EVERY < kSlots ? kSteps / EVERY : kSlots;  // under S^T
   constexpr int NV = kSlots - NS;                                       // under P*V
-  constexpr bool SF = KS == 2 && D_QK == 512;
   static_assert(NV * EVERY <= 2 * kDV / 32, "gather slots per P*V pass");
 #pragma unroll
   for (int kt = 0; kt < kTiles; ++kt) {
     const int r0 = koff + 32 * kt;
     const uint32_t bits = (uint32_t)(mask >> r0);
     if (bits != 0u) {
-      const f32x16 s = kt == 0 ? tile_scores<D_QK, EVERY, NS>(buf, r0, qf, pump, 0)
-                               : tile_scores<D_QK, EVERY, 0>(buf, r0, qf, pump, 0);
+      const f32x16 s = kt == 0 ? tile_scores<D_QK, BK, EVERY, NS, LFRESH>(buf, r0, qf, pump, 0)
+                               : tile_scores<D_QK, BK, EVERY, 0, LFRESH>(buf, r0, qf, pump, 0);
       if (kt == 0)
-        tile_softmax_pv<D_QK, EVERY, NV, SF>(buf, r0, s, bits, acc, st, scale_log2, pump, NS);
+        tile_softmax_pv<D_QK, EVERY, NV, LFRESH>(buf, r0, s, bits, acc, st, scale_log2, pump, NS);
       else
-        tile_softmax_pv<D_QK, EVERY, 0, SF>(buf, r0, s, bits, acc, st, scale_log2, pump, 0);
+        tile_softmax_pv<D_QK, EVERY, 0, LFRESH>(buf, r0, s, bits, acc, st, scale_log2, pump, 0);
     }
   }
 }
@@ -881,16 +890,21 @@ struct Ahead {
   int idx1, page1, idx2;
 };
 
-template <int D_QK, int KS, bool PAGED>
+template <int D_QK, int NW, int KS, bool PAGED>
 struct WidePipe {
-  using T = WideTile<D_QK>;
+  static constexpr int BK = 16 * NW;
+  using T = WideTile<D_QK, BK>;
+  // Per-tile lane addresses: fewer spills and faster in the paged 128-head
+  // kernels, slower in the others (measured).
+  static constexpr bool LFRESH = PAGED && NW == 4 && KS == 1;
   // The gather of block t+1 leaves in the first tile of block t, one row
   // per kEvery MFMAs (16 rows per wave and block), so that the rows have
   // the rest of the block to land.  Paged rows come from HBM, and there every
-  // fourth MFMA keeps the copies' issue cost under the MFMAs; every second
-  // one suits rows that mostly hit in the caches (prefill).  Measured: both
-  // beat spreading the copies over the whole block.
-  static constexpr int kEvery = PAGED && KS == 1 ? 4 : 2;
+  // fourth MFMA keeps the copies' issue cost under the two tiles of a wave's
+  // block; every second one suits rows that mostly hit in the caches
+  // (prefill) and the single tile of the other layouts.  Measured: both beat
+  // spreading the copies over the whole block.
+  static constexpr int kEvery = PAGED && NW == 4 && KS == 1 ? 4 : 2;
   // One half-iteration: block t lives in `cur` (already gathered); gather
   // block t+1 into `nxt` while computing block t.
   static __device__ __forceinline__ void step(const FwdArgs& a, const LDS_AS uint8_t* cur,
@@ -903,21 +917,23 @@ struct WidePipe {
     wait_vm_all();
     __syncthreads();
     const bool have_nxt = t + 1 < nblk;
-    // The last step of a 64-head row gathers the query slice of row q_row
-    // (64 rows of d_qk: one block buffer) into `nxt` instead, head j as row j.
-    // (Wave-uniform; readfirstlane says so to the compiler, which must keep
-    // the selected resource in scalar registers.)
-    const bool q_nxt = __builtin_amdgcn_readfirstlane((int)(!have_nxt && q_row >= 0)) != 0;
-    BlockMeta mn = block_meta<PAGED>(a, index_ok(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
+    // With a key split (64 heads at d_qk = 576), the last step of a row
+    // gathers the query slice of row q_row (64 rows of d_qk: one block
+    // buffer) into `nxt` instead, head j as row j.  (Wave-uniform;
+    // readfirstlane says so to the compiler, which must keep the selected
+    // resource in scalar registers.)
+    const bool q_nxt =
+        KS == 2 && __builtin_amdgcn_readfirstlane((int)(!have_nxt && q_row >= 0)) != 0;
+    BlockMeta mn = block_meta<PAGED>(a, index_ok<BK>(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
     if (q_nxt) mn = BlockMeta{~0ull, lane_id(), true};
     u32x4s rsrc = q_nxt ? query_rsrc(a, q_row, T::kRowBytes) : table_rsrc(a);
 #pragma unroll
     for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
     const int offs = GatherPump<D_QK>::row_offsets(mn);
-    if (have_nxt || q_nxt) stage_rope<D_QK>(nxt, rsrc, offs, wave);
-    const bool ok2 = index_ok(ah.idx2, t + 2, L, bound);
+    if (have_nxt || q_nxt) stage_rope<D_QK, BK, NW>(nxt, rsrc, offs, wave);
+    const bool ok2 = index_ok<BK>(ah.idx2, t + 2, L, bound);
     const int page2 = page_lookup<PAGED>(a, seq, ok2, ah.idx2);
-    const int idx3 = load_index(idx_row, t + 3, a.topk);
+    const int idx3 = load_index<BK>(idx_row, t + 3, a.topk);
     // Past the last block (without a query slice to gather) the mask is
     // empty: the copies zero-fill `nxt`, which nothing reads any more.
     const int row0 = GatherPump<D_QK>::kSlots * wave;
@@ -925,15 +941,17 @@ struct WidePipe {
                           lane_id() * 16, 0u, 0u, 0u};
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
     if (wmask != 0)
-      wide_block<D_QK, KS, kEvery>(cur, mask_cur, koff, qf, acc, st, a.scale_log2, pump);
-    pump.template finish<KS == 1>();
+      wide_block<D_QK, BK, KS, kEvery, LFRESH>(cur, mask_cur, koff, qf, acc, st, a.scale_log2,
+                                               pump);
+    pump.template finish<NW == 4 && KS == 1>();
     mask_cur = mn.mask;
     ah = Ahead{ah.idx2, page2, idx3};
   }
 };
 
 // Row of a workgroup's turn k, or -1 once it has none left.  The grid is at
-// most one workgroup per CU; positions p = 0, 1, ... go to the workgroups in
+// most what the CUs hold at once (one 4-wave or two 2-wave workgroups per
+// CU); positions p = 0, 1, ... go to the workgroups in
 // snake order (0..G-1, then G-1..0, ...), so each gets an even share of long
 // and short rows.  Prefill takes its rows from the last one down (the rows
 // of a causal prefill grow with the row number).
@@ -954,7 +972,7 @@ struct RowHead {
   int idx0, idx1, idx2;
 };
 
-template <bool DYNAMIC>
+template <bool DYNAMIC, int BK>
 __device__ __forceinline__ RowHead<DYNAMIC> load_row_head(const FwdArgs& a, int row) {
   RowHead<DYNAMIC> h;
   const int lane = lane_fresh();
@@ -964,9 +982,9 @@ __device__ __forceinline__ RowHead<DYNAMIC> load_row_head(const FwdArgs& a, int 
     h.tl = a.topk_length[row];
   else
     h.first = load_tail_round(idx_row, a.topk, lane);
-  h.idx0 = load_index(idx_row, 0, a.topk, lane);
-  h.idx1 = load_index(idx_row, 1, a.topk, lane);
-  h.idx2 = load_index(idx_row, 2, a.topk, lane);
+  h.idx0 = load_index<BK>(idx_row, 0, a.topk, lane);
+  h.idx1 = load_index<BK>(idx_row, 1, a.topk, lane);
+  h.idx2 = load_index<BK>(idx_row, 2, a.topk, lane);
   return h;
 }
 
@@ -998,10 +1016,12 @@ __device__ __forceinline__ void load_query_lds(bf16x8 (&qf)[WideTile<D_QK>::kDSt
                : buf + rrow + ((32 * (d - 32)) ^ rw));
 }
 
-template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_wide_kernel(FwdArgs a) {
-  using T = WideTile<D_QK>;
+  constexpr int BK = 16 * NW;  // keys per block: 16 rows per wave
+  constexpr int G = NW / KS;   // head groups of 32
+  using T = WideTile<D_QK, BK>;
   __shared__ __attribute__((aligned(16))) uint8_t buf0_raw[T::kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1_raw[T::kBufBytes];
   LDS_AS uint8_t* buf0 = (LDS_AS uint8_t*)buf0_raw;
@@ -1009,16 +1029,15 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
 
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int G = kWideWaves / KS;
-  const int hg = wave % G, ks = wave / G;
+  const int hg = wave % G, ks = wave / G;  // head group, key split
   const int hl = lane & 31, half = lane >> 5;
-  const int koff = ks * (kBlockKeys / KS);
+  const int koff = ks * (BK / KS);
 
   const int head = hg * 32 + hl;
   // The per-head sinks sit in LDS for the epilogues: a global load there
   // would be counted behind the next row's query loads and wait for them.
-  __shared__ float sink_lds[SINK ? kWideWaves / KS * 32 : 1];
-  if (SINK && (int)threadIdx.x < kWideWaves / KS * 32) sink_lds[threadIdx.x] = a.attn_sink[threadIdx.x];
+  __shared__ float sink_lds[SINK ? G * 32 : 1];
+  if (SINK && (int)threadIdx.x < G * 32) sink_lds[threadIdx.x] = a.attn_sink[threadIdx.x];
   // (The first barrier of the row loop comes before the first epilogue.)
 
   // The workgroup's rows (persistent grid), each started while the previous
@@ -1029,19 +1048,20 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   bf16x8 qf[T::kDSteps];
   load_query<D_QK>(qf, a, row, head, half);
   for (;;) {
-  const RowHead<DYNAMIC> rh = load_row_head<DYNAMIC>(a, row);
+  const RowHead<DYNAMIC> rh = load_row_head<DYNAMIC, BK>(a, row);
   const int seq = row / a.rows_per_seq;
   const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
   const int32_t* idx_row = a.indices + (size_t)row * a.topk;
   const int L = DYNAMIC ? clamp_length(rh.tl, a.topk) : finish_tail_scan(rh.first, idx_row, a.topk, bound);
-  const int nblk = (L + kBlockKeys - 1) / kBlockKeys;
+  const int nblk = (L + BK - 1) / BK;
   // Kept for a recompute: loading them again there would make the compiler
   // wait for every outstanding load (the query rows included) at the join.
   const int idx0 = rh.idx0, idx1 = rh.idx1, idx2 = rh.idx2;
   const int next = turn_row(a, ++turn, PAGED);
-  // 64 heads: the next row's query slice fits one block buffer, and the
-  // last block step gathers it there (contiguous 1 KiB rows; loaded straight
-  // into the MFMA operand layout, each load would touch 32 head rows).
+  // With a key split, the next row's query slice fits one block buffer, and
+  // the last block step gathers it there (contiguous 1 KiB rows; loaded
+  // straight into the MFMA operand layout, each load would touch 32 head
+  // rows).
   const int q_row = KS == 2 && nblk > 0 ? next : -1;
 
   f32x16 acc[kDV / 32];
@@ -1052,8 +1072,8 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
     st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
     if (nblk > 0) {
-      const bool ok0 = index_ok(idx0, 0, L, bound);
-      const bool ok1 = index_ok(idx1, 1, L, bound);
+      const bool ok0 = index_ok<BK>(idx0, 0, L, bound);
+      const bool ok1 = index_ok<BK>(idx1, 1, L, bound);
       const int pg0 = page_lookup<PAGED>(a, seq, ok0, idx0);
       const int pg1 = page_lookup<PAGED>(a, seq, ok1, idx1);
       const BlockMeta m0 = block_meta<PAGED>(a, ok0, idx0, pg0);
@@ -1064,12 +1084,12 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
         const u32x4s rsrc = table_rsrc(a);
         const int offs = GatherPump<D_QK>::row_offsets(m0);
         const int row0 = GatherPump<D_QK>::kSlots * wave;
-        stage_rope<D_QK>(buf0, rsrc, offs, wave);
+        stage_rope<D_QK, BK, NW>(buf0, rsrc, offs, wave);
         GatherPump<D_QK>{rsrc, buf0, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
                          lane_id() * 16, 0u, 0u, 0u}
             .copy_all();
       }
-      using P = WidePipe<D_QK, KS, PAGED>;
+      using P = WidePipe<D_QK, NW, KS, PAGED>;
       for (int t = 0; t < nblk; t += 2) {
         P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf, acc,
                 st, q_row);
@@ -1202,9 +1222,11 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     // The output goes through LDS so that every global store writes one
     // head's whole 1 KiB row: stored straight from the accumulator layout, a
     // store instruction would touch 32 rows with 16 bytes each.  The wave's
-    // bf16 tile takes 32 KiB of a block buffer that no other wave uses any
-    // more.  Chunk c (16 B) of head row h sits at chunk c ^ h of the row.
-    LDS_AS uint8_t* tile = (wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * kDV * 2);
+    // bf16 tile takes 32 KiB of a block buffer that no wave reads any more
+    // (two tiles per buffer of a 64-key block, one per buffer of a 32-key
+    // block).  Chunk c (16 B) of head row h sits at chunk c ^ h of the row.
+    constexpr int kTileBytes = 32 * kDV * 2, kPer = T::kBufBytes / kTileBytes;
+    LDS_AS uint8_t* tile = (wave / kPer == 0 ? buf0 : buf1) + (wave % kPer) * kTileBytes;
 #pragma unroll
     for (int ct = 0; ct < kDV / 32; ++ct)
 #pragma unroll
@@ -1307,15 +1329,19 @@ int cu_count() {
   return n;
 }
 
-template <int D_QK, int KS, bool PAGED, bool DYNAMIC, bool SINK>
+template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK>
 smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
-  if ((args.h_q / 32) * KS != kWideWaves)
-    return fail(SMLA_ERR_UNSUPPORTED, "wide kernel needs h_q=%d (KS=%d)", 32 * kWideWaves / KS, KS);
+  if (args.h_q != 32 * NW / KS)
+    return fail(SMLA_ERR_UNSUPPORTED, "wide kernel with %d waves and %d key splits needs h_q=%d",
+                NW, KS, 32 * NW / KS);
   const int cus = cu_count();
   if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
-  const int grid = args.rows < cus ? args.rows : cus;  // one workgroup per CU, each loops over rows
-  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, KS, PAGED, DYNAMIC, SINK>), dim3(grid),
-                     dim3(kWideWaves * 64), 0, stream, args);
+  // As many workgroups as the CUs hold at once (one wave per SIMD), each
+  // looping over rows.
+  const long long slots = (long long)cus * (kWideWaves / NW);
+  const int grid = args.rows < slots ? args.rows : (int)slots;
+  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, NW, KS, PAGED, DYNAMIC, SINK>), dim3(grid),
+                     dim3(NW * 64), 0, stream, args);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
@@ -1323,29 +1349,33 @@ smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
 
 template <bool PAGED>
 smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
-  const int ks = args.h_q == 64 ? 2 : 1;
+  // 128 heads: 4 waves; 64 heads at d_qk = 512: 2 waves (two workgroups per
+  // CU, 32-key blocks); 64 heads at d_qk = 576: 4 waves as 2 head groups x 2
+  // key splits (a 2-wave kernel at d_qk = 576 does not fit the registers).
+  const int nw = args.h_q == 64 && d_qk == 512 ? 2 : 4;
+  const int ks = args.h_q == 64 && d_qk == 576 ? 2 : 1;
   const bool dyn = args.topk_length != nullptr;
   const bool sink = args.attn_sink != nullptr;
   args.head_groups = 1;
-#define SMLA_WIDE(D, K, DYN, SNK)                                        \
-  if (d_qk == D && ks == K && dyn == DYN && sink == SNK)                 \
-    return launch_wide<D, K, PAGED, DYN, SNK>(args, stream);
-  SMLA_WIDE(512, 1, false, false)
-  SMLA_WIDE(512, 1, false, true)
-  SMLA_WIDE(512, 1, true, false)
-  SMLA_WIDE(512, 1, true, true)
-  SMLA_WIDE(512, 2, false, false)
-  SMLA_WIDE(512, 2, false, true)
-  SMLA_WIDE(512, 2, true, false)
-  SMLA_WIDE(512, 2, true, true)
-  SMLA_WIDE(576, 1, false, false)
-  SMLA_WIDE(576, 1, false, true)
-  SMLA_WIDE(576, 1, true, false)
-  SMLA_WIDE(576, 1, true, true)
-  SMLA_WIDE(576, 2, false, false)
-  SMLA_WIDE(576, 2, false, true)
-  SMLA_WIDE(576, 2, true, false)
-  SMLA_WIDE(576, 2, true, true)
+#define SMLA_WIDE(D, W, K, DYN, SNK)                                     \
+  if (d_qk == D && nw == W && ks == K && dyn == DYN && sink == SNK)      \
+    return launch_wide<D, W, K, PAGED, DYN, SNK>(args, stream);
+  SMLA_WIDE(512, 4, 1, false, false)
+  SMLA_WIDE(512, 4, 1, false, true)
+  SMLA_WIDE(512, 4, 1, true, false)
+  SMLA_WIDE(512, 4, 1, true, true)
+  SMLA_WIDE(512, 2, 1, false, false)
+  SMLA_WIDE(512, 2, 1, false, true)
+  SMLA_WIDE(512, 2, 1, true, false)
+  SMLA_WIDE(512, 2, 1, true, true)
+  SMLA_WIDE(576, 4, 1, false, false)
+  SMLA_WIDE(576, 4, 1, false, true)
+  SMLA_WIDE(576, 4, 1, true, false)
+  SMLA_WIDE(576, 4, 1, true, true)
+  SMLA_WIDE(576, 4, 2, false, false)
+  SMLA_WIDE(576, 4, 2, false, true)
+  SMLA_WIDE(576, 4, 2, true, false)
+  SMLA_WIDE(576, 4, 2, true, true)
 #undef SMLA_WIDE
   return fail(SMLA_ERR_UNSUPPORTED, "no wide kernel instance for d_qk=%d", d_qk);
 }
@@ -1358,9 +1388,9 @@ uint32_t span_or_max(uint64_t bytes) {
 
 template <bool PAGED>
 smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
-  // The wide kernel runs four waves: 64 heads as two head groups times two
-  // key halves, or 128 heads as four head groups; it addresses the KV table
-  // with 32-bit offsets (kv_span, set by the caller, at most kMaxKvSpan).
+  // The wide kernel takes 64 and 128 heads (see dispatch_wide); it
+  // addresses the KV table with 32-bit offsets (kv_span, set by the caller,
+  // at most kMaxKvSpan).
   if ((args.h_q == 64 || args.h_q == 128) && args.kv_span <= kMaxKvSpan)
     return dispatch_wide<PAGED>(d_qk, args, stream);
   const int waves_total = args.h_q / kHeadsPerWave;
