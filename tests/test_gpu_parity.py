@@ -116,12 +116,13 @@ def test_prefill_ragged_topk(topk):
     assert_bitwise(run_prefill(c), got, f"{c.name} derived vs explicit")
 
 
-def _tail_rows(topk=192, s_kv=1000, seed=0):
+def _tail_rows(topk=192, s_kv=1000, seed=0, lens=None):
     """Rows whose last valid entry sits at each boundary length of FlashMLA
     PR #216, "Correctness" (0, 1, 17, 63, 64, 65, 127, 128) and a few more,
     with -1 interior holes."""
     gen = torch.Generator().manual_seed(seed)
-    lens = [0, 1, 17, 63, 64, 65, 127, 128, 129, 191, 192]
+    if lens is None:
+        lens = [0, 1, 17, 63, 64, 65, 127, 128, 129, 191, 192]
     idx = torch.full((len(lens), topk), -1, dtype=torch.int64)
     for r, n in enumerate(lens):
         if n:
@@ -163,6 +164,23 @@ def test_tail_lengths_and_bitwise_equivalences(d_qk):
         c3 = W.PrefillCase("enc", c.q, c.kv, alt.view(n, 1, 192).contiguous(), None, c.attn_sink,
                            c.sm_scale, c.d_v)
         assert_bitwise(base, run_prefill(c3), f"encoding {enc}")
+
+
+@pytest.mark.parametrize("d_qk,with_sink", [(512, False), (512, True), (576, True)])
+def test_tail_lengths_at_32_key_blocks(d_qk, with_sink):
+    """The 64-head kernel at d_qk = 512 works on 32-key blocks: lengths at
+    and around their edges, derived and explicit, against the oracle."""
+    lens, idx = _tail_rows(seed=3, lens=[31, 32, 33, 95, 96, 97, 159, 160, 161, 2])
+    n = len(lens)
+    c = W.make_prefill("tails32", s_q=n, s_kv=1000, h_q=64, d_qk=d_qk, d_v=512, topk=192,
+                       layout="full", seed=11, with_sink=with_sink)
+    c.indices = idx.view(n, 1, 192).contiguous()
+    c.topk_length = None
+    _say(f"32-key tails d{d_qk} sink={with_sink}")
+    base = run_prefill(c)
+    assert_parity(base, oracle_prefill(c), "tails32 derived")
+    explicit = torch.tensor(lens, dtype=torch.int32)
+    assert_bitwise(base, run_prefill(c, topk_length=explicit), "tails32 derived vs explicit")
 
 
 def test_nan_behind_unused_indices_never_leaks():
