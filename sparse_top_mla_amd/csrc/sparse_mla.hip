@@ -5,22 +5,24 @@
 // attends, with all of its heads sharing one latent KV head, to the KV rows
 // its index vector names.  Entries outside [0, K) are masked; the row length
 // L (explicit topk_length, else one past the last valid entry found by a tail
-// scan) bounds the 64-key block loop; positions >= L never address KV; an
+// scan) bounds the block loop; positions >= L never address KV; an
 // optional per-head sink joins the softmax denominator; a row without keys
 // gives out = 0, lse = +inf, max_logits = -inf.
 //
 // Two kernels share the index, validity, tail-scan and paging routines:
-//   * the wide kernel (h_q = 64 or 128, every benchmarked shape): one
-//     workgroup of four waves per query row, one wave per SIMD, 32 heads per
-//     wave on v_mfma_f32_32x32x16_bf16; see the block comment above it.
+//   * the wide kernel (h_q = 64 or 128, every benchmarked shape): a
+//     persistent grid whose workgroups (2 or 4 waves, one wave per SIMD)
+//     walk query rows, 32 heads per wave on v_mfma_f32_32x32x16_bf16; see the
+//     block comment above it.
 //   * the 16-head kernel below (other multiples of 16): one workgroup per
 //     (query row, group of up to 64 heads), 16 heads per wave on
 //     v_mfma_f32_16x16x32_bf16.
 // Common to both:
 //   * the row's query slice stays in VGPRs for the whole row (B operand of
 //     S^T = K Q^T).
-//   * per 64-key block: the index vector is loaded one entry per lane and the
-//     validity of every key becomes a 64-bit wave ballot.  A block without a
+//   * per block (64 keys, or 32 in the 64-head d_qk = 512 layout): the index
+//     vector is loaded one entry per lane and the validity of every key
+//     becomes a wave ballot.  A block without a
 //     valid key is skipped outright (no gather, no MFMA): masked keys add
 //     exactly nothing to the softmax, so skipping is exact.
 //   * valid KV rows are copied global -> LDS directly (16 B per lane, one
