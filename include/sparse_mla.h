@@ -40,6 +40,7 @@
 #ifndef SPARSE_MLA_H
 #define SPARSE_MLA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -102,6 +103,48 @@ smla_status sparse_mla_decode_fwd(const void *q, const void *kv_cache,
                                   int32_t num_blocks, int32_t page_size,
                                   int32_t max_blocks_per_seq, float sm_scale, void *out,
                                   float *lse, float *max_logits, smla_stream_t stream);
+
+/*
+ * Bytes of workspace that sparse_mla_decode_fwd_split needs for num_splits
+ * key-range splits of every row: B*s_q*num_splits*h_q*(d_v + 2) fp32 values
+ * (each split's partial output and its lse and max).  0 for num_splits <= 1
+ * or non-positive sizes.
+ */
+size_t sparse_mla_decode_split_workspace_bytes(int32_t B, int32_t s_q, int32_t h_q, int32_t d_v,
+                                               int32_t num_splits);
+
+/*
+ * Split-KV paged decode: the scheduler-metadata path for batches too small to
+ * fill the device (FlashMLA PR #216, "Kernel performance": the batch-2 runs
+ * reuse scheduler metadata across calls).  Arguments as sparse_mla_decode_fwd.
+ * Split s of a row takes its index blocks [s*n/num_splits, (s+1)*n/num_splits),
+ * n = ceil(L/block), and writes its output normalised by its own softmax sum,
+ * its lse and its max to the workspace; a second kernel merges them: lse =
+ * logsumexp of the split lses (an empty split, lse = -inf, adds nothing),
+ * out = sum of exp(lse_s - lse) * out_s, the sink joins the denominator once
+ * after the merge, and a row whose splits are all empty gives (0, +inf, -inf)
+ * as the unsplit path does.  Results equal the unsplit path's up to rounding.
+ *   num_splits       1 .. 1024; 1 runs the unsplit path (workspace unused)
+ *   workspace        device memory of at least
+ *                    sparse_mla_decode_split_workspace_bytes(...) bytes,
+ *                    16-byte aligned, owned by the caller; its contents
+ *                    need no initialisation and are garbage afterwards;
+ *                    calls that overlap on the same workspace race
+ *   workspace_bytes  its size (checked)
+ * Supported for h_q = 128 (d_qk 512 or 576) and h_q = 64 at d_qk = 512;
+ * other shapes return SMLA_ERR_UNSUPPORTED.  Both kernels are enqueued on
+ * `stream`.
+ */
+smla_status sparse_mla_decode_fwd_split(const void *q, const void *kv_cache,
+                                        const int32_t *block_table, const int32_t *cache_seqlens,
+                                        const int32_t *indices, const int32_t *topk_length,
+                                        const float *attn_sink, int32_t B, int32_t s_q,
+                                        int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v,
+                                        int32_t topk, int32_t num_blocks, int32_t page_size,
+                                        int32_t max_blocks_per_seq, float sm_scale,
+                                        int32_t num_splits, void *workspace,
+                                        size_t workspace_bytes, void *out, float *lse,
+                                        float *max_logits, smla_stream_t stream);
 
 /*
  * The row length L every kernel above uses (FlashMLA PR #196, "Fix": tail

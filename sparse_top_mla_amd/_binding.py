@@ -18,8 +18,8 @@ LIBRARY = _PKG / "libsparse_mla.so"
 _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL_ARG", 2: "SMLA_ERR_BAD_SHAPE", 3: "SMLA_ERR_UNSUPPORTED",
            4: "SMLA_ERR_LAUNCH"}
 
-EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_row_lengths",
-           "sparse_mla_last_error")
+EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_decode_split_workspace_bytes",
+           "sparse_mla_decode_fwd_split", "sparse_mla_row_lengths", "sparse_mla_last_error")
 
 _lib = None
 
@@ -51,6 +51,12 @@ def _declare(lib):
     lib.sparse_mla_decode_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           i32, i32, i32, i32, f32, vp, vp, vp, vp]
     lib.sparse_mla_decode_fwd.restype = ctypes.c_int
+    lib.sparse_mla_decode_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.sparse_mla_decode_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.sparse_mla_decode_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                i32, i32, i32, i32, i32, f32, i32, vp,
+                                                ctypes.c_size_t, vp, vp, vp, vp]
+    lib.sparse_mla_decode_fwd_split.restype = ctypes.c_int
     lib.sparse_mla_row_lengths.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.sparse_mla_row_lengths.restype = ctypes.c_int
     lib.sparse_mla_last_error.argtypes = []
@@ -124,15 +130,9 @@ def fwd(q, kv, indices, sm_scale, d_v=512, attn_sink=None, topk_length=None, *, 
     return out, lse, max_logits
 
 
-def decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, d_v=512,
-               attn_sink=None, topk_length=None, *, out=None, lse=None, max_logits=None,
-               stream=None):
-    """Paged sparse decode forward.  q [B, s_q, h_q, d_qk] bf16,
-    kv_cache [num_blocks, page_size, 1, d_qk] bf16, block_table [B, mbps]
-    int32, cache_seqlens [B] int32, indices [B, s_q, topk] int32,
-    topk_length [B, s_q] (or [B], broadcast over s_q) int32 or None,
-    attn_sink [h_q] fp32 or None.  Returns (out, lse, max_logits)."""
-    lib = load_library()
+def _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink, topk_length,
+                 out, lse, max_logits):
+    """Checks and output buffers shared by the decode entry points."""
     dev = q.device
     _dev(q, "q", torch.bfloat16)
     _dev(kv_cache, "kv_cache", torch.bfloat16, dev)
@@ -165,11 +165,59 @@ def decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, d_v=5
     _dev(max_logits, "max_logits", torch.float32, dev)
     if out.numel() != B * s_q * h_q * d_v or lse.numel() != B * s_q * h_q or max_logits.numel() != B * s_q * h_q:
         raise ValueError("output buffers have the wrong size")
+    return (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
+            max_logits)
+
+
+def decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, d_v=512,
+               attn_sink=None, topk_length=None, *, out=None, lse=None, max_logits=None,
+               stream=None):
+    """Paged sparse decode forward.  q [B, s_q, h_q, d_qk] bf16,
+    kv_cache [num_blocks, page_size, 1, d_qk] bf16, block_table [B, mbps]
+    int32, cache_seqlens [B] int32, indices [B, s_q, topk] int32,
+    topk_length [B, s_q] (or [B], broadcast over s_q) int32 or None,
+    attn_sink [h_q] fp32 or None.  Returns (out, lse, max_logits)."""
+    lib = load_library()
+    dev = q.device
+    (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
+     max_logits) = _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink,
+                                topk_length, out, lse, max_logits)
     st = lib.sparse_mla_decode_fwd(_p(q), _p(kv_cache), _p(block_table), _p(cache_seqlens),
                                    _p(indices), _p(topk_length), _p(attn_sink), B, s_q, h_q, h_kv,
                                    d_qk, d_v, topk, num_blocks, page_size, block_table.shape[1],
                                    float(sm_scale), _p(out), _p(lse), _p(max_logits),
                                    _stream(dev, stream))
+    _check(lib, st)
+    return out, lse, max_logits
+
+
+def decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits):
+    """Workspace bytes sparse_mla_decode_fwd_split needs."""
+    return int(load_library().sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits))
+
+
+def decode_fwd_split(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, num_splits,
+                     d_v=512, attn_sink=None, topk_length=None, *, workspace=None, out=None,
+                     lse=None, max_logits=None, stream=None):
+    """Split-KV paged decode: arguments and results as decode_fwd; each row's
+    index blocks are split num_splits ways and merged.  `workspace` (a uint8
+    CUDA tensor of at least decode_split_workspace_bytes(...) bytes) is
+    allocated here when not given."""
+    lib = load_library()
+    dev = q.device
+    (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
+     max_logits) = _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink,
+                                topk_length, out, lse, max_logits)
+    need = lib.sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8, dev)
+    st = lib.sparse_mla_decode_fwd_split(_p(q), _p(kv_cache), _p(block_table), _p(cache_seqlens),
+                                         _p(indices), _p(topk_length), _p(attn_sink), B, s_q, h_q,
+                                         h_kv, d_qk, d_v, topk, num_blocks, page_size,
+                                         block_table.shape[1], float(sm_scale), int(num_splits),
+                                         _p(workspace), workspace.numel(), _p(out), _p(lse),
+                                         _p(max_logits), _stream(dev, stream))
     _check(lib, st)
     return out, lse, max_logits
 

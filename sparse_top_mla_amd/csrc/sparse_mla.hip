@@ -106,6 +106,9 @@ struct FwdArgs {
   int32_t head_groups;   // workgroups per row (1 or 2)
   float scale_log2;      // sm_scale * log2(e)
   uint32_t kv_span;      // bytes of the KV table (wide kernel: at most kMaxKvSpan)
+  int32_t splits;        // split decode: key-range splits per row (else 1)
+  float* ws_o;           // split decode: [rows][splits][h_q][d_v] partial outputs
+  float* ws_stats;       // split decode: [rows][splits][h_q][2] lse and max of each split
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -398,6 +401,7 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kRefSlack = 64.0f;  // log2 units
 constexpr int kWideWaves = 4;       // waves per CU: one per SIMD
+constexpr int kMaxSplits = 1024;    // split decode: key-range splits per row
 
 template <int D_QK, int BK = 64>
 struct WideTile {
@@ -957,11 +961,13 @@ struct WidePipe {
 // snake order (0..G-1, then G-1..0, ...), so each gets an even share of long
 // and short rows.  Prefill takes its rows from the last one down (the rows
 // of a causal prefill grow with the row number).
-__device__ __forceinline__ int turn_row(const FwdArgs& a, int k, bool paged) {
+// With key-range splits the units are (row, split) pairs, numbered
+// row * splits + split.
+__device__ __forceinline__ int turn_row(int units, int k, bool paged) {
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
   const long long p = (long long)k * G + ((k & 1) ? G - 1 - b : b);
-  if (p >= a.rows) return -1;
-  return paged ? (int)p : a.rows - 1 - (int)p;
+  if (p >= units) return -1;
+  return paged ? (int)p : units - 1 - (int)p;
 }
 
 // What a row needs before its first block: the explicit length (or the last
@@ -1018,9 +1024,14 @@ __device__ __forceinline__ void load_query_lds(bf16x8 (&qf)[WideTile<D_QK>::kDSt
                : buf + rrow + ((32 * (d - 32)) ^ rw));
 }
 
-template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK>
+// SPLIT (paged decode without a key split): a unit is a (row, split) pair
+// covering blocks [split * nblk / splits, (split + 1) * nblk / splits) of the
+// row; it writes its partial output normalised by its own sum, with its lse
+// and max, to the workspace, and split_combine_kernel merges the splits.
+template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_wide_kernel(FwdArgs a) {
+  static_assert(!SPLIT || (PAGED && KS == 1), "split decode: paged, without a key split");
   constexpr int BK = 16 * NW;  // keys per block: 16 rows per wave
   constexpr int G = NW / KS;   // head groups of 32
   using T = WideTile<D_QK, BK>;
@@ -1045,26 +1056,35 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   // The workgroup's rows (persistent grid), each started while the previous
   // row's epilogue runs: its length, first indices and query slice are
   // loaded before that epilogue.
+  const int units = SPLIT ? a.rows * a.splits : a.rows;
   int turn = 0;
-  int row = turn_row(a, turn, PAGED);
+  int unit = turn_row(units, turn, PAGED);
   bf16x8 qf[T::kDSteps];
-  load_query<D_QK>(qf, a, row, head, half);
+  load_query<D_QK>(qf, a, SPLIT ? unit / a.splits : unit, head, half);
   for (;;) {
+  const int row = SPLIT ? unit / a.splits : unit;
   const RowHead<DYNAMIC> rh = load_row_head<DYNAMIC, BK>(a, row);
   const int seq = row / a.rows_per_seq;
   const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
   const int32_t* idx_row = a.indices + (size_t)row * a.topk;
   const int L = DYNAMIC ? clamp_length(rh.tl, a.topk) : finish_tail_scan(rh.first, idx_row, a.topk, bound);
-  const int nblk = (L + BK - 1) / BK;
+  const int nblk_row = (L + BK - 1) / BK;
+  // The unit's blocks [t0, nblk): the whole row, or the split's share.
+  const int split = SPLIT ? unit % a.splits : 0;
+  const int t0 = SPLIT ? (int)((long long)split * nblk_row / a.splits) : 0;
+  const int nblk = SPLIT ? (int)((long long)(split + 1) * nblk_row / a.splits) : nblk_row;
   // Kept for a recompute: loading them again there would make the compiler
   // wait for every outstanding load (the query rows included) at the join.
-  const int idx0 = rh.idx0, idx1 = rh.idx1, idx2 = rh.idx2;
-  const int next = turn_row(a, ++turn, PAGED);
+  const int idx0 = SPLIT ? load_index<BK>(idx_row, t0, a.topk) : rh.idx0;
+  const int idx1 = SPLIT ? load_index<BK>(idx_row, t0 + 1, a.topk) : rh.idx1;
+  const int idx2 = SPLIT ? load_index<BK>(idx_row, t0 + 2, a.topk) : rh.idx2;
+  const int next_unit = turn_row(units, ++turn, PAGED);
+  const int next = next_unit < 0 ? -1 : SPLIT ? next_unit / a.splits : next_unit;
   // With a key split, the next row's query slice fits one block buffer, and
   // the last block step gathers it there (contiguous 1 KiB rows; loaded
   // straight into the MFMA operand layout, each load would touch 32 head
   // rows).
-  const int q_row = KS == 2 && nblk > 0 ? next : -1;
+  const int q_row = KS == 2 && nblk > t0 ? next : -1;
 
   f32x16 acc[kDV / 32];
   SoftmaxState st;
@@ -1073,9 +1093,9 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
     st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
-    if (nblk > 0) {
-      const bool ok0 = index_ok<BK>(idx0, 0, L, bound);
-      const bool ok1 = index_ok<BK>(idx1, 1, L, bound);
+    if (nblk > t0) {
+      const bool ok0 = index_ok<BK>(idx0, t0, L, bound);
+      const bool ok1 = index_ok<BK>(idx1, t0 + 1, L, bound);
       const int pg0 = page_lookup<PAGED>(a, seq, ok0, idx0);
       const int pg1 = page_lookup<PAGED>(a, seq, ok1, idx1);
       const BlockMeta m0 = block_meta<PAGED>(a, ok0, idx0, pg0);
@@ -1092,7 +1112,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
             .copy_all();
       }
       using P = WidePipe<D_QK, NW, KS, PAGED>;
-      for (int t = 0; t < nblk; t += 2) {
+      for (int t = t0; t < nblk; t += 2) {
         P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf, acc,
                 st, q_row);
         if (t + 1 < nblk)
@@ -1115,7 +1135,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   const int lane = lane_fresh(), hl = lane & 31, half = lane >> 5, head = hg * 32 + hl;
   const float sink = SINK ? sink_lds[head] : 0.f;
   if (q_row >= 0)
-    load_query_lds<D_QK>(qf, (nblk - 1) & 1 ? buf0 : buf1, hg, lane);
+    load_query_lds<D_QK>(qf, (nblk - 1 - t0) & 1 ? buf0 : buf1, hg, lane);
   else if (next >= 0)
     load_query<D_QK>(qf, a, next, head, half);
 
@@ -1153,6 +1173,25 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     ml_v = mx_fin * kLn2;
     lse_v = (m_fin + __log2f(l_fin)) * kLn2;
   }
+  if constexpr (SPLIT) {
+    // The split's output normalised by its own sum (the sink joins once, in
+    // the merge), 16 B per lane and value group straight from the
+    // accumulator layout; an empty split has lse = -inf (no contribution).
+    const size_t u = (size_t)unit * a.h_q + head;
+    const float inv = l_fin > 0.f ? 1.f / l_fin : 0.f;
+    float* o = a.ws_o + u * kDV + 4 * half;
+#pragma unroll
+    for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * j) =
+            f32x4{acc[ct][4 * j] * inv, acc[ct][4 * j + 1] * inv, acc[ct][4 * j + 2] * inv,
+                  acc[ct][4 * j + 3] * inv};
+    if (half == 0) {
+      a.ws_stats[2 * u] = l_fin > 0.f ? lse_v : -INFINITY;
+      a.ws_stats[2 * u + 1] = ml_v;
+    }
+  } else {
   if (half == 0 && (KS == 1 || ks == 0)) {
     a.lse[(size_t)row * a.h_q + head] = lse_v;
     a.max_logits[(size_t)row * a.h_q + head] = ml_v;
@@ -1245,8 +1284,63 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
     }
   }
-  if (next < 0) break;
-  row = next;
+  }
+  if (next_unit < 0) break;
+  unit = next_unit;
+  }
+}
+
+// Merge of the splits of split decode, one wave per (row, head): the split
+// lses give lse = logsumexp over the splits, each split's output enters with
+// weight exp(lse_s - lse), and an empty split (lse_s = -inf) contributes
+// nothing; the sink joins the denominator once, after the merge; a row
+// whose splits are all empty gives out = 0, lse = +inf, max_logits = -inf.
+// Lane l takes value columns 8l .. 8l + 7.
+template <bool SINK>
+__global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (long long)a.rows * a.h_q) return;
+  const int row = (int)(w / a.h_q), head = (int)(w % a.h_q), lane = lane_id();
+  const int S = a.splits;
+  const float* st = a.ws_stats + ((size_t)row * S * a.h_q + head) * 2;
+  const size_t sstride = (size_t)a.h_q * 2;  // between the splits of one head
+  float m = -INFINITY, mx = -INFINITY;
+  for (int s = 0; s < S; ++s) {
+    m = fmaxf(m, st[s * sstride]);
+    mx = fmaxf(mx, st[s * sstride + 1]);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse_v = INFINITY, ml_v = -INFINITY;
+  if (m != -INFINITY) {
+    float z = 0.f;
+    for (int s = 0; s < S; ++s) z += expf(st[s * sstride] - m);  // exp(-inf) = 0
+    const float lse = m + logf(z);
+    const float* o = a.ws_o + ((size_t)row * S * a.h_q + head) * kDV + 8 * lane;
+    const size_t ostride = (size_t)a.h_q * kDV;
+    for (int s = 0; s < S; ++s) {
+      const float wgt = expf(st[s * sstride] - lse);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(o + s * ostride);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += wgt * v0[e];
+        acc[4 + e] += wgt * v1[e];
+      }
+    }
+    float f = 1.f;
+    if (SINK) f = 1.f / (1.f + expf(a.attn_sink[head] - lse));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= f;
+    lse_v = lse;
+    ml_v = mx;
+  }
+  bf16x8 ob;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ob[e] = (__bf16)acc[e];
+  *reinterpret_cast<bf16x8*>(a.out + ((size_t)row * a.h_q + head) * kDV + 8 * lane) = ob;
+  if (lane == 0) {
+    a.lse[(size_t)row * a.h_q + head] = lse_v;
+    a.max_logits[(size_t)row * a.h_q + head] = ml_v;
   }
 }
 
@@ -1382,6 +1476,57 @@ smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
   return fail(SMLA_ERR_UNSUPPORTED, "no wide kernel instance for d_qk=%d", d_qk);
 }
 
+// Split decode: the wide kernel over (row, split) units writing partials to
+// the workspace, then the merge.  Only layouts without a key split (128
+// heads, or 64 heads at d_qk = 512).
+template <int D_QK, int NW, bool DYNAMIC, bool SINK>
+smla_status launch_split(const FwdArgs& args, hipStream_t stream) {
+  const int cus = cu_count();
+  if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
+  const long long units = (long long)args.rows * args.splits;
+  const long long slots = (long long)cus * (kWideWaves / NW);
+  const int grid = (int)(units < slots ? units : slots);
+  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, NW, 1, true, DYNAMIC, SINK, true>),
+                     dim3(grid), dim3(NW * 64), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  const long long waves = (long long)args.rows * args.h_q;
+  hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     stream, args);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+smla_status dispatch_split(int d_qk, FwdArgs& args, hipStream_t stream) {
+  if (!(args.h_q == 128 || (args.h_q == 64 && d_qk == 512)))
+    return fail(SMLA_ERR_UNSUPPORTED,
+                "split decode supports h_q=128, or h_q=64 at d_qk=512 (got h_q=%d, d_qk=%d)",
+                args.h_q, d_qk);
+  if (args.kv_span > kMaxKvSpan)
+    return fail(SMLA_ERR_UNSUPPORTED, "split decode: KV pool above %u bytes", kMaxKvSpan);
+  const int nw = args.h_q / 32;
+  const bool dyn = args.topk_length != nullptr;
+  const bool sink = args.attn_sink != nullptr;
+#define SMLA_SPLIT(D, W, DYN, SNK)                              \
+  if (d_qk == D && nw == W && dyn == DYN && sink == SNK)        \
+    return launch_split<D, W, DYN, SNK>(args, stream);
+  SMLA_SPLIT(512, 4, false, false)
+  SMLA_SPLIT(512, 4, false, true)
+  SMLA_SPLIT(512, 4, true, false)
+  SMLA_SPLIT(512, 4, true, true)
+  SMLA_SPLIT(512, 2, false, false)
+  SMLA_SPLIT(512, 2, false, true)
+  SMLA_SPLIT(512, 2, true, false)
+  SMLA_SPLIT(512, 2, true, true)
+  SMLA_SPLIT(576, 4, false, false)
+  SMLA_SPLIT(576, 4, false, true)
+  SMLA_SPLIT(576, 4, true, false)
+  SMLA_SPLIT(576, 4, true, true)
+#undef SMLA_SPLIT
+  return fail(SMLA_ERR_UNSUPPORTED, "no split decode instance for d_qk=%d", d_qk);
+}
+
 // KV table bytes for FwdArgs::kv_span; a table the wide kernel cannot address
 // with 32-bit offsets gets a value above kMaxKvSpan.
 uint32_t span_or_max(uint64_t bytes) {
@@ -1448,13 +1593,16 @@ extern "C" smla_status sparse_mla_fwd(const void* q, const void* kv, const int32
   return dispatch_fwd<false>(d_qk, args, static_cast<hipStream_t>(stream));
 }
 
-extern "C" smla_status sparse_mla_decode_fwd(
-    const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
-    const int32_t* indices, const int32_t* topk_length, const float* attn_sink, int32_t B,
-    int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
-    int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale, void* out,
-    float* lse, float* max_logits, smla_stream_t stream) {
-  g_last_error.clear();
+// Validation and arguments shared by both decode entry points; rows = 0 for
+// an empty batch.
+smla_status decode_args(const char* who, const void* q, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* cache_seqlens,
+                        const int32_t* indices, const int32_t* topk_length, const float* attn_sink,
+                        int32_t B, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                        int32_t d_v, int32_t topk, int32_t num_blocks, int32_t page_size,
+                        int32_t max_blocks_per_seq, float sm_scale, void* out, float* lse,
+                        float* max_logits, FwdArgs& args) {
+  args = FwdArgs{};
   if (B < 0 || s_q <= 0 || num_blocks < 0 || max_blocks_per_seq <= 0)
     return fail(SMLA_ERR_BAD_SHAPE, "bad sizes (B=%d s_q=%d num_blocks=%d max_blocks_per_seq=%d)",
                 B, s_q, num_blocks, max_blocks_per_seq);
@@ -1468,9 +1616,8 @@ extern "C" smla_status sparse_mla_decode_fwd(
   if (!q || (!kv_cache && num_blocks > 0) || !block_table || !cache_seqlens || !indices || !out ||
       !lse || !max_logits)
     return fail(SMLA_ERR_NULL_ARG,
-                "sparse_mla_decode_fwd: q, kv_cache (unless num_blocks = 0), block_table, "
-                "cache_seqlens, indices, out, lse and max_logits are required");
-  FwdArgs args{};
+                "%s: q, kv_cache (unless num_blocks = 0), block_table, cache_seqlens, indices, "
+                "out, lse and max_logits are required", who);
   args.q = static_cast<const __bf16*>(q);
   args.kv = static_cast<const uint8_t*>(kv_cache);
   args.indices = indices;
@@ -1489,7 +1636,63 @@ extern "C" smla_status sparse_mla_decode_fwd(
   args.mbps = max_blocks_per_seq;
   args.scale_log2 = sm_scale * kLog2e;
   args.kv_span = span_or_max((uint64_t)num_blocks * kPage * (uint64_t)d_qk * 2u);
+  args.splits = 1;
+  return SMLA_OK;
+}
+
+extern "C" smla_status sparse_mla_decode_fwd(
+    const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+    const int32_t* indices, const int32_t* topk_length, const float* attn_sink, int32_t B,
+    int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+    int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale, void* out,
+    float* lse, float* max_logits, smla_stream_t stream) {
+  g_last_error.clear();
+  FwdArgs args;
+  const smla_status st = decode_args("sparse_mla_decode_fwd", q, kv_cache, block_table,
+                                     cache_seqlens, indices, topk_length, attn_sink, B, s_q, h_q,
+                                     h_kv, d_qk, d_v, topk, num_blocks, page_size,
+                                     max_blocks_per_seq, sm_scale, out, lse, max_logits, args);
+  if (st != SMLA_OK || args.rows == 0) return st;
   return dispatch_fwd<true>(d_qk, args, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t sparse_mla_decode_split_workspace_bytes(int32_t B, int32_t s_q, int32_t h_q,
+                                                          int32_t d_v, int32_t num_splits) {
+  if (B <= 0 || s_q <= 0 || h_q <= 0 || d_v <= 0 || num_splits <= 1) return 0;
+  return (size_t)B * (size_t)s_q * (size_t)num_splits * (size_t)h_q * ((size_t)d_v + 2) *
+         sizeof(float);
+}
+
+extern "C" smla_status sparse_mla_decode_fwd_split(
+    const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+    const int32_t* indices, const int32_t* topk_length, const float* attn_sink, int32_t B,
+    int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+    int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale,
+    int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, float* lse,
+    float* max_logits, smla_stream_t stream) {
+  g_last_error.clear();
+  FwdArgs args;
+  smla_status st = decode_args("sparse_mla_decode_fwd_split", q, kv_cache, block_table,
+                               cache_seqlens, indices, topk_length, attn_sink, B, s_q, h_q, h_kv,
+                               d_qk, d_v, topk, num_blocks, page_size, max_blocks_per_seq, sm_scale,
+                               out, lse, max_logits, args);
+  if (st != SMLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(SMLA_ERR_BAD_SHAPE, "num_splits=%d (1 .. %d)", num_splits, kMaxSplits);
+  if ((long long)B * s_q * num_splits > 0x7fffffffLL)
+    return fail(SMLA_ERR_BAD_SHAPE, "B*s_q*num_splits overflows int32");
+  if (args.rows == 0) return SMLA_OK;
+  if (num_splits == 1) return dispatch_fwd<true>(d_qk, args, static_cast<hipStream_t>(stream));
+  const size_t need = sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits);
+  if (!workspace) return fail(SMLA_ERR_NULL_ARG, "sparse_mla_decode_fwd_split: workspace is required");
+  if (workspace_bytes < need)
+    return fail(SMLA_ERR_BAD_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 15u) != 0)
+    return fail(SMLA_ERR_BAD_SHAPE, "workspace must be 16-byte aligned");
+  args.splits = num_splits;
+  args.ws_o = static_cast<float*>(workspace);
+  args.ws_stats = args.ws_o + (size_t)args.rows * num_splits * h_q * kDV;
+  return dispatch_split(d_qk, args, static_cast<hipStream_t>(stream));
 }
 
 extern "C" smla_status sparse_mla_row_lengths(const int32_t* indices, const int32_t* topk_length,

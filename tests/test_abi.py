@@ -26,7 +26,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["sparse_mla_decode_fwd", "sparse_mla_fwd",
+    assert _declared_functions() == ["sparse_mla_decode_fwd", "sparse_mla_decode_fwd_split",
+                                     "sparse_mla_decode_split_workspace_bytes", "sparse_mla_fwd",
                                      "sparse_mla_last_error", "sparse_mla_row_lengths"]
 
 
@@ -100,6 +101,38 @@ def test_decode_rejects(lib, kw, status):
 def test_decode_empty_batch_is_noop(lib):
     assert _dec(lib, B=0) == 0
     assert _dec(lib, B=0, q=NULL, indices=NULL, out=NULL, block_table=NULL) == 0
+
+
+def _split(lib, **kw):
+    a = dict(q=P, kv_cache=P, block_table=P, cache_seqlens=P, indices=P, topk_length=NULL,
+             attn_sink=NULL, B=2, s_q=1, h_q=128, h_kv=1, d_qk=576, d_v=512, topk=64,
+             num_blocks=8, page_size=64, max_blocks_per_seq=4, sm_scale=0.1, num_splits=4,
+             workspace=P, workspace_bytes=1 << 30, out=P, lse=P, max_logits=P, stream=NULL)
+    a.update(kw)
+    return lib.sparse_mla_decode_fwd_split(*a.values())
+
+
+def test_split_workspace_bytes(lib):
+    f = lib.sparse_mla_decode_split_workspace_bytes
+    assert f(2, 3, 128, 512, 5) == 2 * 3 * 5 * 128 * 514 * 4
+    assert f(2, 3, 128, 512, 1) == 0 and f(0, 3, 128, 512, 4) == 0 and f(2, 3, 128, 512, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_splits=0), 2), (dict(num_splits=1025), 2), (dict(num_splits=-3), 2),
+    (dict(workspace=NULL), 1),
+    (dict(workspace_bytes=2 * 1 * 4 * 128 * 514 * 4 - 1), 2),
+    (dict(workspace=ctypes.c_void_p(24)), 2),
+    (dict(h_q=64), 3), (dict(h_q=96, d_qk=512), 3),
+    (dict(q=NULL), 1), (dict(page_size=32), 3), (dict(B=-1), 2),
+])
+def test_split_decode_rejects(lib, kw, status):
+    assert _split(lib, **kw) == status
+    assert lib.sparse_mla_last_error().decode()
+
+
+def test_split_decode_empty_batch_is_noop(lib):
+    assert _split(lib, B=0, workspace=NULL, workspace_bytes=0) == 0
 
 
 def test_row_lengths_rejects(lib):

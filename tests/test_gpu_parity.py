@@ -325,6 +325,24 @@ def test_prefill_rows_beyond_grid(h_q, d_qk):
                   c.name + " explicit lengths")
 
 
+@pytest.mark.parametrize("h_q,d_qk", [(64, 512), (64, 576), (128, 576)])
+def test_persistent_grid_is_schedule_invariant(h_q, d_qk):
+    """A row's result does not depend on the workgroup or the turn that
+    computes it: slices of a case (other grid sizes, other snake positions)
+    give the rows of the whole case bit for bit."""
+    c = W.make_prefill(f"sched_h{h_q}_d{d_qk}", s_q=600, s_kv=900, h_q=h_q, d_qk=d_qk, d_v=512,
+                       topk=160, layout="scattered", invalid_frac=0.2, empty_frac=0.03,
+                       with_sink=True, seed=23 + h_q + d_qk)
+    _say(c.name)
+    whole = run_prefill(c)
+    for lo, hi in ((0, 600), (37, 301), (250, 251), (599, 600), (100, 460)):
+        part = W.PrefillCase(c.name, c.q[lo:hi].contiguous(), c.kv, c.indices[lo:hi].contiguous(),
+                             None, c.attn_sink, c.sm_scale, c.d_v)
+        got = run_prefill(part)
+        ref = tuple(t[lo:hi] for t in whole)
+        assert_bitwise(ref, got, f"rows {lo}..{hi - 1}")
+
+
 @pytest.mark.parametrize("h_q", [64, 128])
 def test_decode_rows_beyond_grid(h_q):
     gen = torch.Generator().manual_seed(h_q)
@@ -336,6 +354,73 @@ def test_decode_rows_beyond_grid(h_q):
     dyn = run_decode(c)
     assert_parity(dyn, oracle_decode(c), c.name)
     assert_bitwise(dyn, run_decode(c, topk_length=None), f"{c.name} dynamic vs fixed")
+
+
+# ---------------------------------------------------------------------------
+# split-KV decode: every row's index blocks split several ways and merged
+# (lse = logsumexp of the splits, the sink once after the merge)
+# ---------------------------------------------------------------------------
+
+def run_decode_split(c, num_splits, topk_length="case", workspace=None):
+    tl = c.topk_length if topk_length == "case" else topk_length
+    q, kv, bt, cs, idx_d, tl_d, sk = _to([c.q, c.kv_cache, c.block_table, c.cache_seqlens,
+                                          c.indices, tl, c.attn_sink])
+    res = smla.decode_fwd_split(q, kv, bt, cs, idx_d, c.sm_scale, num_splits, c.d_v,
+                                attn_sink=sk, topk_length=tl_d, workspace=workspace)
+    torch.cuda.synchronize()
+    return res
+
+
+def _small_batch_decode(h_q=128, d_qk=576, with_sink=True, with_length=True, seed=31):
+    """The pages' small-batch decode shape (s_q = 2, topk 2048, variable KV
+    lengths), at cache lengths the oracle takes in seconds."""
+    seqlens = torch.tensor([2500, 4096])
+    return W.make_decode(f"split_b2_h{h_q}_d{d_qk}", batch=2, s_q=2, h_q=h_q, d_qk=d_qk, d_v=512,
+                         topk=2048, seqlens=seqlens, seed=seed, effective=2000,
+                         with_length=with_length, with_sink=with_sink)
+
+
+@pytest.mark.parametrize("num_splits", [2, 3, 7, 32, 40])
+def test_split_decode_matches_oracle(num_splits):
+    c = _small_batch_decode()
+    _say(f"{c.name} splits={num_splits}")
+    ref = oracle_decode(c)
+    got = run_decode_split(c, num_splits)
+    assert_parity(got, ref, f"{c.name} x{num_splits}")
+    # derived lengths (INT_MAX-poisoned tails) give the same split results
+    assert_bitwise(got, run_decode_split(c, num_splits, topk_length=None),
+                   f"{c.name} x{num_splits} dynamic vs fixed")
+    # and the unsplit path agrees within the parity tolerance
+    assert_parity(run_decode(c), ref, f"{c.name} unsplit")
+
+
+@pytest.mark.parametrize("h_q,d_qk,with_sink", [(128, 512, False), (64, 512, True),
+                                                 (128, 576, False)])
+def test_split_decode_layouts(h_q, d_qk, with_sink):
+    c = _small_batch_decode(h_q=h_q, d_qk=d_qk, with_sink=with_sink, with_length=False,
+                            seed=h_q + d_qk)
+    _say(f"{c.name} sink={with_sink}")
+    assert_parity(run_decode_split(c, 5), oracle_decode(c), c.name)
+
+
+def test_split_decode_short_and_empty_rows():
+    """Rows of length 0 and 1 (splits without keys), and a caller's workspace
+    used twice."""
+    c = _small_batch_decode(seed=5)
+    tl = torch.tensor([[0, 1], [64, 2000]], dtype=torch.int32)
+    _say("split decode short rows")
+    ref = oracle_decode(c, topk_length=tl)
+    need = smla.decode_split_workspace_bytes(2, 2, 128, 512, 9)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    a = run_decode_split(c, 9, topk_length=tl, workspace=ws)
+    assert_parity(a, ref, "split short rows")
+    assert_bitwise(a, run_decode_split(c, 9, topk_length=tl, workspace=ws), "workspace reused")
+
+
+def test_split_decode_unsupported_layout_raises():
+    c = _small_batch_decode(h_q=64, d_qk=576)
+    with pytest.raises(smla.SparseMLAError):
+        run_decode_split(c, 4)
 
 
 # ---------------------------------------------------------------------------
