@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_h64",
                     choices=["prefill_h64", "prefill_h64_len", "prefill_h128", "decode_dynamic",
-                             "decode_dynamic_nolen", "decode_fixed", "tiny"])
+                             "decode_dynamic_nolen", "decode_fixed", "decode_fixed_b2", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -78,6 +78,9 @@ def make_case(name):
         return W.decode_dynamic(with_length=False)
     if name == "decode_fixed":
         return W.decode_fixed()
+    if name == "decode_fixed_b2":
+        # the pages' small-batch run of the fixed top-k shape (B = 2)
+        return W.decode_fixed(batch=2)
     if name == "tiny":
         return W.tiny_prefill()
     raise ValueError(name)
@@ -141,7 +144,10 @@ def algorithmic_counts(case):
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def gpu_call(case, dev):
+def gpu_call(case, dev, num_splits=1):
+    """One call of the workload on `dev` with its inputs resident there;
+    decode with num_splits > 1 runs the split-KV path (workspace allocated
+    here, outside the call)."""
     import torch
     import sparse_top_mla_amd as smla
     t = lambda x: None if x is None else x.to(dev)  # noqa: E731
@@ -152,6 +158,16 @@ def gpu_call(case, dev):
         out = torch.empty(case.batch, case.s_q, case.h_q, case.d_v, dtype=torch.bfloat16, device=dev)
         lse = torch.empty(case.batch, case.s_q, case.h_q, dtype=torch.float32, device=dev)
         ml = torch.empty_like(lse)
+        if num_splits > 1:
+            ws = torch.empty(smla.decode_split_workspace_bytes(case.batch, case.s_q, case.h_q,
+                                                               case.d_v, num_splits),
+                             dtype=torch.uint8, device=dev)
+
+            def call():
+                smla.decode_fwd_split(*args, case.sm_scale, num_splits, case.d_v, attn_sink=sink,
+                                      topk_length=tl, workspace=ws, out=out, lse=lse,
+                                      max_logits=ml)
+            return call
 
         def call():
             smla.decode_fwd(*args, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl,
@@ -469,6 +485,20 @@ def main():
             "kernel_ms_median": statistics.median(per_cold),
             "hbm_gbs_algorithmic": counts["bytes"] / (statistics.fmean(per_cold) * 1e-3) / 1e9}
         del calls
+    rows = case.batch * case.s_q if is_decode(case) else case.s_q
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if is_decode(case) and rows < cus and case.h_q == 128:
+        # Fewer rows than CUs: the split-KV path, at the binding's split count.
+        import sparse_top_mla_amd as smla
+        splits = max(2, smla.decode_num_splits(case.batch, case.s_q, case.topk))
+        call_split = gpu_call(case, dev, num_splits=splits)
+        ms_split, per_split = time_steps(call_split, args.steps, args.warmup)
+        variants[f"split_{splits}"] = {
+            "num_splits": splits, "ms_per_call": ms_split,
+            "kernel_ms": statistics.fmean(per_split),
+            "kernel_ms_median": statistics.median(per_split),
+            "hbm_gbs_algorithmic": counts["bytes"] / (statistics.fmean(per_split) * 1e-3) / 1e9}
+        del call_split
     if args.workload == "prefill_h64":
         case_len = make_case("prefill_h64_len")
         call_len = gpu_call(case_len, dev)

@@ -4,7 +4,9 @@ The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
 of include/sparse_mla.h (libsparse_mla.so); this package only binds it.
 """
 from ._binding import (EXPORTS, SparseMLAError, decode_fwd, decode_fwd_split,  # noqa: F401
-                       decode_split_workspace_bytes, fwd, load_library, row_lengths)
+                       decode_num_splits, decode_split_workspace_bytes, fwd, load_library,
+                       row_lengths)
 
-__all__ = ["fwd", "decode_fwd", "decode_fwd_split", "decode_split_workspace_bytes", "row_lengths",
+__all__ = ["fwd", "decode_fwd", "decode_fwd_split", "decode_num_splits",
+           "decode_split_workspace_bytes", "row_lengths",
            "load_library", "SparseMLAError", "EXPORTS"]

