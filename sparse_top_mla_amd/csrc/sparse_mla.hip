@@ -1681,6 +1681,8 @@ extern "C" smla_status sparse_mla_decode_fwd_split(
     return fail(SMLA_ERR_BAD_SHAPE, "num_splits=%d (1 .. %d)", num_splits, kMaxSplits);
   if ((long long)B * s_q * num_splits > 0x7fffffffLL)
     return fail(SMLA_ERR_BAD_SHAPE, "B*s_q*num_splits overflows int32");
+  if ((long long)B * s_q * h_q > 0x7fffffffLL)  // the merge's grid: one wave per (row, head)
+    return fail(SMLA_ERR_BAD_SHAPE, "B*s_q*h_q overflows int32");
   if (args.rows == 0) return SMLA_OK;
   if (num_splits == 1) return dispatch_fwd<true>(d_qk, args, static_cast<hipStream_t>(stream));
   const size_t need = sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits);

@@ -125,6 +125,7 @@ def test_split_workspace_bytes(lib):
     (dict(workspace=ctypes.c_void_p(24)), 2),
     (dict(h_q=64), 3), (dict(h_q=96, d_qk=512), 3),
     (dict(q=NULL), 1), (dict(page_size=32), 3), (dict(B=-1), 2),
+    (dict(B=1 << 20, s_q=1 << 4, num_splits=2), 2),
 ])
 def test_split_decode_rejects(lib, kw, status):
     assert _split(lib, **kw) == status
