@@ -262,10 +262,15 @@ def cpu_baseline(case, counts, target_s):
 # ---------------------------------------------------------------------------
 
 def kernel_source_digest():
-    """Digest of the kernel source without comments and blank lines, so that
-    stored counter figures stay attached to the code they were taken on."""
+    """Digest of the device code (the source above its host-side section)
+    without comments and blank lines, so that stored counter figures stay
+    attached to the kernels they were taken on; host-side validation and
+    dispatch changes do not touch them."""
     import re
     src = (ROOT / "sparse_top_mla_amd" / "csrc" / "sparse_mla.hip").read_text()
+    cut = src.find("\n// host side\n")
+    if cut >= 0:
+        src = src[:cut]
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     src = re.sub(r"//[^\n]*", "", src)
     code = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
