@@ -424,6 +424,54 @@ def test_split_decode_unsupported_layout_raises():
 
 
 # ---------------------------------------------------------------------------
+# randomized shapes: head counts, d_qk, row counts beyond the grid, lengths,
+# sinks, paging and split counts drawn from a fixed seed
+# ---------------------------------------------------------------------------
+
+def _random_case(rng, i):
+    h = rng.choice([64, 128, 64, 128, 16, 96]); d = rng.choice([512, 576])
+    sink = rng.random() < 0.5
+    seed = rng.randrange(1 << 20)
+    if rng.random() < 0.6:
+        s_kv = rng.choice([100, 700, 2000])
+        topk = min(rng.choice([1, 31, 33, 64, 65, 96, 200, 256]), s_kv)
+        lay = rng.choice(["scattered", "ramp"])
+        kw = (dict(invalid_frac=rng.choice([0.0, 0.1, 0.5]), empty_frac=0.05)
+              if lay == "scattered" else dict(ramp_cap=topk // 2 + 1))
+        c = W.make_prefill(f"rnd{i}_h{h}_d{d}", s_q=rng.choice([3, 100, 300, 513]), s_kv=s_kv,
+                           h_q=h, d_qk=d, d_v=512, topk=topk, layout=lay, seed=seed,
+                           with_sink=sink, **kw)
+        tl = None
+        if rng.random() < 0.4:
+            tl = torch.randint(0, topk + 1, (c.s_q,), dtype=torch.int32,
+                               generator=torch.Generator().manual_seed(seed))
+        return c, tl, 0
+    B, s_q, topk = rng.choice([2, 40, 150]), rng.choice([1, 2, 3]), rng.choice([64, 128, 256])
+    eff = rng.choice([topk, topk // 2])
+    seqlens = torch.randint(eff, eff + 900, (B,), generator=torch.Generator().manual_seed(seed))
+    c = W.make_decode(f"rnd{i}_dec_h{h}_d{d}", batch=B, s_q=s_q, h_q=h, d_qk=d, d_v=512,
+                      topk=topk, seqlens=seqlens, seed=seed, effective=eff,
+                      with_length=rng.random() < 0.5, with_sink=sink)
+    split_ok = h == 128 or (h == 64 and d == 512)
+    return c, None, rng.choice([1, 2, 5]) if split_ok else 1
+
+
+def test_randomized_shapes():
+    import random
+    rng = random.Random(2024)
+    for i in range(24):
+        c, tl, splits = _random_case(rng, i)
+        _say(f"{c.name} splits={splits}")
+        if hasattr(c, "kv_cache"):
+            got = run_decode_split(c, splits) if splits > 1 else run_decode(c)
+            assert_parity(got, oracle_decode(c), c.name)
+        else:
+            got = run_prefill(c, topk_length=tl if tl is not None else "case")
+            assert_parity(got, oracle_prefill(c, topk_length=tl if tl is not None else "case"),
+                          c.name)
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times:
 # sampled rows against the oracle, properties on every row
 # ---------------------------------------------------------------------------
