@@ -424,6 +424,50 @@ def test_split_decode_unsupported_layout_raises():
 
 
 # ---------------------------------------------------------------------------
+# the recompute: a logit far above the first tile's maximum (more than 2^64
+# in exp2 units) makes the workgroup redo the row with the true maximum as
+# the reference.  Head 0's query of a planted row is scaled by 10 and one key
+# (after the first tile) is that row's original query, so its logit leads by
+# about 290 in log2 units while V keeps ordinary magnitudes.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h_q,d_qk", [(64, 512), (64, 576), (128, 576)])
+def test_recompute_on_dominant_logit(h_q, d_qk):
+    c = W.make_prefill(f"recompute_h{h_q}_d{d_qk}", s_q=300, s_kv=1200, h_q=h_q, d_qk=d_qk,
+                       d_v=512, topk=192, layout="scattered", seed=41 + h_q + d_qk,
+                       with_sink=True)
+    idx = c.indices.view(c.s_q, c.topk)
+    rows = [0, 7, 150, 263, 299]
+    for j, r in enumerate(rows):
+        kvr = 1100 + j                    # KV rows no other index names
+        idx[r][idx[r] == kvr] = 0
+        c.kv[kvr, 0] = c.q[r, 0]
+        c.q[r, 0] = (10.0 * c.q[r, 0].float()).to(torch.bfloat16)
+        idx[r, 100 + j] = kvr             # after the first tile (and block)
+    _say(c.name)
+    res = run_prefill(c)
+    ref = oracle_prefill(c)
+    assert np.all(ref[1][rows, 0] > ref[1][rows, 1] + 150)  # the planted logit dominates head 0
+    assert_parity(res, ref, c.name)
+
+
+def test_recompute_in_split_decode():
+    c = _small_batch_decode(seed=43, with_length=False)
+    idx = c.indices.view(4, c.topk)
+    pos = 1500                            # late in the row: a later split
+    for r in range(4):
+        b = r // 2
+        tok = int(idx[r, pos].item())
+        page = int(c.block_table[b, tok // 64].item())
+        c.kv_cache[page, tok % 64, 0] = c.q[b, r % 2, 0]
+        c.q[b, r % 2, 0] = (10.0 * c.q[b, r % 2, 0].float()).to(torch.bfloat16)
+    _say("split decode recompute")
+    ref = oracle_decode(c)
+    assert_parity(run_decode_split(c, 8), ref, "split recompute")
+    assert_parity(run_decode(c), ref, "unsplit recompute")
+
+
+# ---------------------------------------------------------------------------
 # randomized shapes: head counts, d_qk, row counts beyond the grid, lengths,
 # sinks, paging and split counts drawn from a fixed seed
 # ---------------------------------------------------------------------------
