@@ -468,6 +468,61 @@ def test_recompute_in_split_decode():
 
 
 # ---------------------------------------------------------------------------
+# KV tables past 4 GiB (beyond the wide kernel's 32-bit buffer offsets): the
+# rows of a small case are placed at rows or pages of a larger table, many of
+# them past the 4 GiB mark, and the results must be the small case's
+# ---------------------------------------------------------------------------
+
+BIG_ROWS = (1 << 32) // 1152 + 40_000  # ~4.35 GB at d_qk = 576
+
+
+@pytest.mark.parametrize("h_q", [64, 128])
+def test_kv_table_past_4gib(h_q):
+    small = W.make_prefill(f"big_kv_h{h_q}", s_q=6, s_kv=768, h_q=h_q, d_qk=576, d_v=512, topk=128,
+                           layout="scattered", invalid_frac=0.2, seed=5 + h_q, with_sink=True)
+    gen = torch.Generator().manual_seed(6)
+    pos = torch.randperm(BIG_ROWS - 700_000, generator=gen)[:small.s_kv]
+    pos[::2] = BIG_ROWS - 1 - torch.arange(0, small.s_kv, 2)  # half of them in the last rows
+    idx = small.indices.long()
+    ok = (idx >= 0) & (idx < small.s_kv)
+    # invalid entries stay invalid in the big table (-1; an out-of-range value
+    # of the small table may be a row of the big one)
+    big_idx = torch.where(ok, pos[idx.clamp(0, small.s_kv - 1)], -1).to(torch.int32)
+    kv_big = torch.zeros((BIG_ROWS, 1, 576), dtype=torch.bfloat16, device=DEV)
+    kv_big[pos.to(DEV)] = small.kv.to(DEV)
+    _say(small.name)
+    sk = small.attn_sink.to(DEV)
+    res = smla.fwd(small.q.to(DEV), kv_big, big_idx.to(DEV), small.sm_scale, small.d_v,
+                   attn_sink=sk)
+    torch.cuda.synchronize()
+    assert_parity(res, oracle_prefill(small), small.name + " in a >4 GiB table")
+    del kv_big
+    torch.cuda.empty_cache()
+
+
+def test_decode_pool_past_4gib():
+    c = W.make_decode("big_pool", batch=3, s_q=2, h_q=128, d_qk=576, d_v=512, topk=256,
+                      seqlens=torch.tensor([900, 300, 2000]), seed=8, effective=200,
+                      with_length=True, with_sink=True, spare_pages=4)
+    big_pages = BIG_ROWS // 64
+    gen = torch.Generator().manual_seed(9)
+    n = c.kv_cache.shape[0]
+    new_page = (big_pages - 1 - torch.randperm(big_pages // 4, generator=gen)[:n]).to(torch.int32)
+    bt = c.block_table.clone()
+    bt[bt >= 0] = new_page[bt[bt >= 0].long()]
+    pool = torch.zeros((big_pages, 64, 1, 576), dtype=torch.bfloat16, device=DEV)
+    pool[new_page.long().to(DEV)] = c.kv_cache.to(DEV)
+    _say(c.name)
+    t = lambda x: None if x is None else x.to(DEV)  # noqa: E731
+    res = smla.decode_fwd(t(c.q), pool, t(bt), t(c.cache_seqlens), t(c.indices), c.sm_scale,
+                          c.d_v, attn_sink=t(c.attn_sink), topk_length=t(c.topk_length))
+    torch.cuda.synchronize()
+    assert_parity(res, oracle_decode(c), c.name + " in a >4 GiB pool")
+    del pool
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # randomized shapes: head counts, d_qk, row counts beyond the grid, lengths,
 # sinks, paging and split counts drawn from a fixed seed
 # ---------------------------------------------------------------------------
