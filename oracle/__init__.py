@@ -12,6 +12,9 @@ Parity status per function (what pins it is listed in tests/oracle_pins.py):
                        force, closed forms, sink closed form)
   sparse_mla_decode_fwd pinned (paged == prefill on a numpy-gathered cache,
                        dense library attention on contiguous pages)
+  sparse_mla_bwd       pinned (float64 autograd of dense attention with the
+                       multiplicity bias, with and without a sink column;
+                       single-key closed form; base-2 lse; selections)
 """
 from __future__ import annotations
 
@@ -48,6 +51,10 @@ def _bind(lib):
                                                  i32, i32, i64, i32, i32, dbl, vp, i64, vp, vp,
                                                  vp, vp, ctypes.c_int]
     lib.oracle_sparse_mla_decode_fwd.restype = ctypes.c_int
+    lib.oracle_sparse_mla_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32,
+                                          i32, dbl, ctypes.c_int, vp, i64, vp, i64, vp, vp, vp,
+                                          ctypes.c_int]
+    lib.oracle_sparse_mla_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -170,3 +177,52 @@ def sparse_mla_decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_s
     if rc:
         raise ValueError(f"oracle_sparse_mla_decode_fwd failed ({rc})")
     return out, lse, ml, rl
+
+
+def sparse_mla_bwd(q, kv, out, dout, indices, lse, sm_scale, d_v, attn_sink=None,
+                   topk_length=None, lse_base2=False, rows=None, kv_rows=None, want_dq=True,
+                   want_dkv=True, want_d_sink=False, threads=None, lib=None):
+    """Backward oracle.  q [s_q, h_q, d_qk] bf16; kv [s_kv, 1, d_qk] bf16;
+    out, dout [s_q, h_q, d_v] (bf16 or float; widened to float64);
+    indices [s_q, 1, topk]; lse [s_q, h_q] (natural log, or base 2 with
+    lse_base2).  Returns (dq [n, h_q, d_qk] f64 or None, dkv [n_kv, d_qk] f64
+    or None, d_sink [h_q] f64 or None); `rows` / `kv_rows` select the query
+    rows of dq and the KV rows of dkv (all when None)."""
+    lib = lib or load()
+    qn = _np(q, np.uint16)
+    kvn = _np(kv, np.uint16)
+    s_q, h_q, d_qk = qn.shape
+    s_kv = kvn.shape[0]
+    idx = _np(indices, np.int32)
+    topk = idx.shape[-1]
+    on = _f64_array(out).reshape(s_q, h_q, d_v)
+    don = _f64_array(dout).reshape(s_q, h_q, d_v)
+    ln = _f64_array(lse).reshape(s_q, h_q)
+    sel = None if rows is None else _np(rows, np.int64)
+    ksel = None if kv_rows is None else _np(kv_rows, np.int64)
+    n = s_q if sel is None else sel.size
+    nk = s_kv if ksel is None else ksel.size
+    dq = np.empty((n, h_q, d_qk)) if want_dq else None
+    dkv = np.empty((nk, d_qk)) if want_dkv else None
+    ds = np.empty(h_q) if want_d_sink else None
+    sink = _np(attn_sink, np.float32)
+    tl = _np(topk_length, np.int32)
+    rc = lib.oracle_sparse_mla_bwd(_ptr(qn), _ptr(kvn), _ptr(on), _ptr(don), _ptr(idx), _ptr(tl),
+                                   _ptr(ln), _ptr(sink), s_q, s_kv, h_q, d_qk, d_v, topk,
+                                   float(sm_scale), int(bool(lse_base2)), _ptr(sel), n,
+                                   _ptr(ksel), nk, _ptr(dq), _ptr(dkv), _ptr(ds),
+                                   _threads(threads))
+    if rc:
+        raise ValueError(f"oracle_sparse_mla_bwd failed ({rc})")
+    return dq, dkv, ds
+
+
+def _f64_array(x):
+    """torch (any float dtype, bf16 included) / numpy -> contiguous float64."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().cpu().to(torch.float64).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))

@@ -248,3 +248,180 @@ int oracle_sparse_mla_decode_fwd(const uint16_t *q, const uint16_t *kv_cache,
     }
     return bad ? 3 : 0;
 }
+
+/* Backward of the prefill operation (FlashMLA PR #198, "Summary", item 1: the
+ * sparse MLA backward works from the forward's saved out and lse; the key and
+ * value gradients of a row go to the KV row the index names, summed over every
+ * query row, head and occurrence).  It is the gradient of the forward's
+ * definition above, written out per (query row i, key occurrence j, head h):
+ *
+ *   lse'  = lse                          (natural log, as the forward returns)
+ *         = lse * ln 2                   (lse_base2: the pages' bwd takes
+ *                                          base-2 lse)
+ *         = ln(exp(lse') + exp(sink[h])) (with attn_sink: the forward's lse
+ *                                          leaves the sink out; the softmax
+ *                                          denominator holds it)
+ *   p     = exp(s_j - lse')              (the forward's softmax weight)
+ *   delta = sum_c dout[c] * out[c]       (c < d_v; d out / d s_j = p (v_j - out))
+ *   dp    = sum_c dout[c] * kv[key_j][c]
+ *   ds    = p * (dp - delta)             (d loss / d s_j)
+ *   dq[i][h][d]      += sm_scale * ds * kv[key_j][d]           d < d_qk
+ *   dkv[key_j][d]    += sm_scale * ds * q[i][h][d]             d < d_qk
+ *   dkv[key_j][c]    += p * dout[c]                            c < d_v
+ *   d_sink[h]        -= exp(sink[h] - lse') * delta            (once per row)
+ *
+ * The keys of a row are the forward's (valid positions before the row's
+ * length, each occurrence once).  A row whose lse' is +inf (no key) adds
+ * nothing.  out and dout come in as doubles (the caller widens bf16 exactly).
+ *
+ * dq is evaluated for the rows rows_sel lists (all rows when NULL), dkv for
+ * the KV rows kv_sel lists (all when NULL), each a sum over the query rows
+ * that name it, gathered through a per-KV-row list of (row) occurrences. */
+
+/* lse' of (row, head), see above. */
+static double effective_lse(double lse, int lse_base2, const float *attn_sink, int32_t h)
+{
+    double l = lse_base2 ? lse * log(2.0) : lse;
+    if (attn_sink != NULL && !isinf(l)) {
+        double s = (double)attn_sink[h];
+        double m = l > s ? l : s;
+        l = m + log(exp(l - m) + exp(s - m));
+    }
+    return l;
+}
+
+/* Gradient terms of one (row, key occurrence) over all heads.  dq_row
+ * [h_q][d_qk] and dkv_row [d_qk] are added to when not NULL. */
+static void key_grad(const uint16_t *q_row, const uint16_t *key, const double *dout_row,
+                     const double *lse_eff, const double *delta, int32_t h_q, int32_t d_qk,
+                     int32_t d_v, double sm_scale, double *dq_row, double *dkv_row)
+{
+    for (int32_t h = 0; h < h_q; ++h) {
+        if (isinf(lse_eff[h])) continue;
+        const uint16_t *qh = q_row + (int64_t)h * d_qk;
+        const double *doh = dout_row + (int64_t)h * d_v;
+        double acc = 0.0;
+        for (int32_t d = 0; d < d_qk; ++d) acc += bf16_to_double(qh[d]) * bf16_to_double(key[d]);
+        double p = exp(sm_scale * acc - lse_eff[h]);
+        double dp = 0.0;
+        for (int32_t c = 0; c < d_v; ++c) dp += doh[c] * bf16_to_double(key[c]);
+        double ds = p * (dp - delta[h]);
+        if (dq_row != NULL) {
+            double *dqh = dq_row + (int64_t)h * d_qk;
+            for (int32_t d = 0; d < d_qk; ++d) dqh[d] += sm_scale * ds * bf16_to_double(key[d]);
+        }
+        if (dkv_row != NULL) {
+            for (int32_t d = 0; d < d_qk; ++d) dkv_row[d] += sm_scale * ds * bf16_to_double(qh[d]);
+            for (int32_t c = 0; c < d_v; ++c) dkv_row[c] += p * doh[c];
+        }
+    }
+}
+
+/* q [s_q][h_q][d_qk] bf16; kv [s_kv][d_qk] bf16; out, dout [s_q][h_q][d_v]
+ * double; indices [s_q][topk]; topk_length [s_q] or NULL; lse [s_q][h_q];
+ * attn_sink [h_q] or NULL.  Outputs: dq [n_sel][h_q][d_qk] (NULL: skipped),
+ * dkv [n_kv_sel][d_qk] (NULL: skipped), d_sink [h_q] (NULL: skipped; needs
+ * attn_sink). */
+int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const double *out,
+                          const double *dout, const int32_t *indices, const int32_t *topk_length,
+                          const double *lse, const float *attn_sink, int64_t s_q, int64_t s_kv,
+                          int32_t h_q, int32_t d_qk, int32_t d_v, int32_t topk, double sm_scale,
+                          int lse_base2, const int64_t *rows_sel, int64_t n_sel,
+                          const int64_t *kv_sel, int64_t n_kv_sel, double *dq, double *dkv,
+                          double *d_sink, int threads)
+{
+    if (!q || !kv || !out || !dout || !indices || !lse) return 1;
+    if (h_q <= 0 || d_qk <= 0 || d_v <= 0 || d_v > d_qk || topk <= 0 || s_q < 0 || s_kv < 0)
+        return 2;
+    if (d_sink != NULL && attn_sink == NULL) return 2;
+    if (rows_sel == NULL) n_sel = s_q;
+    if (kv_sel == NULL) n_kv_sel = s_kv;
+    const int nt = oracle_threads(threads);
+
+    /* Per row: length, lse' and delta of every head. */
+    int32_t *len = malloc(sizeof(int32_t) * (size_t)(s_q > 0 ? s_q : 1));
+    double *lse_eff = malloc(sizeof(double) * (size_t)(s_q * h_q > 0 ? s_q * h_q : 1));
+    double *delta = malloc(sizeof(double) * (size_t)(s_q * h_q > 0 ? s_q * h_q : 1));
+    if (!len || !lse_eff || !delta) { free(len); free(lse_eff); free(delta); return 3; }
+    for (int64_t i = 0; i < s_q; ++i) {
+        len[i] = row_length(indices + i * topk, topk, topk_length ? topk_length + i : NULL, s_kv);
+        for (int32_t h = 0; h < h_q; ++h) {
+            int64_t rh = i * h_q + h;
+            lse_eff[rh] = effective_lse(lse[rh], lse_base2, attn_sink, h);
+            double dl = 0.0;
+            for (int32_t c = 0; c < d_v; ++c) dl += dout[rh * d_v + c] * out[rh * d_v + c];
+            delta[rh] = dl;
+        }
+    }
+
+    int bad = 0;
+    if (dq != NULL) {
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(| : bad)
+        for (int64_t n = 0; n < n_sel; ++n) {
+            int64_t i = rows_sel ? rows_sel[n] : n;
+            double *dq_row = dq + n * (int64_t)h_q * d_qk;
+            for (int64_t e = 0; e < (int64_t)h_q * d_qk; ++e) dq_row[e] = 0.0;
+            if (i < 0 || i >= s_q) { bad = 1; continue; }
+            const int32_t *idx = indices + i * topk;
+            for (int32_t j = 0; j < len[i]; ++j)
+                if (is_valid_index(idx[j], s_kv))
+                    key_grad(q + i * (int64_t)h_q * d_qk, kv + (int64_t)idx[j] * d_qk,
+                             dout + i * (int64_t)h_q * d_v, lse_eff + i * h_q, delta + i * h_q,
+                             h_q, d_qk, d_v, sm_scale, dq_row, NULL);
+        }
+    }
+
+    if (dkv != NULL && !bad) {
+        /* Occurrence lists: first[k] .. first[k + 1] - 1 in `who` are the query
+         * rows naming KV row k, in row then position order. */
+        int64_t *first = calloc((size_t)s_kv + 1, sizeof(int64_t));
+        if (!first) bad = 1;
+        for (int64_t i = 0; !bad && i < s_q; ++i)
+            for (int32_t j = 0; j < len[i]; ++j) {
+                int32_t k = indices[i * topk + j];
+                if (is_valid_index(k, s_kv)) first[k + 1]++;
+            }
+        for (int64_t k = 0; !bad && k < s_kv; ++k) first[k + 1] += first[k];
+        int64_t total = bad ? 0 : first[s_kv];
+        int64_t *who = malloc(sizeof(int64_t) * (size_t)(total > 0 ? total : 1));
+        int64_t *fill = calloc((size_t)s_kv + 1, sizeof(int64_t));
+        if (!who || !fill) bad = 1;
+        for (int64_t i = 0; !bad && i < s_q; ++i)
+            for (int32_t j = 0; j < len[i]; ++j) {
+                int32_t k = indices[i * topk + j];
+                if (is_valid_index(k, s_kv)) who[first[k] + fill[k]++] = i;
+            }
+        if (!bad) {
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(| : bad)
+            for (int64_t n = 0; n < n_kv_sel; ++n) {
+                int64_t k = kv_sel ? kv_sel[n] : n;
+                double *dkv_row = dkv + n * (int64_t)d_qk;
+                for (int32_t d = 0; d < d_qk; ++d) dkv_row[d] = 0.0;
+                if (k < 0 || k >= s_kv) { bad = 1; continue; }
+                for (int64_t e = first[k]; e < first[k + 1]; ++e) {
+                    int64_t i = who[e];
+                    key_grad(q + i * (int64_t)h_q * d_qk, kv + k * (int64_t)d_qk,
+                             dout + i * (int64_t)h_q * d_v, lse_eff + i * h_q, delta + i * h_q,
+                             h_q, d_qk, d_v, sm_scale, NULL, dkv_row);
+                }
+            }
+        }
+        free(first);
+        free(who);
+        free(fill);
+    }
+
+    if (d_sink != NULL && !bad) {
+        for (int32_t h = 0; h < h_q; ++h) d_sink[h] = 0.0;
+        for (int64_t i = 0; i < s_q; ++i)
+            for (int32_t h = 0; h < h_q; ++h) {
+                int64_t rh = i * h_q + h;
+                if (isinf(lse_eff[rh])) continue;
+                d_sink[h] -= exp((double)attn_sink[h] - lse_eff[rh]) * delta[rh];
+            }
+    }
+    free(len);
+    free(lse_eff);
+    free(delta);
+    return bad ? 3 : 0;
+}

@@ -16,7 +16,11 @@ AssertionError when the oracle disagrees with:
     PR #196 "Correctness notes"; row lengths of tests/golden/row_lengths.txt);
   * invariances the pages state (derived == explicit length, PR #196
     "Numbers"; INT_MAX-poisoned dynamic == -1-padded fixed, PR #216
-    "Dynamic top-k"; any invalid encoding masks alike, PR #196 "Fix").
+    "Dynamic top-k"; any invalid encoding masks alike, PR #196 "Fix");
+  * for the backward (PR #198, "Summary", item 1): float64 autograd of the
+    dense multiplicity-bias attention (with the sink as an extra value-less
+    column, PR #198 "Numerics"), a single-key closed form, base-2 lse
+    (PR #198's bwd contract) and row / KV-row selection.
 
 tests/test_oracle_pins.py runs them on the real oracle;
 tests/test_oracle_mutants.py checks that each planted mistake fails one.
@@ -436,6 +440,119 @@ def pin_row_selection(lib):
         assert np.array_equal(a[sel], b)
 
 
+# ---------------------------------------------------------------------------
+# backward pins
+# ---------------------------------------------------------------------------
+
+def _dense_bwd_reference(q, kv, indices, sm_scale, d_v, dout, topk_length=None, sink=None):
+    """float64 torch autograd of dense attention over every KV row with bias
+    ln(count) (count: how often a row is named before the row's length) and,
+    with a sink, one more value-less column of logit sink[h].  Returns
+    (out, sink-free lse, dq, dkv, d_sink); rows without keys are left out of
+    the loss (out 0, lse +inf)."""
+    qd = _f64(q).clone().requires_grad_(True)
+    kvd = _f64(kv[:, 0, :]).clone().requires_grad_(True)
+    sd = None if sink is None else sink.to(torch.float64).clone().requires_grad_(True)
+    idx = indices.reshape(indices.shape[0], -1).numpy().astype(np.int64)
+    s_q, h_q, _ = qd.shape
+    s_kv = kvd.shape[0]
+    topk = idx.shape[1]
+    out = torch.zeros(s_q, h_q, d_v, dtype=torch.float64)
+    lse = torch.full((s_q, h_q), math.inf, dtype=torch.float64)
+    loss = torch.zeros((), dtype=torch.float64)
+    for r in range(s_q):
+        valid = (idx[r] >= 0) & (idx[r] < s_kv)
+        if topk_length is None:
+            nz = np.nonzero(valid)[0]
+            L = int(nz[-1]) + 1 if nz.size else 0
+        else:
+            L = int(min(max(int(topk_length[r]), 0), topk))
+        count = np.bincount(idx[r, :L][valid[:L]], minlength=s_kv).astype(np.float64)
+        if count.sum() == 0:
+            continue
+        with np.errstate(divide="ignore"):
+            bias = torch.from_numpy(np.log(count))
+        scores = sm_scale * (qd[r] @ kvd.T) + bias[None, :]
+        full = scores if sd is None else torch.cat([scores, sd[:, None]], dim=1)
+        p = torch.softmax(full, dim=1)[:, :s_kv]
+        o = p @ kvd[:, :d_v]
+        loss = loss + (_f64(dout[r]) * o).sum()
+        out[r] = o.detach()
+        lse[r] = torch.logsumexp(scores, dim=1).detach()
+    loss.backward()
+    d_sink = None if sd is None else sd.grad.numpy()
+    return out, lse, qd.grad.numpy(), kvd.grad.numpy(), d_sink
+
+
+def _bwd_case(seed, s_q=6, s_kv=29, h_q=3, d_qk=20, d_v=12, topk=17):
+    gen, q, kv = _tiny(seed, s_q, s_kv, h_q, d_qk, d_v)
+    idx = torch.randint(0, s_kv, (s_q, 1, topk), generator=gen).to(torch.int32)
+    idx[0, 0, 3] = idx[0, 0, 1]            # a repeated key
+    idx[1, 0, -4:] = -1                    # -1 padded tail
+    idx[2, 0, 5] = s_kv                    # invalid entries inside the row
+    idx[2, 0, 7] = INT32_MAX
+    idx[3, 0, :] = -1                      # a row without keys
+    dout = _bf16((s_q, h_q, d_v), gen)
+    return gen, q, kv, idx, dout
+
+
+def pin_bwd_equals_autograd(lib):
+    """dq, dkv (and d_sink) equal float64 autograd of the dense formulation,
+    with and without topk_length and a sink."""
+    for seed, with_len, with_sink in [(201, False, False), (202, True, False), (203, False, True),
+                                      (204, True, True)]:
+        gen, q, kv, idx, dout = _bwd_case(seed)
+        s_q, h_q = q.shape[0], q.shape[1]
+        tl = torch.randint(0, idx.shape[-1] + 3, (s_q,), generator=gen).to(torch.int32) \
+            if with_len else None
+        sink = (torch.randn(h_q, generator=gen) * 2).to(torch.float32) if with_sink else None
+        scale = 0.45
+        out, lse, dq_ref, dkv_ref, ds_ref = _dense_bwd_reference(q, kv, idx, scale, 12, dout, tl,
+                                                                 sink)
+        dq, dkv, ds = oracle.sparse_mla_bwd(q, kv, out, dout, idx, lse, scale, 12, attn_sink=sink,
+                                            topk_length=tl, want_d_sink=with_sink, lib=lib)
+        _close(dq, dq_ref, 1e-9, 1e-11, f"dq seed {seed}")
+        _close(dkv, dkv_ref, 1e-9, 1e-11, f"dkv seed {seed}")
+        if with_sink:
+            _close(ds, ds_ref, 1e-9, 1e-11, f"d_sink seed {seed}")
+        assert np.all(dq[3] == 0.0), "a row without keys has a zero dq"
+
+
+def pin_bwd_single_key(lib):
+    """One key per row: out = v and p = 1, so dq = 0 and the key's row gets the
+    sum of dout over its heads (and rows) in the value columns, nothing else."""
+    gen, q, kv = _tiny(211, 5, 11, 3, 20, 12)
+    keys = torch.tensor([4, 7, 4, 0, 10], dtype=torch.int32)
+    idx = torch.full((5, 1, 6), -1, dtype=torch.int32)
+    idx[torch.arange(5), 0, torch.tensor([0, 2, 5, 1, 3])] = keys
+    dout = _bf16((5, 3, 12), gen)
+    kvn = _f64(kv[:, 0, :]).numpy()
+    out = np.stack([np.tile(kvn[int(k), :12], (3, 1)) for k in keys])
+    lse = np.stack([0.3 * (_f64(q[r]).numpy() @ kvn[int(keys[r])]) for r in range(5)])
+    dq, dkv, _ = oracle.sparse_mla_bwd(q, kv, out, dout, idx, lse, 0.3, 12, lib=lib)
+    assert np.abs(dq).max() < 1e-12, "dq of single-key rows"
+    want = np.zeros((11, 20))
+    for r in range(5):
+        want[int(keys[r]), :12] += _f64(dout[r]).numpy().sum(axis=0)
+    _close(dkv, want, 1e-12, 1e-12, "dkv of single-key rows")
+
+
+def pin_bwd_base2_and_selection(lib):
+    """Base-2 lse gives the natural-log result; row and KV-row selections are
+    exactly the matching slices of the full result."""
+    gen, q, kv, idx, dout = _bwd_case(221)
+    out, lse, *_ = _dense_bwd_reference(q, kv, idx, 0.45, 12, dout)
+    dq, dkv, _ = oracle.sparse_mla_bwd(q, kv, out, dout, idx, lse, 0.45, 12, lib=lib)
+    dq2, dkv2, _ = oracle.sparse_mla_bwd(q, kv, out, dout, idx, lse / math.log(2), 0.45, 12,
+                                         lse_base2=True, lib=lib)
+    _close(dq2, dq, 1e-12, 1e-14, "dq, base-2 lse")
+    _close(dkv2, dkv, 1e-12, 1e-14, "dkv, base-2 lse")
+    rows, krows = np.array([5, 0, 2]), np.array([28, 3, 3, 11])
+    dq3, dkv3, _ = oracle.sparse_mla_bwd(q, kv, out, dout, idx, lse, 0.45, 12, rows=rows,
+                                         kv_rows=krows, lib=lib)
+    assert np.array_equal(dq3, dq[rows]) and np.array_equal(dkv3, dkv[krows])
+
+
 ALL_PINS = [
     pin_dense_equals_library_attention,
     pin_sink_equals_extra_key,
@@ -449,4 +566,7 @@ ALL_PINS = [
     pin_nan_in_unreferenced_rows,
     pin_decode_equals_gathered_prefill,
     pin_row_selection,
+    pin_bwd_equals_autograd,
+    pin_bwd_single_key,
+    pin_bwd_base2_and_selection,
 ]

@@ -45,6 +45,22 @@ MUTANTS = [
     ("positions_past_length_used", "for (int32_t j = 0; j < L; ++j)\n                if (is_valid_index(idx[j], s_kv))",
      "for (int32_t j = 0; j < topk; ++j)\n                if (is_valid_index(idx[j], s_kv))"),
     ("softmax_not_shifted", "Z += exp(s[j] - m);", "Z += exp(s[j]);"),
+    ("bwd_delta_dropped", "double ds = p * (dp - delta[h]);", "double ds = p * dp;"),
+    ("bwd_delta_sign", "double ds = p * (dp - delta[h]);", "double ds = p * (dp + delta[h]);"),
+    ("bwd_dq_unscaled", "dqh[d] += sm_scale * ds * bf16_to_double(key[d]);",
+     "dqh[d] += ds * bf16_to_double(key[d]);"),
+    ("bwd_dv_missing", "for (int32_t c = 0; c < d_v; ++c) dkv_row[c] += p * doh[c];", ""),
+    ("bwd_dk_from_key", "dkv_row[d] += sm_scale * ds * bf16_to_double(qh[d]);",
+     "dkv_row[d] += sm_scale * ds * bf16_to_double(key[d]);"),
+    ("bwd_dp_over_q", "dp += doh[c] * bf16_to_double(key[c]);", "dp += doh[c] * bf16_to_double(qh[c]);"),
+    ("bwd_delta_without_out", "dl += dout[rh * d_v + c] * out[rh * d_v + c];",
+     "dl += dout[rh * d_v + c];"),
+    ("bwd_sink_ignored", "if (attn_sink != NULL && !isinf(l)) {", "if (0) {"),
+    ("bwd_base2_inverted", "double l = lse_base2 ? lse * log(2.0) : lse;",
+     "double l = lse_base2 ? lse / log(2.0) : lse;"),
+    ("bwd_d_sink_sign", "d_sink[h] -= exp(", "d_sink[h] += exp("),
+    ("bwd_length_ignored", "for (int32_t j = 0; j < len[i]; ++j)\n                if (is_valid_index(idx[j], s_kv))",
+     "for (int32_t j = 0; j < topk; ++j)\n                if (is_valid_index(idx[j], s_kv))"),
 ]
 
 
