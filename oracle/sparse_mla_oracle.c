@@ -275,8 +275,16 @@ int oracle_sparse_mla_decode_fwd(const uint16_t *q, const uint16_t *kv_cache,
  * nothing.  out and dout come in as doubles (the caller widens bf16 exactly).
  *
  * dq is evaluated for the rows rows_sel lists (all rows when NULL), dkv for
- * the KV rows kv_sel lists (all when NULL), each a sum over the query rows
- * that name it, gathered through a per-KV-row list of (row) occurrences. */
+ * the KV rows kv_sel lists (all when NULL), each a sum over the occurrences
+ * of that KV row in the query rows' key lists. */
+
+/* Orders (KV row, query row) pairs. */
+static int cmp_pair(const void *a, const void *b)
+{
+    const int64_t *x = a, *y = b;
+    if (x[0] != y[0]) return x[0] < y[0] ? -1 : 1;
+    return x[1] < y[1] ? -1 : (x[1] > y[1]);
+}
 
 /* lse' of (row, head), see above. */
 static double effective_lse(double lse, int lse_base2, const float *attn_sink, int32_t h)
@@ -298,10 +306,10 @@ static void key_grad(const uint16_t *q_row, const uint16_t *key, const double *d
 {
     for (int32_t h = 0; h < h_q; ++h) {
         if (isinf(lse_eff[h])) continue;
-        const uint16_t *qh = q_row + (int64_t)h * d_qk;
+        const uint16_t *qhd = q_row + (int64_t)h * d_qk;
         const double *doh = dout_row + (int64_t)h * d_v;
         double acc = 0.0;
-        for (int32_t d = 0; d < d_qk; ++d) acc += bf16_to_double(qh[d]) * bf16_to_double(key[d]);
+        for (int32_t d = 0; d < d_qk; ++d) acc += bf16_to_double(qhd[d]) * bf16_to_double(key[d]);
         double p = exp(sm_scale * acc - lse_eff[h]);
         double dp = 0.0;
         for (int32_t c = 0; c < d_v; ++c) dp += doh[c] * bf16_to_double(key[c]);
@@ -311,7 +319,7 @@ static void key_grad(const uint16_t *q_row, const uint16_t *key, const double *d
             for (int32_t d = 0; d < d_qk; ++d) dqh[d] += sm_scale * ds * bf16_to_double(key[d]);
         }
         if (dkv_row != NULL) {
-            for (int32_t d = 0; d < d_qk; ++d) dkv_row[d] += sm_scale * ds * bf16_to_double(qh[d]);
+            for (int32_t d = 0; d < d_qk; ++d) dkv_row[d] += sm_scale * ds * bf16_to_double(qhd[d]);
             for (int32_t c = 0; c < d_v; ++c) dkv_row[c] += p * doh[c];
         }
     }
@@ -372,25 +380,25 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const double *o
     }
 
     if (dkv != NULL && !bad) {
-        /* Occurrence lists: first[k] .. first[k + 1] - 1 in `who` are the query
-         * rows naming KV row k, in row then position order. */
-        int64_t *first = calloc((size_t)s_kv + 1, sizeof(int64_t));
-        if (!first) bad = 1;
+        /* Occurrences as (KV row, query row) pairs sorted by KV row then query
+         * row; the pairs of KV row k are found by binary search. */
+        int64_t total = 0;
+        for (int64_t i = 0; i < s_q; ++i)
+            for (int32_t j = 0; j < len[i]; ++j)
+                if (is_valid_index(indices[i * topk + j], s_kv)) ++total;
+        int64_t *pairs = malloc(sizeof(int64_t) * 2 * (size_t)(total > 0 ? total : 1));
+        if (!pairs) bad = 1;
+        int64_t np = 0;
         for (int64_t i = 0; !bad && i < s_q; ++i)
             for (int32_t j = 0; j < len[i]; ++j) {
                 int32_t k = indices[i * topk + j];
-                if (is_valid_index(k, s_kv)) first[k + 1]++;
+                if (is_valid_index(k, s_kv)) {
+                    pairs[2 * np] = k;
+                    pairs[2 * np + 1] = i;
+                    ++np;
+                }
             }
-        for (int64_t k = 0; !bad && k < s_kv; ++k) first[k + 1] += first[k];
-        int64_t total = bad ? 0 : first[s_kv];
-        int64_t *who = malloc(sizeof(int64_t) * (size_t)(total > 0 ? total : 1));
-        int64_t *fill = calloc((size_t)s_kv + 1, sizeof(int64_t));
-        if (!who || !fill) bad = 1;
-        for (int64_t i = 0; !bad && i < s_q; ++i)
-            for (int32_t j = 0; j < len[i]; ++j) {
-                int32_t k = indices[i * topk + j];
-                if (is_valid_index(k, s_kv)) who[first[k] + fill[k]++] = i;
-            }
+        if (!bad) qsort(pairs, (size_t)np, 2 * sizeof(int64_t), cmp_pair);
         if (!bad) {
 #pragma omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(| : bad)
             for (int64_t n = 0; n < n_kv_sel; ++n) {
@@ -398,17 +406,20 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const double *o
                 double *dkv_row = dkv + n * (int64_t)d_qk;
                 for (int32_t d = 0; d < d_qk; ++d) dkv_row[d] = 0.0;
                 if (k < 0 || k >= s_kv) { bad = 1; continue; }
-                for (int64_t e = first[k]; e < first[k + 1]; ++e) {
-                    int64_t i = who[e];
+                int64_t lo = 0, hi = np;  /* first pair with KV row >= k */
+                while (lo < hi) {
+                    int64_t mid = lo + (hi - lo) / 2;
+                    if (pairs[2 * mid] < k) lo = mid + 1; else hi = mid;
+                }
+                for (int64_t e = lo; e < np && pairs[2 * e] == k; ++e) {
+                    int64_t i = pairs[2 * e + 1];
                     key_grad(q + i * (int64_t)h_q * d_qk, kv + k * (int64_t)d_qk,
                              dout + i * (int64_t)h_q * d_v, lse_eff + i * h_q, delta + i * h_q,
                              h_q, d_qk, d_v, sm_scale, NULL, dkv_row);
                 }
             }
         }
-        free(first);
-        free(who);
-        free(fill);
+        free(pairs);
     }
 
     if (d_sink != NULL && !bad) {

@@ -50,9 +50,9 @@ MUTANTS = [
     ("bwd_dq_unscaled", "dqh[d] += sm_scale * ds * bf16_to_double(key[d]);",
      "dqh[d] += ds * bf16_to_double(key[d]);"),
     ("bwd_dv_missing", "for (int32_t c = 0; c < d_v; ++c) dkv_row[c] += p * doh[c];", ""),
-    ("bwd_dk_from_key", "dkv_row[d] += sm_scale * ds * bf16_to_double(qh[d]);",
+    ("bwd_dk_from_key", "dkv_row[d] += sm_scale * ds * bf16_to_double(qhd[d]);",
      "dkv_row[d] += sm_scale * ds * bf16_to_double(key[d]);"),
-    ("bwd_dp_over_q", "dp += doh[c] * bf16_to_double(key[c]);", "dp += doh[c] * bf16_to_double(qh[c]);"),
+    ("bwd_dp_over_q", "dp += doh[c] * bf16_to_double(key[c]);", "dp += doh[c] * bf16_to_double(qhd[c]);"),
     ("bwd_delta_without_out", "dl += dout[rh * d_v + c] * out[rh * d_v + c];",
      "dl += dout[rh * d_v + c];"),
     ("bwd_sink_ignored", "if (attn_sink != NULL && !isinf(l)) {", "if (0) {"),
