@@ -164,6 +164,49 @@ smla_status sparse_mla_row_lengths(const int32_t *indices, const int32_t *topk_l
                                    int32_t max_blocks_per_seq, int32_t *row_len,
                                    smla_stream_t stream);
 
+/*
+ * Backward of the prefill operation (FlashMLA PR #198, "Summary", item 1:
+ * sparse MLA backward from the forward's saved out and lse; key and value
+ * gradients scattered into an fp32 accumulator with atomic adds).  Per query
+ * row i, head h and key occurrence j (the forward's keys: valid entries
+ * before the row length):
+ *   p = exp(s_j - lse'),  ds = sm_scale p (dout_h . v_j - dout_h . out_h)
+ *   dq[i][h]   = sum_j ds k_j
+ *   dkv[idx_j] += ds q_h (all d_qk columns) + p dout_h (the d_v value columns)
+ * lse' is the row's softmax normaliser: lse itself (natural log, as the
+ * forward returns it; lse_base2 = 1 takes it in base 2, the pages' backward
+ * contract), combined with attn_sink[h] when a sink is given (the forward's
+ * lse leaves the sink out).
+ *   q             bf16 [s_q, h_q, d_qk]
+ *   kv            bf16 [s_kv, 1, d_qk]
+ *   out, dout     bf16 [s_q, h_q, d_v]   forward output and its gradient
+ *   indices       int32 [s_q, 1, topk]; topk_length int32 [s_q] or NULL
+ *                 (same meaning as in sparse_mla_fwd)
+ *   lse           fp32 [s_q, h_q]        forward lse (+inf: row without keys)
+ *   attn_sink     fp32 [h_q] or NULL     the sink the forward used
+ *   lse_base2     0: natural-log lse, 1: base-2 lse
+ *   workspace     device memory of sparse_mla_bwd_workspace_bytes(s_q, s_kv,
+ *                 d_qk) bytes, 16-byte aligned (the fp32 dkv accumulator and
+ *                 the row lengths); no initialisation needed, garbage after;
+ *                 calls that overlap on one workspace race
+ *   dq            bf16 [s_q, h_q, d_qk]  (output)
+ *   dkv           bf16 [s_kv, 1, d_qk]   (output; rows no query names are 0)
+ *   d_sink        fp32 [h_q] or NULL     (output, needs attn_sink):
+ *                 -sum_i exp(sink[h] - lse'_ih) (dout_ih . out_ih)
+ * Supported: h_q = 64, h_kv = 1, d_qk 512 or 576, d_v = 512.  The dkv sums
+ * are accumulated in a run-dependent order (fp32 atomics).  Four kernels are
+ * enqueued on `stream` (zero fill, row lengths, backward, dkv conversion).
+ */
+size_t sparse_mla_bwd_workspace_bytes(int32_t s_q, int32_t s_kv, int32_t d_qk);
+
+smla_status sparse_mla_bwd(const void *q, const void *kv, const void *out, const void *dout,
+                           const int32_t *indices, const int32_t *topk_length, const float *lse,
+                           const float *attn_sink, int32_t s_q, int32_t s_kv, int32_t h_q,
+                           int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+                           float sm_scale, int32_t lse_base2, void *workspace,
+                           size_t workspace_bytes, void *dq, void *dkv, float *d_sink,
+                           smla_stream_t stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *sparse_mla_last_error(void);
 

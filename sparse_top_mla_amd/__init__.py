@@ -1,12 +1,14 @@
-"""Sparse top-k MLA attention forward (prefill and paged decode) for MI355X.
+"""Sparse top-k MLA attention (prefill and paged decode forward, prefill
+backward) for MI355X.
 
 The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
 of include/sparse_mla.h (libsparse_mla.so); this package only binds it.
 """
-from ._binding import (EXPORTS, SparseMLAError, decode_fwd, decode_fwd_split,  # noqa: F401
+from ._binding import (EXPORTS, SparseMLAError, bwd, bwd_workspace_bytes,  # noqa: F401
+                       decode_fwd, decode_fwd_split,
                        decode_num_splits, decode_split_workspace_bytes, fwd, load_library,
                        row_lengths)
 
-__all__ = ["fwd", "decode_fwd", "decode_fwd_split", "decode_num_splits",
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode_fwd", "decode_fwd_split", "decode_num_splits",
            "decode_split_workspace_bytes", "row_lengths",
            "load_library", "SparseMLAError", "EXPORTS"]

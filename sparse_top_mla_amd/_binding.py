@@ -19,7 +19,8 @@ _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL_ARG", 2: "SMLA_ERR_BAD_SHAPE", 3: "SM
            4: "SMLA_ERR_LAUNCH"}
 
 EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_decode_split_workspace_bytes",
-           "sparse_mla_decode_fwd_split", "sparse_mla_row_lengths", "sparse_mla_last_error")
+           "sparse_mla_decode_fwd_split", "sparse_mla_row_lengths", "sparse_mla_bwd_workspace_bytes",
+           "sparse_mla_bwd", "sparse_mla_last_error")
 
 _lib = None
 
@@ -59,6 +60,11 @@ def _declare(lib):
     lib.sparse_mla_decode_fwd_split.restype = ctypes.c_int
     lib.sparse_mla_row_lengths.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.sparse_mla_row_lengths.restype = ctypes.c_int
+    lib.sparse_mla_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sparse_mla_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.sparse_mla_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                   f32, i32, vp, ctypes.c_size_t, vp, vp, vp, vp]
+    lib.sparse_mla_bwd.restype = ctypes.c_int
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
     return lib
@@ -254,3 +260,60 @@ def row_lengths(indices, topk_length=None, cache_seqlens=None, *, s_kv=0, rows_p
                                     _stream(dev, stream))
     _check(lib, st)
     return out
+
+
+def bwd_workspace_bytes(s_q, s_kv, d_qk):
+    """Workspace bytes sparse_mla_bwd needs."""
+    return int(load_library().sparse_mla_bwd_workspace_bytes(s_q, s_kv, d_qk))
+
+
+def bwd(q, kv, out, dout, indices, lse, sm_scale, d_v=512, attn_sink=None, topk_length=None, *,
+        lse_base2=False, want_d_sink=False, workspace=None, dq=None, dkv=None, stream=None):
+    """Sparse prefill backward.  q [s_q, h_q, d_qk], kv [s_kv, 1, d_qk],
+    out / dout [s_q, h_q, d_v] bf16; indices [s_q, 1, topk] int32; lse
+    [s_q, h_q] fp32 (the forward's); attn_sink [h_q] fp32 or None.  Returns
+    (dq, dkv, d_sink or None)."""
+    lib = load_library()
+    dev = q.device
+    _dev(q, "q", torch.bfloat16)
+    _dev(kv, "kv", torch.bfloat16, dev)
+    _dev(out, "out", torch.bfloat16, dev)
+    _dev(dout, "dout", torch.bfloat16, dev)
+    _dev(indices, "indices", torch.int32, dev)
+    _dev(lse, "lse", torch.float32, dev)
+    _dev(topk_length, "topk_length", torch.int32, dev)
+    _dev(attn_sink, "attn_sink", torch.float32, dev)
+    if q.dim() != 3 or kv.dim() != 3 or indices.dim() != 3:
+        raise ValueError("q, kv and indices must be 3-d")
+    s_q, h_q, d_qk = q.shape
+    s_kv, h_kv = kv.shape[0], kv.shape[1]
+    topk = indices.shape[-1]
+    if kv.shape[2] != d_qk or indices.shape[0] != s_q or indices.shape[1] != h_kv:
+        raise ValueError("inconsistent shapes of q, kv and indices")
+    if tuple(out.shape) != (s_q, h_q, d_v) or tuple(dout.shape) != (s_q, h_q, d_v):
+        raise ValueError("out and dout must have shape [s_q, h_q, d_v]")
+    if tuple(lse.shape) != (s_q, h_q):
+        raise ValueError("lse must have shape [s_q, h_q]")
+    if topk_length is not None and tuple(topk_length.shape) != (s_q,):
+        raise ValueError("topk_length must have shape [s_q]")
+    if attn_sink is not None and tuple(attn_sink.shape) != (h_q,):
+        raise ValueError("attn_sink must have shape [h_q]")
+    if want_d_sink and attn_sink is None:
+        raise ValueError("d_sink needs attn_sink")
+    nbytes = int(lib.sparse_mla_bwd_workspace_bytes(s_q, s_kv, d_qk))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dkv = torch.empty_like(kv) if dkv is None else dkv
+    _dev(dq, "dq", torch.bfloat16, dev)
+    _dev(dkv, "dkv", torch.bfloat16, dev)
+    if dq.numel() != q.numel() or dkv.numel() != kv.numel():
+        raise ValueError("output buffers have the wrong size")
+    d_sink = torch.empty(h_q, dtype=torch.float32, device=dev) if want_d_sink else None
+    st = lib.sparse_mla_bwd(_p(q), _p(kv), _p(out), _p(dout), _p(indices), _p(topk_length),
+                            _p(lse), _p(attn_sink), s_q, s_kv, h_q, h_kv, d_qk, d_v, topk,
+                            float(sm_scale), int(bool(lse_base2)), _p(workspace),
+                            workspace.numel(), _p(dq), _p(dkv), _p(d_sink), _stream(dev, stream))
+    _check(lib, st)
+    return dq, dkv, d_sink

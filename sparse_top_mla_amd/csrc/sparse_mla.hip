@@ -1720,3 +1720,10 @@ extern "C" smla_status sparse_mla_row_lengths(const int32_t* indices, const int3
 }
 
 extern "C" const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }
+
+// Error reporting for the library's other translation units (the backward).
+__attribute__((visibility("hidden"))) smla_status smla_report(smla_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+__attribute__((visibility("hidden"))) void smla_clear_error() { g_last_error.clear(); }

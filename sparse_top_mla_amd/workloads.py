@@ -243,6 +243,40 @@ def prefill_h128(seed=0, s_q=4096, s_kv=4096, topk=2048):
                         empty_frac=0.01, with_sink=True, seed=seed)
 
 
+def bwd_h64(seed=0, s_q=4096, s_kv=4096, topk=2048, d_qk=576):
+    """Backward shape of the pages: T = s_q = s_kv = 4096, h_q = 64,
+    d_qk = 576, d_v = 512, topk = 2048; row i holds min(i + 1, 2048) distinct
+    causal keys in random order, then -1 (causal top-k selection)."""
+    return make_prefill(f"bwd_h64_d{d_qk}_T{s_q}_topk{topk}", s_q=s_q, s_kv=s_kv, h_q=64,
+                        d_qk=d_qk, d_v=512, topk=topk, layout="ramp", ramp_cap=topk, seed=seed,
+                        with_length=True)
+
+
+def bwd_dout(case, seed):
+    """Seeded gradient of the forward output: bf16 [s_q, h_q, d_v], N(0, 1)."""
+    gen = torch.Generator().manual_seed(seed)
+    return _randn_bf16((case.s_q, case.h_q, case.d_v), gen)
+
+
+def bwd_synthetic_stats(case, seed):
+    """Seeded stand-ins for the forward's out and lse when the forward itself
+    is too costly to evaluate on the CPU: lse = ln(keys of the row) + 1/2 + a
+    little noise (the size of the normaliser for unit-variance logits), out =
+    N(0, 1) / sqrt(keys), bf16 (the size of a softmax average of unit values).
+    Rows without keys get lse = +inf and out = 0."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = case.topk_length.to(torch.float64) if case.topk_length is not None else None
+    if lens is None:
+        raise ValueError("case needs explicit row lengths")
+    n = torch.clamp(lens, min=1.0)
+    lse = (torch.log(n) + 0.5)[:, None] + 0.1 * torch.randn(case.s_q, case.h_q, generator=gen,
+                                                              dtype=torch.float64)
+    lse = torch.where((lens > 0)[:, None], lse, torch.full_like(lse, math.inf))
+    out = _randn_bf16((case.s_q, case.h_q, case.d_v), gen).to(torch.float32)
+    out = (out / torch.sqrt(n).to(torch.float32)[:, None, None]) * (lens > 0).to(torch.float32)[:, None, None]
+    return out.to(torch.bfloat16), lse.to(torch.float32)
+
+
 # ---------------------------------------------------------------------------
 # decode cases
 # ---------------------------------------------------------------------------

@@ -26,7 +26,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["sparse_mla_decode_fwd", "sparse_mla_decode_fwd_split",
+    assert _declared_functions() == ["sparse_mla_bwd", "sparse_mla_bwd_workspace_bytes",
+                                     "sparse_mla_decode_fwd", "sparse_mla_decode_fwd_split",
                                      "sparse_mla_decode_split_workspace_bytes", "sparse_mla_fwd",
                                      "sparse_mla_last_error", "sparse_mla_row_lengths"]
 
@@ -134,6 +135,39 @@ def test_split_decode_rejects(lib, kw, status):
 
 def test_split_decode_empty_batch_is_noop(lib):
     assert _split(lib, B=0, workspace=NULL, workspace_bytes=0) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(q=P, kv=P, out=P, dout=P, indices=P, topk_length=NULL, lse=P, attn_sink=NULL,
+             s_q=8, s_kv=64, h_q=64, h_kv=1, d_qk=576, d_v=512, topk=32, sm_scale=0.1,
+             lse_base2=0, workspace=P, workspace_bytes=1 << 30, dq=P, dkv=P, d_sink=NULL,
+             stream=NULL)
+    a.update(kw)
+    return lib.sparse_mla_bwd(*a.values())
+
+
+def test_bwd_workspace_bytes(lib):
+    f = lib.sparse_mla_bwd_workspace_bytes
+    assert f(8, 64, 576) == 64 * 576 * 4 + 256
+    assert f(300, 1, 512) == 2048 + 1280
+    assert f(0, 0, 576) == 0 and f(-1, 4, 576) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_q=32), 3), (dict(h_q=128), 3), (dict(d_qk=320), 3), (dict(d_v=256), 3),
+    (dict(h_kv=2), 3), (dict(sm_scale=0.0), 3), (dict(sm_scale=float("nan")), 3),
+    (dict(topk=0), 2), (dict(s_q=-1), 2), (dict(s_kv=-5), 2), (dict(lse_base2=2), 2),
+    (dict(d_sink=P), 1), (dict(workspace=NULL), 1),
+    (dict(workspace_bytes=64 * 576 * 4 + 255), 2), (dict(workspace=ctypes.c_void_p(24)), 2),
+    (dict(q=NULL), 1), (dict(lse=NULL), 1), (dict(dkv=NULL), 1), (dict(dq=NULL), 1),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+    assert lib.sparse_mla_last_error().decode()
+
+
+def test_bwd_empty_is_noop(lib):
+    assert _bwd(lib, s_q=0, s_kv=0, workspace=NULL, workspace_bytes=0) == 0
 
 
 def test_row_lengths_rejects(lib):
