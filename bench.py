@@ -31,6 +31,7 @@ import numpy as np
 ROOT = Path(__file__).resolve().parent
 PROFILES = ROOT / "profiles"
 METRIC = "sparse MLA fwd ms/call + TFLOP/s over valid keys; % MFMA / HBM peak"
+METRIC_BWD = "sparse MLA bwd ms/call + TFLOP/s over valid keys; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -42,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_h64",
                     choices=["prefill_h64", "prefill_h64_len", "prefill_h128", "decode_dynamic",
-                             "decode_dynamic_nolen", "decode_fixed", "decode_fixed_b2", "tiny"])
+                             "decode_dynamic_nolen", "decode_fixed", "decode_fixed_b2", "tiny",
+                             "bwd_h64"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -83,6 +85,9 @@ def make_case(name):
         return W.decode_fixed(batch=2)
     if name == "tiny":
         return W.tiny_prefill()
+    if name == "bwd_h64":
+        # the pages' backward shape: T = 4096, topk = 2048, h_q = 64, d_qk = 576
+        return W.bwd_h64()
     raise ValueError(name)
 
 
@@ -140,9 +145,48 @@ def algorithmic_counts(case):
                 rows=rows, valid_per_row=ok.sum(axis=1))
 
 
+def bwd_counts(case):
+    """Backward FLOPs over valid keys (S = QK^T, dP = dO V^T, dQ = dS K,
+    dK = dS^T Q, dV = P^T dO: 2 h_q (3 d_qk + 2 d_v) per valid pair) and the
+    minimum HBM bytes of one call: q, out, dout, lse, the index vectors and
+    lengths read once, every named KV row read once, dq and the whole dkv
+    written once."""
+    c = algorithmic_counts(case)
+    h_q, d_qk, d_v, rows = case.h_q, case.d_qk, case.d_v, c["rows"]
+    c["flops"] = 2.0 * h_q * (3 * d_qk + 2 * d_v) * c["valid_pairs"]
+    c["bytes"] = float(rows * h_q * d_qk * 2 + c["kv_rows"] * d_qk * 2 + case.indices.numel() * 4
+                       + (rows * 4 if case.topk_length is not None else 0)
+                       + 2 * rows * h_q * d_v * 2 + rows * h_q * 4
+                       + rows * h_q * d_qk * 2 + case.s_kv * d_qk * 2)
+    return c
+
+
 # ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
+
+def gpu_call_bwd(case, dev):
+    """One backward call with every input resident on `dev`: out and lse come
+    from the library's forward on the same inputs (run once, untimed), dout
+    is seeded; workspace and outputs are allocated here, outside the call."""
+    import torch
+    import sparse_top_mla_amd as smla
+    from sparse_top_mla_amd import workloads as W
+    t = lambda x: None if x is None else x.to(dev)  # noqa: E731
+    q, kv, idx = t(case.q), t(case.kv), t(case.indices)
+    sink, tl = t(case.attn_sink), t(case.topk_length)
+    out, lse, _ = smla.fwd(q, kv, idx, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl)
+    dout = t(W.bwd_dout(case, seed=8))
+    ws = torch.empty(smla.bwd_workspace_bytes(case.s_q, case.s_kv, case.d_qk), dtype=torch.uint8,
+                     device=dev)
+    dq, dkv = torch.empty_like(q), torch.empty_like(kv)
+    torch.cuda.synchronize()
+
+    def call():
+        smla.bwd(q, kv, out, dout, idx, lse, case.sm_scale, case.d_v, attn_sink=sink,
+                 topk_length=tl, workspace=ws, dq=dq, dkv=dkv)
+    return call
+
 
 def gpu_call(case, dev, num_splits=1):
     """One call of the workload on `dev` with its inputs resident there;
@@ -255,6 +299,43 @@ def cpu_baseline(case, counts, target_s):
             "sample": f"{sel.size} of {rows} rows, evenly spaced ({flops / counts['flops']:.2%} of "
                       f"the valid-key FLOPs), {t:.1f} s, fp64 C oracle",
             "seconds": t, "ms_per_call_extrapolated": float(t * counts["flops"] / flops * 1e3)}
+
+
+def cpu_baseline_bwd(case, counts, target_s):
+    """The backward oracle's dq (S, dP and dQ of each pair: 2 h_q (2 d_qk +
+    d_v) FLOPs) on an evenly spaced row sample, with seeded stand-ins for out
+    and lse."""
+    import oracle
+    from sparse_top_mla_amd import workloads as W
+    rows = counts["rows"]
+    per_row = counts["valid_per_row"]
+    threads = host_threads()
+    dout = W.bwd_dout(case, seed=8)
+    out, lse = W.bwd_synthetic_stats(case, seed=9)
+    pair_flops = 2.0 * case.h_q * (2 * case.d_qk + case.d_v)
+
+    def run(sel):
+        t0 = time.perf_counter()
+        oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse, case.sm_scale,
+                              case.d_v, attn_sink=case.attn_sink, topk_length=case.topk_length,
+                              rows=sel, want_dkv=False, threads=threads)
+        return time.perf_counter() - t0
+
+    def sample(n):
+        n = max(1, min(rows, n))
+        return np.unique(np.linspace(0, rows - 1, n).round().astype(np.int64))
+
+    probe = sample(2 * threads)
+    t = run(probe)
+    rate = pair_flops * per_row[probe].sum() / max(t, 1e-9)
+    n = int(target_s * rate / max(pair_flops * per_row.mean(), 1.0))
+    sel = sample(n)
+    t = run(sel)
+    flops = pair_flops * per_row[sel].sum()
+    return {"value": float(flops / t / 1e12), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"dq of {sel.size} of {rows} rows, evenly spaced (S, dP, dQ FLOPs), "
+                      f"{t:.1f} s, fp64 C oracle",
+            "seconds": t}
 
 
 # ---------------------------------------------------------------------------
@@ -466,8 +547,9 @@ def main():
     torch.cuda.set_device(dev)
 
     case = make_case(args.workload)
-    counts = algorithmic_counts(case)
-    call = gpu_call(case, dev)
+    bwd = args.workload == "bwd_h64"
+    counts = bwd_counts(case) if bwd else algorithmic_counts(case)
+    call = gpu_call_bwd(case, dev) if bwd else gpu_call(case, dev)
     call()
     torch.cuda.synchronize()
     ms_per_step, per = time_steps(call, args.steps, args.warmup)
@@ -514,7 +596,7 @@ def main():
         del call_len, case_len
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -554,7 +636,9 @@ def main():
         att = p["hbm_gbs"] if is_decode(case) else p["mfma_tflops"]
         result["attainable"] = {"mfma_tflops": p["mfma_tflops"], "hbm_gbs": p["hbm_gbs"],
                                 "frac_of_attainable": result["roofline"]["achieved"] / att}
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and bwd:
+        result["cpu_baseline"] = cpu_baseline_bwd(case, counts, args.cpu_seconds)
+    elif args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(case, counts, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None

@@ -23,11 +23,13 @@
 //   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_16x16x32_bf16 (each lane owns
 //   one head, so lse' and delta are per-lane scalars);
 //   P and dS in registers; dS^T and P^T also go to LDS as bf16;
-//   dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16 and dS^T taken from
-//   the registers (the key order of both operands is permuted alike);
 //   dKV[32 keys x d_qk] = dS^T Q (+ P^T dO on the value columns), the d_qk
 //   columns split over the four waves, contracted over all 64 heads, then
-//   added to the fp32 accumulator with global_atomic_add_f32.
+//   added to the fp32 accumulator with global_atomic_add_f32;
+//   dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16 and dS^T taken from
+//   the registers (the key order of both operands is permuted alike).
+// The atomic adds bound the kernel: one fp32 add per valid (row, key) pair
+// and d_qk column.
 // The query rows stay in LDS for the whole row; dO stays in registers (its
 // B-operand fragments for both products).
 
@@ -268,11 +270,6 @@ sparse_mla_bwd_kernel(BwdArgs a) {
         *reinterpret_cast<LDS_AS __bf16*>(pst + key * T::kSRow + head * 2) = (__bf16)p;
       }
 
-    // dQ^T += K^T dS^T: element e of both operands is key 16 (e / 4) + 4g + e % 4.
-#pragma unroll
-    for (int ct = 0; ct < T::kTiles; ++ct)
-      dqa[ct] = mfma(tr_pair(ks, T::kRow, 0, ct * 16, g, hl), dsf, dqa[ct]);
-
     __syncthreads();  // dS^T and P^T of every wave are in LDS
 
     // dKV of this wave's columns: element e of both operands is head
@@ -304,6 +301,13 @@ sparse_mla_bwd_kernel(BwdArgs a) {
         }
       }
     }
+
+    // dQ^T += K^T dS^T, after the atomic adds so that they drain behind it
+    // (the next block's loads wait for them): element e of both operands is
+    // key 16 (e / 4) + 4g + e % 4.
+#pragma unroll
+    for (int ct = 0; ct < T::kTiles; ++ct)
+      dqa[ct] = mfma(tr_pair(ks, T::kRow, 0, ct * 16, g, hl), dsf, dqa[ct]);
   }
 
   // dq[row][head][16 ct + 4g + r] = dqa[ct][r].
