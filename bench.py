@@ -342,13 +342,23 @@ def cpu_baseline_bwd(case, counts, target_s):
 # roofline
 # ---------------------------------------------------------------------------
 
-def kernel_source_digest():
+def kernel_file(workload):
+    """Source file of the workload's dominant kernel."""
+    return "sparse_mla_bwd.hip" if workload == "bwd_h64" else "sparse_mla.hip"
+
+
+def kernel_name(workload):
+    """Name fragment of the workload's dominant kernel in rocprofv3 records."""
+    return "sparse_mla_bwd_kernel" if workload == "bwd_h64" else "sparse_mla_fwd"
+
+
+def kernel_source_digest(workload=None):
     """Digest of the device code (the source above its host-side section)
     without comments and blank lines, so that stored counter figures stay
     attached to the kernels they were taken on; host-side validation and
     dispatch changes do not touch them."""
     import re
-    src = (ROOT / "sparse_top_mla_amd" / "csrc" / "sparse_mla.hip").read_text()
+    src = (ROOT / "sparse_top_mla_amd" / "csrc" / kernel_file(workload)).read_text()
     cut = src.find("\n// host side\n")
     if cut >= 0:
         src = src[:cut]
@@ -365,7 +375,7 @@ def stored_counters(workload):
     if not f.exists():
         return None
     rec = json.loads(f.read_text())
-    if rec.get("kernel_source_sha256_16") != kernel_source_digest():
+    if rec.get("kernel_source_sha256_16") != kernel_source_digest(workload):
         return None
     return rec
 
@@ -413,13 +423,13 @@ def ingest_counters(d):
         if not v:
             raise SystemExit(f"no copy kernel in pmc_copy_{c}")
         cal[c] = (1 << 30) / (statistics.fmean(v) * 1024.0)
-    digest = kernel_source_digest()
     for sub in sorted(d.glob("pmc_*_FETCH_SIZE")):
         w = sub.name[len("pmc_"):-len("_FETCH_SIZE")]
         if w == "copy":
             continue
-        f = _counter_values(sub / "run_counter_collection.csv", "sparse_mla_fwd")
-        wr = _counter_values(d / f"pmc_{w}_WRITE_SIZE" / "run_counter_collection.csv", "sparse_mla_fwd")
+        digest = kernel_source_digest(w)
+        f = _counter_values(sub / "run_counter_collection.csv", kernel_name(w))
+        wr = _counter_values(d / f"pmc_{w}_WRITE_SIZE" / "run_counter_collection.csv", kernel_name(w))
         if not f or not wr:
             continue
         fetch = statistics.fmean(f) * 1024.0 * cal["FETCH_SIZE"]
@@ -433,7 +443,7 @@ def ingest_counters(d):
                           f"python3 -u bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0; "
                           f"calibration: ... -- python3 -u bench.py --calibrate-copy",
                "kernel_source_sha256_16": digest}
-        busy = _mfma_busy(d / f"pmc_{w}_MFMA")
+        busy = _mfma_busy(d / f"pmc_{w}_MFMA", kernel_name(w))
         if busy is not None:
             rec.update(busy)
         PROFILES.mkdir(exist_ok=True)
@@ -442,7 +452,7 @@ def ingest_counters(d):
               f"(fetch {fetch / 1e6:.1f}, write {write / 1e6:.1f})")
 
 
-def _mfma_busy(sub):
+def _mfma_busy(sub, kernel):
     """MFMA-busy fraction of the attention kernel from one rocprofv3 run with
     SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.  The SQ counter sums busy
     cycles over every SIMD; GRBM_GUI_ACTIVE sums the active cycles of every
@@ -460,7 +470,7 @@ def _mfma_busy(sub):
                 simd, xcc = int(r["Simd_Count"]), int(r["Num_Xcc"])
     vals = {}
     with open(f) as fh:
-        rows = [r for r in csv.DictReader(fh) if "sparse_mla_fwd" in r["Kernel_Name"]]
+        rows = [r for r in csv.DictReader(fh) if kernel in r["Kernel_Name"]]
     if not rows or not simd:
         return None
     name = rows[0]["Kernel_Name"]

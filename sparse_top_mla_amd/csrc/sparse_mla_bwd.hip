@@ -336,6 +336,8 @@ __global__ void __launch_bounds__(256) bwd_convert_kernel(const float* acc, __bf
   }
 }
 
+// host side
+
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 smla_status bwd_fail(smla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
