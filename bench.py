@@ -452,7 +452,7 @@ def ingest_counters(d):
               f"(fetch {fetch / 1e6:.1f}, write {write / 1e6:.1f})")
 
 
-def _mfma_busy(sub, kernel):
+def _mfma_busy(sub, kernel="sparse_mla_fwd"):
     """MFMA-busy fraction of the attention kernel from one rocprofv3 run with
     SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.  The SQ counter sums busy
     cycles over every SIMD; GRBM_GUI_ACTIVE sums the active cycles of every
