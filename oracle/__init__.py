@@ -12,6 +12,8 @@ Parity status per function (what pins it is listed in tests/oracle_pins.py):
                        force, closed forms, sink closed form)
   sparse_mla_decode_fwd pinned (paged == prefill on a numpy-gathered cache,
                        dense library attention on contiguous pages)
+  block_sparse_fwd     pinned (torch SDPA for full causal / full selections,
+                       numpy dense-mask brute force, empty rows)
   sparse_mla_bwd       pinned (float64 autograd of dense attention with the
                        multiplicity bias, with and without a sink column;
                        single-key closed form; base-2 lse; selections)
@@ -55,6 +57,9 @@ def _bind(lib):
                                           i32, dbl, ctypes.c_int, vp, i64, vp, i64, vp, vp, vp,
                                           ctypes.c_int]
     lib.oracle_sparse_mla_bwd.restype = ctypes.c_int
+    lib.oracle_block_sparse_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_int, dbl, vp, i64, vp, vp, ctypes.c_int]
+    lib.oracle_block_sparse_fwd.restype = ctypes.c_int
     return lib
 
 
@@ -226,3 +231,30 @@ def _f64_array(x):
     except ImportError:  # pragma: no cover
         pass
     return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def block_sparse_fwd(q, k, v, q2k_row_ptr, q2k_col_idx, q_block, k_block, sm_scale, causal=True,
+                     rows=None, threads=None, lib=None):
+    """Block-sparse forward oracle.  q [s, h_q, d_qk], k [s, h_kv, d_qk],
+    v [s, h_kv, d_v] bf16; q2k_row_ptr [ceil(s / q_block) + 1], q2k_col_idx
+    [nnz] int32.  Returns (out [n, h_q, d_v] f64, lse [n, h_q] f64) for the
+    selected rows (all when None)."""
+    lib = lib or load()
+    qn, kn, vn = _np(q, np.uint16), _np(k, np.uint16), _np(v, np.uint16)
+    s, h_q, d_qk = qn.shape
+    h_kv, d_v = kn.shape[1], vn.shape[2]
+    rp = _np(q2k_row_ptr, np.int32)
+    ci = _np(q2k_col_idx, np.int32)
+    if ci.size == 0:
+        ci = np.zeros(1, dtype=np.int32)
+    sel = None if rows is None else _np(rows, np.int64)
+    n = s if sel is None else sel.size
+    out = np.empty((n, h_q, d_v))
+    lse = np.empty((n, h_q))
+    rc = lib.oracle_block_sparse_fwd(_ptr(qn), _ptr(kn), _ptr(vn), _ptr(rp), _ptr(ci), s, h_q, h_kv,
+                                     d_qk, d_v, int(q_block), int(k_block), int(bool(causal)),
+                                     float(sm_scale), _ptr(sel), n, _ptr(out), _ptr(lse),
+                                     _threads(threads))
+    if rc:
+        raise ValueError(f"oracle_block_sparse_fwd failed ({rc})")
+    return out, lse

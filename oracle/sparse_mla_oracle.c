@@ -436,3 +436,89 @@ int oracle_sparse_mla_bwd(const uint16_t *q, const uint16_t *kv, const double *o
     free(delta);
     return bad ? 3 : 0;
 }
+
+/* Block-sparse attention forward, non-absorbed MLA shape (FlashMLA PR #198,
+ * "Summary", item 3: each query block attends only the key blocks it
+ * selects; "Benchmarks": 192/128 heads).  One sequence of s tokens;
+ * q [s][h_q][d_qk], k [s][h_kv][d_qk], v [s][h_kv][d_v] bf16; query head h
+ * reads KV head h / (h_q / h_kv).  The selection of query block
+ * qb = i / q_block is the list q2k_col_idx[q2k_row_ptr[qb] .. q2k_row_ptr[qb + 1]).
+ *
+ * Keys of row i (readings): every listed block b with 0 <= b < ceil(s / k_block)
+ * contributes its keys b * k_block .. min((b + 1) * k_block, s) - 1, each
+ * listing once (a block listed twice counts twice, like a repeated top-k
+ * index); other block ids are ignored; with `causal`, keys j > i are left
+ * out.  Attention per (row, head) is the forward's definition above (no
+ * sink); a row without keys gives out = 0, lse = +inf.
+ * rows_sel / n_sel select the rows (NULL: all); outputs are packed in that
+ * order: out [n_sel][h_q][d_v], lse [n_sel][h_q] (natural log). */
+int oracle_block_sparse_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const int32_t *q2k_row_ptr, const int32_t *q2k_col_idx, int64_t s,
+                            int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t q_block,
+                            int32_t k_block, int causal, double sm_scale, const int64_t *rows_sel,
+                            int64_t n_sel, double *out, double *lse, int threads)
+{
+    if (!q || !k || !v || !q2k_row_ptr || !out || !lse) return 1;
+    if (s < 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || d_qk <= 0 || d_v <= 0 ||
+        q_block <= 0 || k_block <= 0)
+        return 2;
+    if (rows_sel == NULL) n_sel = s;
+    const int64_t n_kblocks = (s + k_block - 1) / k_block;
+    const int32_t group = h_q / h_kv;
+    int bad = 0;
+#pragma omp parallel num_threads(oracle_threads(threads)) reduction(| : bad)
+    {
+        int64_t cap = 0;
+        int64_t *keys = NULL;
+        double *sc = NULL;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_sel; ++n) {
+            int64_t i = rows_sel ? rows_sel[n] : n;
+            if (i < 0 || i >= s) { bad = 1; continue; }
+            int64_t qb = i / q_block;
+            int64_t nk = 0;
+            for (int32_t e = q2k_row_ptr[qb]; e < q2k_row_ptr[qb + 1]; ++e) {
+                int64_t b = q2k_col_idx[e];
+                if (b < 0 || b >= n_kblocks) continue;
+                int64_t end = (b + 1) * k_block < s ? (b + 1) * k_block : s;
+                for (int64_t j = b * k_block; j < end; ++j) {
+                    if (causal && j > i) continue;
+                    if (nk == cap) {
+                        cap = cap ? 2 * cap : 1024;
+                        keys = realloc(keys, sizeof(int64_t) * (size_t)cap);
+                        sc = realloc(sc, sizeof(double) * (size_t)cap);
+                        if (!keys || !sc) { bad = 1; cap = 0; nk = 0; break; }
+                    }
+                    keys[nk++] = j;
+                }
+            }
+            for (int32_t h = 0; h < h_q; ++h) {
+                double *o = out + (n * h_q + h) * (int64_t)d_v;
+                for (int32_t c = 0; c < d_v; ++c) o[c] = 0.0;
+                if (nk == 0) { lse[n * h_q + h] = INFINITY; continue; }
+                const uint16_t *qh = q + (i * h_q + h) * (int64_t)d_qk;
+                const int32_t kvh = h / group;
+                double m = -INFINITY;
+                for (int64_t t = 0; t < nk; ++t) {
+                    const uint16_t *kr = k + (keys[t] * h_kv + kvh) * (int64_t)d_qk;
+                    double acc = 0.0;
+                    for (int32_t d = 0; d < d_qk; ++d) acc += bf16_to_double(qh[d]) * bf16_to_double(kr[d]);
+                    sc[t] = sm_scale * acc;
+                    if (sc[t] > m) m = sc[t];
+                }
+                double Z = 0.0;
+                for (int64_t t = 0; t < nk; ++t) {
+                    const double p = exp(sc[t] - m);
+                    const uint16_t *vr = v + (keys[t] * h_kv + kvh) * (int64_t)d_v;
+                    Z += p;
+                    for (int32_t c = 0; c < d_v; ++c) o[c] += p * bf16_to_double(vr[c]);
+                }
+                for (int32_t c = 0; c < d_v; ++c) o[c] /= Z;
+                lse[n * h_q + h] = m + log(Z);
+            }
+        }
+        free(keys);
+        free(sc);
+    }
+    return bad ? 3 : 0;
+}

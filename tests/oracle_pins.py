@@ -20,7 +20,11 @@ AssertionError when the oracle disagrees with:
   * for the backward (PR #198, "Summary", item 1): float64 autograd of the
     dense multiplicity-bias attention (with the sink as an extra value-less
     column, PR #198 "Numerics"), a single-key closed form, base-2 lse
-    (PR #198's bwd contract) and row / KV-row selection.
+    (PR #198's bwd contract) and row / KV-row selection;
+  * for the block-sparse forward (PR #198, "Summary", item 3, "Benchmarks":
+    a full-causal selection reproduces dense attention): torch SDPA in
+    float64 for full causal and full non-causal selections (with grouped KV
+    heads), and a numpy dense-mask brute force for random selections.
 
 tests/test_oracle_pins.py runs them on the real oracle;
 tests/test_oracle_mutants.py checks that each planted mistake fails one.
@@ -553,6 +557,93 @@ def pin_bwd_base2_and_selection(lib):
     assert np.array_equal(dq3, dq[rows]) and np.array_equal(dkv3, dkv[krows])
 
 
+
+# ---------------------------------------------------------------------------
+# block-sparse forward pins
+# ---------------------------------------------------------------------------
+
+def _bs_tiny(seed, s=45, h_q=4, h_kv=2, d_qk=24, d_v=16):
+    gen = torch.Generator().manual_seed(seed)
+    return gen, _bf16((s, h_q, d_qk), gen), _bf16((s, h_kv, d_qk), gen), _bf16((s, h_kv, d_v), gen)
+
+
+def _csr(lists):
+    ptr = np.zeros(len(lists) + 1, dtype=np.int32)
+    ptr[1:] = np.cumsum([len(x) for x in lists])
+    col = np.array([b for x in lists for b in x], dtype=np.int32)
+    return torch.from_numpy(ptr), torch.from_numpy(col)
+
+
+def _sdpa(q, k, v, scale, causal):
+    """torch SDPA in float64 with grouped KV heads; returns (out, lse)."""
+    qd, kd, vd = (_f64(x).permute(1, 0, 2) for x in (q, k, v))
+    g = qd.shape[0] // kd.shape[0]
+    kd, vd = kd.repeat_interleave(g, 0), vd.repeat_interleave(g, 0)
+    out = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, scale=scale, is_causal=causal)
+    sc = scale * (qd @ kd.transpose(1, 2))
+    if causal:
+        n = sc.shape[-1]
+        sc = sc.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), -math.inf)
+    return out.permute(1, 0, 2).numpy(), torch.logsumexp(sc, -1).T.numpy()
+
+
+def pin_block_sparse_full_selection_is_dense(lib):
+    """Selecting every key block up to the diagonal (causal), or every block
+    (not causal), is dense attention."""
+    for seed, (q_block, k_block) in [(301, (8, 4)), (302, (16, 16)), (303, (6, 10))]:
+        gen, q, k, v = _bs_tiny(seed)
+        s = q.shape[0]
+        nq, nk = -(-s // q_block), -(-s // k_block)
+        scale = 0.6 / math.sqrt(q.shape[2])
+        causal_lists = [list(range(min(nk, ((qb + 1) * q_block - 1) // k_block + 1)))[::-1]
+                        for qb in range(nq)]
+        for causal, lists in [(True, causal_lists), (False, [list(range(nk))] * nq)]:
+            ptr, col = _csr(lists)
+            out, lse = oracle.block_sparse_fwd(q, k, v, ptr, col, q_block, k_block, scale,
+                                               causal=causal, lib=lib)
+            ref_out, ref_lse = _sdpa(q, k, v, scale, causal)
+            _close(out, ref_out, 1e-11, 1e-12, f"block-sparse out (causal={causal})")
+            _close(lse, ref_lse, 1e-11, 1e-12, f"block-sparse lse (causal={causal})")
+
+
+def pin_block_sparse_bruteforce(lib):
+    """Random selections (repeated and out-of-range block ids, empty lists)
+    against dense attention with bias ln(count) over a numpy mask."""
+    for seed, causal in [(311, True), (312, False)]:
+        gen, q, k, v = _bs_tiny(seed, s=37, h_q=6, h_kv=3)
+        s, h_q, _ = q.shape
+        q_block, k_block = 8, 6
+        nq, nk = -(-s // q_block), -(-s // k_block)
+        lists = []
+        for qb in range(nq):
+            n = int(torch.randint(0, nk + 2, (1,), generator=gen))
+            lists.append([int(b) for b in torch.randint(-1, nk + 2, (n,), generator=gen)])
+        lists[0] = []
+        lists[1] = [2, 2, 0]
+        ptr, col = _csr(lists)
+        out, lse = oracle.block_sparse_fwd(q, k, v, ptr, col, q_block, k_block, 0.4, causal=causal,
+                                           lib=lib)
+        qn, kn, vn = _f64(q).numpy(), _f64(k).numpy(), _f64(v).numpy()
+        g = h_q // kn.shape[1]
+        for i in range(s):
+            count = np.zeros(s)
+            for b in lists[i // q_block]:
+                if 0 <= b < nk:
+                    count[b * k_block:min((b + 1) * k_block, s)] += 1
+            if causal:
+                count[i + 1:] = 0
+            for h in range(h_q):
+                if count.sum() == 0:
+                    assert np.all(out[i, h] == 0) and lse[i, h] == math.inf, "empty row"
+                    continue
+                with np.errstate(divide="ignore"):
+                    sc = 0.4 * (kn[:, h // g] @ qn[i, h]) + np.log(count)
+                m = sc.max()
+                w = np.exp(sc - m)
+                _close(out[i, h], (w @ vn[:, h // g]) / w.sum(), 1e-11, 1e-12, f"row {i} head {h}")
+                _close(lse[i, h], m + np.log(w.sum()), 1e-11, 1e-12, f"lse row {i} head {h}")
+
+
 ALL_PINS = [
     pin_dense_equals_library_attention,
     pin_sink_equals_extra_key,
@@ -569,4 +660,6 @@ ALL_PINS = [
     pin_bwd_equals_autograd,
     pin_bwd_single_key,
     pin_bwd_base2_and_selection,
+    pin_block_sparse_full_selection_is_dense,
+    pin_block_sparse_bruteforce,
 ]
