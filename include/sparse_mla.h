@@ -207,6 +207,34 @@ smla_status sparse_mla_bwd(const void *q, const void *kv, const void *out, const
                            size_t workspace_bytes, void *dq, void *dkv, float *d_sink,
                            smla_stream_t stream);
 
+/*
+ * Block-sparse attention forward at the non-absorbed MLA shape (FlashMLA
+ * PR #198, "Summary", item 3: each query block attends only its selected key
+ * blocks; "Benchmarks": 192/128 heads, full-causal selection = dense).  One
+ * sequence of s tokens.
+ *   q            bf16 [s, h_q, 192]
+ *   k            bf16 [s, h_kv, 192]; query head h reads KV head h / (h_q / h_kv)
+ *   v            bf16 [s, h_kv, 128]
+ *   q2k_row_ptr  int32 [ceil(s / q_block) + 1], non-decreasing from 0
+ *   q2k_col_idx  int32 [q2k_row_ptr[last]]: the key-block ids of each query
+ *                block (may be NULL when there are none).  Row i attends the
+ *                keys of every listed id of block i / q_block, each listing
+ *                once; ids outside [0, ceil(s / k_block)) are ignored
+ *   q_block, k_block  multiples of 64 (the pages' forward uses 256 / 128)
+ *   causal       1: only keys j <= i; 0: every key of the listed blocks
+ *   out          bf16 [s, h_q, 128] (output)
+ *   lse          fp32 [s, h_q] natural-log normaliser (output; +inf for a
+ *                row without keys, whose out is 0)
+ * The selection arrays are trusted to be consistent (they are read, not
+ * checked).  One kernel is enqueued on `stream`.
+ */
+smla_status sparse_mla_block_sparse_fwd(const void *q, const void *k, const void *v,
+                                        const int32_t *q2k_row_ptr, const int32_t *q2k_col_idx,
+                                        int32_t s, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                                        int32_t d_v, int32_t q_block, int32_t k_block,
+                                        int32_t causal, float sm_scale, void *out, float *lse,
+                                        smla_stream_t stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *sparse_mla_last_error(void);
 

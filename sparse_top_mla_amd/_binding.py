@@ -20,7 +20,7 @@ _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL_ARG", 2: "SMLA_ERR_BAD_SHAPE", 3: "SM
 
 EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_decode_split_workspace_bytes",
            "sparse_mla_decode_fwd_split", "sparse_mla_row_lengths", "sparse_mla_bwd_workspace_bytes",
-           "sparse_mla_bwd", "sparse_mla_last_error")
+           "sparse_mla_bwd", "sparse_mla_block_sparse_fwd", "sparse_mla_last_error")
 
 _lib = None
 
@@ -65,6 +65,9 @@ def _declare(lib):
     lib.sparse_mla_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                    f32, i32, vp, ctypes.c_size_t, vp, vp, vp, vp]
     lib.sparse_mla_bwd.restype = ctypes.c_int
+    lib.sparse_mla_block_sparse_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                i32, i32, f32, vp, vp, vp]
+    lib.sparse_mla_block_sparse_fwd.restype = ctypes.c_int
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
     return lib
@@ -317,3 +320,40 @@ def bwd(q, kv, out, dout, indices, lse, sm_scale, d_v=512, attn_sink=None, topk_
                             workspace.numel(), _p(dq), _p(dkv), _p(d_sink), _stream(dev, stream))
     _check(lib, st)
     return dq, dkv, d_sink
+
+
+def block_sparse_fwd(q, k, v, q2k_row_ptr, q2k_col_idx, q_block, k_block, sm_scale, causal=True,
+                     *, out=None, lse=None, stream=None):
+    """Block-sparse forward.  q [s, h_q, 192], k [s, h_kv, 192],
+    v [s, h_kv, 128] bf16; q2k_row_ptr [ceil(s / q_block) + 1] and
+    q2k_col_idx [nnz] int32 (the key-block ids of each query block).
+    Returns (out [s, h_q, 128] bf16, lse [s, h_q] fp32)."""
+    lib = load_library()
+    dev = q.device
+    _dev(q, "q", torch.bfloat16)
+    _dev(k, "k", torch.bfloat16, dev)
+    _dev(v, "v", torch.bfloat16, dev)
+    _dev(q2k_row_ptr, "q2k_row_ptr", torch.int32, dev)
+    if q2k_col_idx is not None and q2k_col_idx.numel() == 0:
+        q2k_col_idx = None
+    _dev(q2k_col_idx, "q2k_col_idx", torch.int32, dev)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be 3-d ([s, h, d])")
+    s, h_q, d_qk = q.shape
+    h_kv, d_v = k.shape[1], v.shape[2]
+    if k.shape[0] != s or v.shape[0] != s or k.shape[2] != d_qk or v.shape[1] != h_kv:
+        raise ValueError("inconsistent shapes of q, k and v")
+    if q2k_row_ptr.numel() != -(-s // q_block) + 1:
+        raise ValueError("q2k_row_ptr must have ceil(s / q_block) + 1 entries")
+    out = torch.empty((s, h_q, d_v), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse = torch.empty((s, h_q), dtype=torch.float32, device=dev) if lse is None else lse
+    _dev(out, "out", torch.bfloat16, dev)
+    _dev(lse, "lse", torch.float32, dev)
+    if out.numel() != s * h_q * d_v or lse.numel() != s * h_q:
+        raise ValueError("output buffers have the wrong size")
+    st = lib.sparse_mla_block_sparse_fwd(_p(q), _p(k), _p(v), _p(q2k_row_ptr), _p(q2k_col_idx), s,
+                                         h_q, h_kv, d_qk, d_v, int(q_block), int(k_block),
+                                         int(bool(causal)), float(sm_scale), _p(out), _p(lse),
+                                         _stream(dev, stream))
+    _check(lib, st)
+    return out, lse

@@ -12,7 +12,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SOURCES = [PKG / "csrc" / "sparse_mla.hip", PKG / "csrc" / "sparse_mla_bwd.hip"]
+SOURCES = [PKG / "csrc" / "sparse_mla.hip", PKG / "csrc" / "sparse_mla_bwd.hip",
+           PKG / "csrc" / "block_sparse_fwd.hip"]
 OUTPUT = PKG / "libsparse_mla.so"
 PROBE_SOURCES = [PKG / "csrc" / "peak_probe.hip"]
 PROBE_OUTPUT = PKG / "libsmla_probe.so"

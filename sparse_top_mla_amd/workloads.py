@@ -277,6 +277,79 @@ def bwd_synthetic_stats(case, seed):
     return out.to(torch.bfloat16), lse.to(torch.float32)
 
 
+@dataclass
+class BlockSparseCase:
+    name: str
+    q: torch.Tensor            # [s, h_q, 192] bf16
+    k: torch.Tensor            # [s, h_kv, 192] bf16
+    v: torch.Tensor            # [s, h_kv, 128] bf16
+    row_ptr: torch.Tensor      # [ceil(s / q_block) + 1] int32
+    col_idx: torch.Tensor      # [nnz] int32
+    q_block: int
+    k_block: int
+    causal: bool
+    sm_scale: float
+
+    @property
+    def s(self):
+        return self.q.shape[0]
+
+    @property
+    def h_q(self):
+        return self.q.shape[1]
+
+
+def _csr(lists):
+    ptr = torch.zeros(len(lists) + 1, dtype=torch.int32)
+    ptr[1:] = torch.cumsum(torch.tensor([len(x) for x in lists], dtype=torch.int64), 0).to(torch.int32)
+    col = torch.tensor([b for x in lists for b in x], dtype=torch.int32)
+    return ptr, col
+
+
+def make_block_sparse(name, *, s, h_q, h_kv, q_block, k_block, selection, seed, causal=True,
+                      window=4, density=0.3):
+    """Block-sparse case (192/128 heads).  selection:
+      "sink_window"  key block 0 plus the `window` key blocks that end at the
+                     query block's last row (the pages' benchmark selection)
+      "full_causal"  every key block up to that one (dense causal attention)
+      "random"       each key block up to that one with probability
+                     `density`, in random order, plus a few ids out of range"""
+    gen = torch.Generator().manual_seed(seed)
+    q = _randn_bf16((s, h_q, 192), gen)
+    k = _randn_bf16((s, h_kv, 192), gen)
+    v = _randn_bf16((s, h_kv, 128), gen)
+    nq, nk = -(-s // q_block), -(-s // k_block)
+    lists = []
+    for qb in range(nq):
+        last = min(nk - 1, (min((qb + 1) * q_block, s) - 1) // k_block) if causal else nk - 1
+        if selection == "sink_window":
+            sel = list(range(max(0, last - window + 1), last + 1))
+            if 0 not in sel:
+                sel = [0] + sel
+        elif selection == "full_causal":
+            sel = list(range(last + 1))
+        elif selection == "random":
+            keep = torch.rand(last + 1, generator=gen) < density
+            sel = [int(b) for b in torch.nonzero(keep).flatten()]
+            sel = [sel[i] for i in torch.randperm(len(sel), generator=gen).tolist()]
+            if torch.rand(1, generator=gen).item() < 0.3:
+                sel.append(int(nk + torch.randint(0, 3, (1,), generator=gen)))
+                sel.append(-1)
+        else:
+            raise ValueError(selection)
+        lists.append(sel)
+    ptr, col = _csr(lists)
+    return BlockSparseCase(name, q, k, v, ptr, col, q_block, k_block, causal,
+                           _as_f32(1.0 / math.sqrt(192)))
+
+
+def block_sparse_h8(seed=0, s=65536):
+    """The pages' block-sparse forward benchmark: h = 8, 192/128 heads,
+    q_block 256, k_block 128, causal, key block 0 plus a 4-block window."""
+    return make_block_sparse(f"block_sparse_h8_s{s}_sink_window4", s=s, h_q=8, h_kv=8, q_block=256,
+                             k_block=128, selection="sink_window", seed=seed)
+
+
 # ---------------------------------------------------------------------------
 # decode cases
 # ---------------------------------------------------------------------------

@@ -26,7 +26,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["sparse_mla_bwd", "sparse_mla_bwd_workspace_bytes",
+    assert _declared_functions() == ["sparse_mla_block_sparse_fwd", "sparse_mla_bwd",
+                                     "sparse_mla_bwd_workspace_bytes",
                                      "sparse_mla_decode_fwd", "sparse_mla_decode_fwd_split",
                                      "sparse_mla_decode_split_workspace_bytes", "sparse_mla_fwd",
                                      "sparse_mla_last_error", "sparse_mla_row_lengths"]
@@ -168,6 +169,28 @@ def test_bwd_rejects(lib, kw, status):
 
 def test_bwd_empty_is_noop(lib):
     assert _bwd(lib, s_q=0, s_kv=0, workspace=NULL, workspace_bytes=0) == 0
+
+
+def _bs(lib, **kw):
+    a = dict(q=P, k=P, v=P, row_ptr=P, col_idx=P, s=512, h_q=8, h_kv=8, d_qk=192, d_v=128,
+             q_block=256, k_block=128, causal=1, sm_scale=0.07, out=P, lse=P, stream=NULL)
+    a.update(kw)
+    return lib.sparse_mla_block_sparse_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_qk=576), 3), (dict(d_v=512), 3), (dict(q_block=100), 3), (dict(k_block=32), 3),
+    (dict(q_block=0), 3), (dict(h_kv=3), 2), (dict(h_q=0), 2), (dict(s=-1), 2),
+    (dict(causal=2), 2), (dict(sm_scale=-1.0), 3), (dict(q=NULL), 1), (dict(row_ptr=NULL), 1),
+    (dict(lse=NULL), 1),
+])
+def test_block_sparse_rejects(lib, kw, status):
+    assert _bs(lib, **kw) == status
+    assert lib.sparse_mla_last_error().decode()
+
+
+def test_block_sparse_empty_is_noop(lib):
+    assert _bs(lib, s=0, q=NULL, k=NULL, v=NULL, row_ptr=NULL, out=NULL, lse=NULL) == 0
 
 
 def test_row_lengths_rejects(lib):
