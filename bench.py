@@ -32,6 +32,7 @@ ROOT = Path(__file__).resolve().parent
 PROFILES = ROOT / "profiles"
 METRIC = "sparse MLA fwd ms/call + TFLOP/s over valid keys; % MFMA / HBM peak"
 METRIC_BWD = "sparse MLA bwd ms/call + TFLOP/s over valid keys; % MFMA peak"
+METRIC_BS = "block-sparse MLA fwd ms/call + TFLOP/s over selected (causal) pairs; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--workload", default="prefill_h64",
                     choices=["prefill_h64", "prefill_h64_len", "prefill_h128", "decode_dynamic",
                              "decode_dynamic_nolen", "decode_fixed", "decode_fixed_b2", "tiny",
-                             "bwd_h64"])
+                             "bwd_h64", "block_sparse_h8"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -88,11 +89,46 @@ def make_case(name):
     if name == "bwd_h64":
         # the pages' backward shape: T = 4096, topk = 2048, h_q = 64, d_qk = 576
         return W.bwd_h64()
+    if name == "block_sparse_h8":
+        # the pages' block-sparse forward benchmark: h = 8, 192/128, sink + 4-block window
+        return W.block_sparse_h8()
     raise ValueError(name)
 
 
 def is_decode(case):
     return hasattr(case, "kv_cache")
+
+
+def is_block_sparse(case):
+    return hasattr(case, "row_ptr")
+
+
+def bs_counts(case):
+    """Block-sparse FLOPs over the selected pairs (2 h_q (192 + 128) per
+    (row, key) pair a row attends) and the minimum bytes of one call: q, the
+    K and V rows some query block selects (once per KV head), the selection,
+    out and lse."""
+    s, qbk, kbk = case.s, case.q_block, case.k_block
+    ptr, col = case.row_ptr.numpy(), case.col_idx.numpy()
+    nk = -(-s // kbk)
+    pairs = np.zeros(s, dtype=np.int64)
+    named = np.zeros(nk, dtype=bool)
+    for qb in range(ptr.size - 1):
+        r0, r1 = qb * qbk, min((qb + 1) * qbk, s)
+        i = np.arange(r0, r1)
+        for b in col[ptr[qb]:ptr[qb + 1]]:
+            if not 0 <= b < nk:
+                continue
+            named[b] = True
+            k0, k1 = b * kbk, min((b + 1) * kbk, s)
+            pairs[r0:r1] += np.clip(i - k0 + 1, 0, k1 - k0) if case.causal else (k1 - k0)
+    h_q, h_kv = case.h_q, case.k.shape[1]
+    key_rows = int(sum(min((b + 1) * kbk, s) - b * kbk for b in np.nonzero(named)[0]))
+    n_pairs = int(pairs.sum())
+    bytes_ = (s * h_q * 192 * 2 + key_rows * h_kv * (192 + 128) * 2 + (ptr.size + col.size) * 4
+              + s * h_q * 128 * 2 + s * h_q * 4)
+    return dict(flops=2.0 * h_q * (192 + 128) * n_pairs, bytes=float(bytes_), valid_pairs=n_pairs,
+                rows=s, valid_per_row=pairs)
 
 
 def valid_mask(case):
@@ -164,6 +200,21 @@ def bwd_counts(case):
 # ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
+
+def gpu_call_bs(case, dev):
+    """One block-sparse forward call with every input resident on `dev`."""
+    import torch
+    import sparse_top_mla_amd as smla
+    args = [case.q.to(dev), case.k.to(dev), case.v.to(dev), case.row_ptr.to(dev),
+            case.col_idx.to(dev)]
+    out = torch.empty(case.s, case.h_q, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(case.s, case.h_q, dtype=torch.float32, device=dev)
+
+    def call():
+        smla.block_sparse_fwd(*args, case.q_block, case.k_block, case.sm_scale, causal=case.causal,
+                              out=out, lse=lse)
+    return call
+
 
 def gpu_call_bwd(case, dev):
     """One backward call with every input resident on `dev`: out and lse come
@@ -301,6 +352,37 @@ def cpu_baseline(case, counts, target_s):
             "seconds": t, "ms_per_call_extrapolated": float(t * counts["flops"] / flops * 1e3)}
 
 
+def cpu_baseline_bs(case, counts, target_s):
+    """The block-sparse oracle on an evenly spaced row sample."""
+    import oracle
+    rows = counts["rows"]
+    per_row = counts["valid_per_row"]
+    threads = host_threads()
+    pair_flops = 2.0 * case.h_q * (192 + 128)
+
+    def run(sel):
+        t0 = time.perf_counter()
+        oracle.block_sparse_fwd(case.q, case.k, case.v, case.row_ptr, case.col_idx, case.q_block,
+                                case.k_block, case.sm_scale, causal=case.causal, rows=sel,
+                                threads=threads)
+        return time.perf_counter() - t0
+
+    def sample(n):
+        n = max(1, min(rows, n))
+        return np.unique(np.linspace(0, rows - 1, n).round().astype(np.int64))
+
+    probe = sample(8 * threads)
+    t = run(probe)
+    rate = pair_flops * per_row[probe].sum() / max(t, 1e-9)
+    n = int(target_s * rate / max(pair_flops * per_row.mean(), 1.0))
+    sel = sample(n)
+    t = run(sel)
+    flops = pair_flops * per_row[sel].sum()
+    return {"value": float(flops / t / 1e12), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sel.size} of {rows} rows, evenly spaced, {t:.1f} s, fp64 C oracle",
+            "seconds": t}
+
+
 def cpu_baseline_bwd(case, counts, target_s):
     """The backward oracle's dq (S, dP and dQ of each pair: 2 h_q (2 d_qk +
     d_v) FLOPs) on an evenly spaced row sample, with seeded stand-ins for out
@@ -344,12 +426,14 @@ def cpu_baseline_bwd(case, counts, target_s):
 
 def kernel_file(workload):
     """Source file of the workload's dominant kernel."""
-    return "sparse_mla_bwd.hip" if workload == "bwd_h64" else "sparse_mla.hip"
+    return {"bwd_h64": "sparse_mla_bwd.hip",
+            "block_sparse_h8": "block_sparse_fwd.hip"}.get(workload, "sparse_mla.hip")
 
 
 def kernel_name(workload):
     """Name fragment of the workload's dominant kernel in rocprofv3 records."""
-    return "sparse_mla_bwd_kernel" if workload == "bwd_h64" else "sparse_mla_fwd"
+    return {"bwd_h64": "sparse_mla_bwd_kernel",
+            "block_sparse_h8": "block_sparse_fwd_kernel"}.get(workload, "sparse_mla_fwd")
 
 
 def kernel_source_digest(workload=None):
@@ -558,8 +642,9 @@ def main():
 
     case = make_case(args.workload)
     bwd = args.workload == "bwd_h64"
-    counts = bwd_counts(case) if bwd else algorithmic_counts(case)
-    call = gpu_call_bwd(case, dev) if bwd else gpu_call(case, dev)
+    bs = is_block_sparse(case)
+    counts = bwd_counts(case) if bwd else bs_counts(case) if bs else algorithmic_counts(case)
+    call = gpu_call_bwd(case, dev) if bwd else gpu_call_bs(case, dev) if bs else gpu_call(case, dev)
     call()
     torch.cuda.synchronize()
     ms_per_step, per = time_steps(call, args.steps, args.warmup)
@@ -582,7 +667,7 @@ def main():
             "kernel_ms_median": statistics.median(per_cold),
             "hbm_gbs_algorithmic": counts["bytes"] / (statistics.fmean(per_cold) * 1e-3) / 1e9}
         del calls
-    rows = case.batch * case.s_q if is_decode(case) else case.s_q
+    rows = case.batch * case.s_q if is_decode(case) else counts["rows"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if is_decode(case) and rows < cus and case.h_q == 128:
         # Fewer rows than CUs: the split-KV path, at the binding's split count.
@@ -606,7 +691,7 @@ def main():
         del call_len, case_len
 
     result = {
-        "metric": METRIC_BWD if bwd else METRIC,
+        "metric": METRIC_BWD if bwd else METRIC_BS if bs else METRIC,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -618,7 +703,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
+        "config": ({
+            "workload": case.name, "s": case.s, "h_q": case.h_q, "h_kv": case.k.shape[1],
+            "d_qk": 192, "d_v": 128, "q_block": case.q_block, "k_block": case.k_block,
+            "causal": case.causal, "selected_blocks": int(case.col_idx.numel()),
+            "valid_pairs": counts["valid_pairs"], "flops_per_call": counts["flops"],
+            "algorithmic_bytes_per_call": counts["bytes"],
+        } if bs else {
             "workload": case.name,
             "rows": counts["rows"],
             "h_q": case.h_q, "d_qk": case.d_qk, "d_v": case.d_v, "topk": case.topk,
@@ -627,7 +718,7 @@ def main():
             "algorithmic_bytes_per_call": counts["bytes"],
             "topk_length": case.topk_length is not None,
             "attn_sink": case.attn_sink is not None,
-        },
+        }),
         "kernel_ms": {"mean": kernel_ms, "median": statistics.median(per), "min": min(per),
                       "max": max(per)},
         "roofline": roofline(args.workload, case, counts, kernel_ms),
@@ -648,6 +739,8 @@ def main():
                                 "frac_of_attainable": result["roofline"]["achieved"] / att}
     if args.cpu_seconds > 0 and bwd:
         result["cpu_baseline"] = cpu_baseline_bwd(case, counts, args.cpu_seconds)
+    elif args.cpu_seconds > 0 and bs:
+        result["cpu_baseline"] = cpu_baseline_bs(case, counts, args.cpu_seconds)
     elif args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(case, counts, args.cpu_seconds)
     else:

@@ -12,9 +12,16 @@
 // without keys gives out = 0, lse = +inf.
 //
 // Layout of work: one workgroup per (64 query rows, query head), four waves
-// of 16 rows.  The key blocks of the query block are walked in 64-key tiles
-// (a tile wholly after the workgroup's last row is skipped under `causal`):
-//   K and V of the tile go to LDS (padded rows; keys past s as zeros);
+// of 16 rows.  Work items are numbered head-major (neighbouring items share
+// a head and their key tiles), and the launch hands each XCD a contiguous
+// range of them: workgroups are dispatched to the 8 XCDs in turn, so
+// workgroup L runs item (L % 8) * ceil(N / 8) + L / 8, and the items that
+// read the same K and V tiles meet in one XCD's L2.  The key blocks of the
+// query block are walked in 64-key tiles (a tile wholly after the
+// workgroup's last row is skipped under `causal`):
+//   K and V of the tile go to LDS (padded rows; keys past the block or s as
+//   zeros); the next tile's K and V are loaded into registers while this
+//   one is computed;
 //   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the query rows' slice in
 //   registers as the B operand, so each lane owns one query row and keeps
 //   its online-softmax state (running max, sum) as scalars;
@@ -61,6 +68,8 @@ struct BsArgs {
   __bf16* out;
   float* lse;
   int32_t s, h_q, h_kv, q_block, k_block, n_kblocks;
+  int32_t n_sub;       // 64-row groups of the sequence
+  int32_t per_xcd;     // work items per XCD range, ceil(n_sub * h_q / 8)
   float scale_log2;
 };
 
@@ -77,6 +86,68 @@ __device__ __forceinline__ bf16x8 tr_pair(const LDS_AS uint8_t* tile, int row_by
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Moves (e, t0, kend) to the tile after the current one (t0 < 0: to the
+// first tile of the list from entry e on): the next 64 keys of the current
+// block, else the first tile of the next listed block id in range.  Under
+// CAUSAL a tile starting after row_last ends its block.  Returns false at the
+// end of the list.  Every thread computes the same answer.
+template <bool CAUSAL>
+__device__ __forceinline__ bool next_tile(const BsArgs& a, int e_end, int row_last, int& e, int& t0,
+                                          int& kend) {
+  if (t0 >= 0) {
+    t0 += kTile;
+    if (t0 < kend && !(CAUSAL && t0 > row_last)) return true;
+    ++e;
+  }
+  for (; e < e_end; ++e) {
+    const int b = a.col_idx[e];
+    if (b < 0 || b >= a.n_kblocks) continue;
+    t0 = b * a.k_block;
+    kend = min(t0 + a.k_block, a.s);
+    if (CAUSAL && t0 > row_last) continue;
+    return true;
+  }
+  return false;
+}
+
+// One thread's share of a tile's K (6 chunks) and V (4 chunks) of 16 bytes;
+// keys at or past kend read as zeros.
+struct TileRegs {
+  u32x4 k[6], v[4];
+};
+
+__device__ __forceinline__ void load_tile(const BsArgs& a, int kvh, int t0, int kend, int tid,
+                                          TileRegs& r) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int c = tid + 256 * i, j = c / 24, ch = c % 24;
+    r.k[i] = t0 + j < kend ? *reinterpret_cast<const u32x4*>(
+                                 a.k + ((size_t)(t0 + j) * a.h_kv + kvh) * kDQK + ch * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, j = c / 16, ch = c % 16;
+    r.v[i] = t0 + j < kend ? *reinterpret_cast<const u32x4*>(
+                                 a.v + ((size_t)(t0 + j) * a.h_kv + kvh) * kDV + ch * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void store_tile(LDS_AS uint8_t* ks, LDS_AS uint8_t* vs, int tid,
+                                           const TileRegs& r) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int c = tid + 256 * i;
+    *reinterpret_cast<LDS_AS u32x4*>(ks + (c / 24) * kKRow + (c % 24) * 16) = r.k[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    *reinterpret_cast<LDS_AS u32x4*>(vs + (c / 16) * kVRow + (c % 16) * 16) = r.v[i];
+  }
+}
+
 template <bool CAUSAL>
 __global__ void __launch_bounds__(256) block_sparse_fwd_kernel(BsArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kTile * (kKRow + kVRow)];
@@ -88,9 +159,11 @@ __global__ void __launch_bounds__(256) block_sparse_fwd_kernel(BsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int hl = lane & 15;
-  const int head = blockIdx.y;
+  const int item = (int)(blockIdx.x % 8u) * a.per_xcd + (int)(blockIdx.x / 8u);
+  if (item >= a.n_sub * a.h_q) return;  // padding of the last XCD range (whole workgroup)
+  const int head = item / a.n_sub;
   const int kvh = head / (a.h_q / a.h_kv);
-  const int row0 = blockIdx.x * kRows;
+  const int row0 = (item % a.n_sub) * kRows;
   const int row = row0 + wave * 16 + hl;           // this lane's query row
   const int row_last = min(row0 + kRows, a.s) - 1;  // last row of the workgroup
 
@@ -110,32 +183,19 @@ __global__ void __launch_bounds__(256) block_sparse_fwd_kernel(BsArgs a) {
 
   const int qb = row0 / a.q_block;
   const int e_end = a.row_ptr[qb + 1];
-  for (int e = a.row_ptr[qb]; e < e_end; ++e) {
-    const int b = a.col_idx[e];
-    if (b < 0 || b >= a.n_kblocks) continue;
-    const int key_end = min((b + 1) * a.k_block, a.s);
-    for (int t0 = b * a.k_block; t0 < key_end; t0 += kTile) {
-      if (CAUSAL && t0 > row_last) break;  // every later key is after every row here
-
+  int e = a.row_ptr[qb], t0 = -1, kend = 0;
+  bool have = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+  TileRegs regs;
+  if (have) load_tile(a, kvh, t0, kend, tid, regs);
+  while (have) {
+    {
       __syncthreads();  // the previous tile's readers are done
-      // K: 64 rows x 24 chunks; V: 64 rows x 16 chunks (16 bytes each).
-      for (int c = tid; c < kTile * 24; c += 256) {
-        const int j = c / 24, ch = c % 24;
-        const int key = t0 + j;
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (key < key_end)
-          x = *reinterpret_cast<const u32x4*>(a.k + ((size_t)key * a.h_kv + kvh) * kDQK + ch * 8);
-        *reinterpret_cast<LDS_AS u32x4*>(ks + j * kKRow + ch * 16) = x;
-      }
-      for (int c = tid; c < kTile * 16; c += 256) {
-        const int j = c / 16, ch = c % 16;
-        const int key = t0 + j;
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (key < key_end)
-          x = *reinterpret_cast<const u32x4*>(a.v + ((size_t)key * a.h_kv + kvh) * kDV + ch * 8);
-        *reinterpret_cast<LDS_AS u32x4*>(vs + j * kVRow + ch * 16) = x;
-      }
+      store_tile(ks, vs, tid, regs);
       __syncthreads();
+      const int key_end = kend;
+      const int tile0 = t0;
+      have = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+      if (have) load_tile(a, kvh, t0, kend, tid, regs);  // in flight during this tile
 
       // S^T: lane (g, hl) gets keys 16 kt + 4g + r of row `row`.
       f32x4 st[4];
@@ -158,7 +218,7 @@ __global__ void __launch_bounds__(256) block_sparse_fwd_kernel(BsArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = t0 + kt * 16 + 4 * g + r;
+          const int key = tile0 + kt * 16 + 4 * g + r;
           const bool ok = key < key_end && (!CAUSAL || key <= row);
           const float x = ok ? st[kt][r] * a.scale_log2 : -INFINITY;
           st[kt][r] = x;
@@ -254,7 +314,6 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
     return bs_fail(SMLA_ERR_UNSUPPORTED, "q_block=%d k_block=%d (supported: multiples of 64)", q_block,
                    k_block);
   if (causal != 0 && causal != 1) return bs_fail(SMLA_ERR_BAD_SHAPE, "causal=%d (0 or 1)", causal);
-  if (h_q > 65535) return bs_fail(SMLA_ERR_UNSUPPORTED, "h_q=%d exceeds 65535", h_q);
   if (s == 0) return SMLA_OK;
   if (!q || !k || !v || !q2k_row_ptr || !out || !lse)
     return bs_fail(SMLA_ERR_NULL_ARG,
@@ -274,7 +333,12 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
   args.k_block = k_block;
   args.n_kblocks = (int32_t)(((int64_t)s + k_block - 1) / k_block);
   args.scale_log2 = sm_scale * kLog2e;
-  const dim3 grid((unsigned)((s + kRows - 1) / kRows), (unsigned)h_q);
+  args.n_sub = (s + kRows - 1) / kRows;
+  const int64_t items = (int64_t)args.n_sub * h_q;
+  if (items > 0x7fffffffLL - 8)
+    return bs_fail(SMLA_ERR_UNSUPPORTED, "s=%d with h_q=%d gives too many work items", s, h_q);
+  args.per_xcd = (int32_t)((items + 7) / 8);
+  const dim3 grid((unsigned)(8 * args.per_xcd));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (causal)
     hipLaunchKernelGGL(block_sparse_fwd_kernel<true>, grid, dim3(256), 0, st, args);
