@@ -11,8 +11,10 @@
 // [0, ceil(s / k_block)) ignored, and with `causal` only keys j <= i.  A row
 // without keys gives out = 0, lse = +inf.
 //
-// Layout of work: one workgroup per (64 query rows, query head), four waves
-// of 16 rows.  Work items are numbered head-major (neighbouring items share
+// Layout of work: one workgroup per (ROWS query rows, query head), waves of
+// 16 rows: ROWS = 128 (8 waves) when the query block is a multiple of 128,
+// else 64 (4 waves); the larger group shares each K and V tile between
+// twice the rows.  Work items are numbered head-major (neighbouring items share
 // a head and their key tiles), and the launch hands each XCD a contiguous
 // range of them: workgroups are dispatched to the 8 XCDs in turn, so
 // workgroup L runs item (L % 8) * ceil(N / 8) + L / 8, and the items that
@@ -51,7 +53,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDQK = 192;
 constexpr int kDV = 128;
-constexpr int kRows = 64;       // query rows per workgroup (16 per wave)
 constexpr int kTile = 64;       // keys per tile
 constexpr int kKRow = 2 * kDQK + 16;   // padded LDS row of K
 constexpr int kVRow = 2 * kDV + 16;    // padded LDS row of V
@@ -68,7 +69,7 @@ struct BsArgs {
   __bf16* out;
   float* lse;
   int32_t s, h_q, h_kv, q_block, k_block, n_kblocks;
-  int32_t n_sub;       // 64-row groups of the sequence
+  int32_t n_sub;       // ROWS-row groups of the sequence
   int32_t per_xcd;     // work items per XCD range, ceil(n_sub * h_q / 8)
   float scale_log2;
 };
@@ -110,46 +111,52 @@ __device__ __forceinline__ bool next_tile(const BsArgs& a, int e_end, int row_la
   return false;
 }
 
-// One thread's share of a tile's K (6 chunks) and V (4 chunks) of 16 bytes;
-// keys at or past kend read as zeros.
+// One thread's share of a tile's K (64 rows x 24 chunks) and V (64 x 16)
+// in 16-byte chunks, for THREADS threads; keys at or past kend read as zeros.
+template <int THREADS>
 struct TileRegs {
-  u32x4 k[6], v[4];
+  static constexpr int kK = kTile * 24 / THREADS, kV = kTile * 16 / THREADS;
+  u32x4 k[kK], v[kV];
 };
 
+template <int THREADS>
 __device__ __forceinline__ void load_tile(const BsArgs& a, int kvh, int t0, int kend, int tid,
-                                          TileRegs& r) {
+                                          TileRegs<THREADS>& r) {
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int c = tid + 256 * i, j = c / 24, ch = c % 24;
+  for (int i = 0; i < TileRegs<THREADS>::kK; ++i) {
+    const int c = tid + THREADS * i, j = c / 24, ch = c % 24;
     r.k[i] = t0 + j < kend ? *reinterpret_cast<const u32x4*>(
                                  a.k + ((size_t)(t0 + j) * a.h_kv + kvh) * kDQK + ch * 8)
                            : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, j = c / 16, ch = c % 16;
+  for (int i = 0; i < TileRegs<THREADS>::kV; ++i) {
+    const int c = tid + THREADS * i, j = c / 16, ch = c % 16;
     r.v[i] = t0 + j < kend ? *reinterpret_cast<const u32x4*>(
                                  a.v + ((size_t)(t0 + j) * a.h_kv + kvh) * kDV + ch * 8)
                            : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
+template <int THREADS>
 __device__ __forceinline__ void store_tile(LDS_AS uint8_t* ks, LDS_AS uint8_t* vs, int tid,
-                                           const TileRegs& r) {
+                                           const TileRegs<THREADS>& r) {
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < TileRegs<THREADS>::kK; ++i) {
+    const int c = tid + THREADS * i;
     *reinterpret_cast<LDS_AS u32x4*>(ks + (c / 24) * kKRow + (c % 24) * 16) = r.k[i];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < TileRegs<THREADS>::kV; ++i) {
+    const int c = tid + THREADS * i;
     *reinterpret_cast<LDS_AS u32x4*>(vs + (c / 16) * kVRow + (c % 16) * 16) = r.v[i];
   }
 }
 
-template <bool CAUSAL>
-__global__ void __launch_bounds__(256) block_sparse_fwd_kernel(BsArgs a) {
+template <bool CAUSAL, int ROWS>
+__global__ void __launch_bounds__(ROWS * 4) block_sparse_fwd_kernel(BsArgs a) {
+  constexpr int kRows = ROWS;
+  constexpr int kThreads = ROWS * 4;  // 16 rows per wave
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kTile * (kKRow + kVRow)];
   LDS_AS uint8_t* ks = (LDS_AS uint8_t*)lds_raw;
   LDS_AS uint8_t* vs = ks + kTile * kKRow;
@@ -185,7 +192,7 @@ __global__ void __launch_bounds__(256) block_sparse_fwd_kernel(BsArgs a) {
   const int e_end = a.row_ptr[qb + 1];
   int e = a.row_ptr[qb], t0 = -1, kend = 0;
   bool have = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
-  TileRegs regs;
+  TileRegs<kThreads> regs;
   if (have) load_tile(a, kvh, t0, kend, tid, regs);
   while (have) {
     {
@@ -310,7 +317,7 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
     return bs_fail(SMLA_ERR_UNSUPPORTED, "sm_scale=%g (must be positive and finite)", (double)sm_scale);
   if (d_qk != kDQK || d_v != kDV)
     return bs_fail(SMLA_ERR_UNSUPPORTED, "d_qk=%d d_v=%d (supported: 192 / 128)", d_qk, d_v);
-  if (q_block <= 0 || q_block % kRows != 0 || k_block <= 0 || k_block % kTile != 0)
+  if (q_block <= 0 || q_block % 64 != 0 || k_block <= 0 || k_block % kTile != 0)
     return bs_fail(SMLA_ERR_UNSUPPORTED, "q_block=%d k_block=%d (supported: multiples of 64)", q_block,
                    k_block);
   if (causal != 0 && causal != 1) return bs_fail(SMLA_ERR_BAD_SHAPE, "causal=%d (0 or 1)", causal);
@@ -333,17 +340,26 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
   args.k_block = k_block;
   args.n_kblocks = (int32_t)(((int64_t)s + k_block - 1) / k_block);
   args.scale_log2 = sm_scale * kLog2e;
-  args.n_sub = (s + kRows - 1) / kRows;
+  const int rows = q_block % 128 == 0 ? 128 : 64;
+  args.n_sub = (s + rows - 1) / rows;
   const int64_t items = (int64_t)args.n_sub * h_q;
   if (items > 0x7fffffffLL - 8)
     return bs_fail(SMLA_ERR_UNSUPPORTED, "s=%d with h_q=%d gives too many work items", s, h_q);
   args.per_xcd = (int32_t)((items + 7) / 8);
   const dim3 grid((unsigned)(8 * args.per_xcd));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (causal)
-    hipLaunchKernelGGL(block_sparse_fwd_kernel<true>, grid, dim3(256), 0, st, args);
-  else
-    hipLaunchKernelGGL(block_sparse_fwd_kernel<false>, grid, dim3(256), 0, st, args);
+  const dim3 block((unsigned)(rows * 4));
+  if (rows == 128) {
+    if (causal)
+      hipLaunchKernelGGL((block_sparse_fwd_kernel<true, 128>), grid, block, 0, st, args);
+    else
+      hipLaunchKernelGGL((block_sparse_fwd_kernel<false, 128>), grid, block, 0, st, args);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((block_sparse_fwd_kernel<true, 64>), grid, block, 0, st, args);
+    else
+      hipLaunchKernelGGL((block_sparse_fwd_kernel<false, 64>), grid, block, 0, st, args);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return bs_fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
