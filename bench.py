@@ -621,7 +621,7 @@ def main():
         ingest_counters(args.ingest_counters)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
