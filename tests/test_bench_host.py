@@ -8,6 +8,9 @@ plausible-looking number.
 import csv
 import json
 
+import numpy as np
+import pytest
+
 import bench
 
 
@@ -62,3 +65,32 @@ def test_ingest_counters_scales_by_the_copy(tmp_path, monkeypatch):
     assert abs(rec["write_bytes_per_launch"] - 500 * 1024 * 1.0) < 1e-6
     assert rec["kernel_source_sha256_16"] == bench.kernel_source_digest()
     assert "mfma_busy_frac" not in rec  # no MFMA run given
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_sparse_pair_count_is_brute_force(causal):
+    """bench.bs_counts counts the (row, key) pairs the block-sparse forward
+    attends: brute force over rows, listed blocks and keys."""
+    from sparse_top_mla_amd import workloads as W
+    case = W.make_block_sparse("count", s=300, h_q=2, h_kv=1, q_block=64, k_block=64,
+                               selection="random", seed=3, causal=causal)
+    got = bench.bs_counts(case)
+    ptr, col = case.row_ptr.numpy(), case.col_idx.numpy()
+    per_row = np.zeros(300, dtype=np.int64)
+    for i in range(300):
+        qb = i // 64
+        for b in col[ptr[qb]:ptr[qb + 1]]:
+            if 0 <= b < 5:
+                per_row[i] += sum(1 for j in range(b * 64, min(b * 64 + 64, 300))
+                                  if not causal or j <= i)
+    assert np.array_equal(got["valid_per_row"], per_row)
+    assert got["flops"] == 2.0 * 2 * (192 + 128) * per_row.sum()
+
+
+def test_bwd_flops_count_five_products():
+    """The backward's FLOPs are 2 h_q (3 d_qk + 2 d_v) per valid pair."""
+    from sparse_top_mla_amd import workloads as W
+    case = W.bwd_h64(s_q=64, s_kv=64, topk=32)
+    c = bench.bwd_counts(case)
+    assert c["flops"] == 2.0 * 64 * (3 * 576 + 2 * 512) * c["valid_pairs"]
+    assert c["valid_pairs"] == sum(min(i + 1, 32) for i in range(64))
