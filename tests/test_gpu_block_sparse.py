@@ -83,3 +83,12 @@ def test_block_sparse_full_size_sampled():
     out, lse = _run(case)
     rows = np.array([0, 1, 63, 64, 255, 256, 511, 1000, 4095, 30000, 65279, 65280, 65535])
     _check(case, out, lse, rows=rows)
+
+
+def test_block_sparse_one_kv_head_not_causal():
+    """16 query heads on one KV head, no causal mask, 128-row workgroups with
+    a sequence that ends inside a workgroup and inside a key block."""
+    case = W.make_block_sparse("bs_mqa_noncausal", s=1000, h_q=16, h_kv=1, q_block=128,
+                               k_block=64, selection="random", causal=False, seed=21, density=0.5)
+    out, lse = _run(case)
+    _check(case, out, lse)

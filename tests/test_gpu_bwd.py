@@ -163,3 +163,19 @@ def test_bwd_unsupported_heads_raise():
     lse = torch.zeros(4, 32)
     with pytest.raises(smla.SparseMLAError, match="h_q"):
         _run(case, out, lse, dout)
+
+
+def test_bwd_d512_sampled():
+    """d_qk = 512 at T = 2048, topk = 1024: dq of sampled rows and dkv of
+    sampled KV rows."""
+    case = W.bwd_h64(s_q=2048, s_kv=2048, topk=1024, d_qk=512)
+    dout = W.bwd_dout(case, seed=12)
+    out, lse = W.bwd_synthetic_stats(case, seed=13)
+    dq, dkv, _ = _run(case, out, lse, dout)
+    rows = np.array([0, 5, 1023, 1024, 1500, 2047])
+    kv_rows = np.array([0, 3, 1000, 1024, 2040, 2047])
+    rq, rkv, _ = oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse,
+                                       case.sm_scale, case.d_v, topk_length=case.topk_length,
+                                       rows=rows, kv_rows=kv_rows)
+    _close("dq (sampled rows, d512)", dq[torch.from_numpy(rows).to(DEV)], rq)
+    _close("dkv (sampled KV rows, d512)", dkv[torch.from_numpy(kv_rows).to(DEV), 0, :], rkv)
