@@ -92,3 +92,23 @@ def test_block_sparse_one_kv_head_not_causal():
                                k_block=64, selection="random", causal=False, seed=21, density=0.5)
     out, lse = _run(case)
     _check(case, out, lse)
+
+
+def test_block_sparse_random_shapes():
+    """Seeded random shapes: sequence lengths down to 1, head groupings, both
+    workgroup sizes (query blocks multiple of 128 or only of 64), key blocks
+    of 64 to 192, causal or not, random selections."""
+    rng = np.random.default_rng(77)
+    for t in range(10):
+        s = int(rng.choice([1, 7, 63, 64, 65, 200, 513, 900]))
+        h_kv = int(rng.choice([1, 2, 4]))
+        h_q = h_kv * int(rng.choice([1, 2, 4]))
+        q_block = int(rng.choice([64, 128, 192, 256]))
+        k_block = int(rng.choice([64, 128, 192]))
+        causal = bool(rng.integers(0, 2))
+        case = W.make_block_sparse(f"bs_rand{t}_s{s}_h{h_q}x{h_kv}_q{q_block}_k{k_block}", s=s,
+                                   h_q=h_q, h_kv=h_kv, q_block=q_block, k_block=k_block,
+                                   selection="random", causal=causal, seed=100 + t,
+                                   density=float(rng.uniform(0.2, 0.9)))
+        out, lse = _run(case)
+        _check(case, out, lse)
