@@ -179,3 +179,31 @@ def test_bwd_d512_sampled():
                                        rows=rows, kv_rows=kv_rows)
     _close("dq (sampled rows, d512)", dq[torch.from_numpy(rows).to(DEV)], rq)
     _close("dkv (sampled KV rows, d512)", dkv[torch.from_numpy(kv_rows).to(DEV), 0, :], rkv)
+
+
+def test_bwd_random_shapes():
+    """Seeded random shapes: row and KV counts, topk not a multiple of the
+    32-key block, d_qk, layout, lengths and sink."""
+    rng = np.random.default_rng(91)
+    for t in range(6):
+        d_qk = int(rng.choice([512, 576]))
+        s_q = int(rng.integers(1, 40))
+        s_kv = int(rng.integers(8, 300))
+        topk = int(rng.integers(1, min(s_kv, 130) + 1))
+        layout = str(rng.choice(["ramp", "scattered"]))
+        sink = bool(rng.integers(0, 2))
+        kw = dict(ramp_cap=topk, with_length=bool(rng.integers(0, 2))) if layout == "ramp" else \
+            dict(invalid_frac=0.2, empty_frac=0.1)
+        case = W.make_prefill(f"bwd_rand{t}_d{d_qk}_{layout}", s_q=s_q, s_kv=s_kv, h_q=64,
+                              d_qk=d_qk, d_v=512, topk=topk, layout=layout, seed=200 + t,
+                              with_sink=sink, **kw)
+        dout = W.bwd_dout(case, seed=300 + t)
+        out, lse = _oracle_stats(case)
+        dq, dkv, ds = _run(case, out, lse, dout)
+        rq, rkv, rs = oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse,
+                                            case.sm_scale, case.d_v, attn_sink=case.attn_sink,
+                                            topk_length=case.topk_length, want_d_sink=sink)
+        _close(f"dq {case.name}", dq, rq)
+        _close(f"dkv {case.name}", dkv[:, 0, :], rkv)
+        if sink:
+            _close(f"d_sink {case.name}", ds, rs)
