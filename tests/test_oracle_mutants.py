@@ -59,7 +59,7 @@ MUTANTS = [
     ("bwd_base2_inverted", "double l = lse_base2 ? lse * log(2.0) : lse;",
      "double l = lse_base2 ? lse / log(2.0) : lse;"),
     ("bs_causal_excludes_diagonal", "if (causal && j > i) continue;", "if (causal && j >= i) continue;"),
-    ("bs_query_block_by_key_block", "int64_t qb = i / q_block;", "int64_t qb = i / k_block;"),
+    ("bs_query_block_halved", "int64_t qb = i / q_block;", "int64_t qb = i / (2 * q_block);"),
     ("bs_kv_head_interleaved", "const int32_t kvh = h / group;", "const int32_t kvh = h % h_kv;"),
     ("bs_lse_drops_max", "lse[n * h_q + h] = m + log(Z);", "lse[n * h_q + h] = log(Z);"),
     ("bs_value_not_weighted", "for (int32_t c = 0; c < d_v; ++c) o[c] += p * bf16_to_double(vr[c]);",
