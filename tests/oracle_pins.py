@@ -433,6 +433,74 @@ def pin_decode_equals_gathered_prefill(lib):
         assert np.array_equal(long[0][r], ref[0][r]) and long_len[r] == ref_len[r]
 
 
+def pin_decode_page_range_mask(lib):
+    """A valid position whose block-table entry lies outside [0, num_blocks)
+    is masked like an invalid index (reading of FlashMLA PR #216,
+    "Correctness": no illegal memory access), while the tail scan still reads
+    index values only.  Every other key is kept, among them keys on physical
+    pages 0 and num_blocks - 1 and on a page two requests share.  Checked on
+    every row, with and without explicit lengths and with a sink, against
+    the numpy multiplicity brute force over the request's keys with those
+    positions dropped."""
+    page, num_blocks = 8, 9
+    gen = torch.Generator().manual_seed(97)
+    B, s_q, h_q, d_qk, d_v, topk = 2, 3, 3, 24, 16, 40
+    seqlens = torch.tensor([48, 40], dtype=torch.int32)
+    # logical pages: request 0 -> 0, -1, 8, num_blocks, 3, 5; request 1 ->
+    # num_blocks + 3, 7, 1, -7, 8 (physical page 8 is shared)
+    bt = torch.tensor([[0, -1, 8, num_blocks, 3, 5, 2],
+                       [num_blocks + 3, 7, 1, -7, 8, 4, 6]], dtype=torch.int32)
+    q = _bf16((B, s_q, h_q, d_qk), gen)
+    cache = _bf16((num_blocks, page, 1, d_qk), gen)
+    sink = torch.randn(h_q, generator=gen)
+    idx = torch.full((B, s_q, topk), -1, dtype=torch.int32)
+    for b in range(B):
+        n = int(seqlens[b])
+        for t in range(s_q):
+            k = 30 - 4 * t
+            idx[b, t, :k] = torch.randperm(n, generator=gen)[:k].to(torch.int32)
+    # the last valid entry of these rows sits on a masked page: the derived
+    # length still counts it (the tail scan reads index values only)
+    idx[0, 0, 29] = 1 * page + 3      # logical page 1 -> -1
+    idx[1, 1, 25] = 0 * page + 5      # logical page 0 -> num_blocks + 3
+    idx[0, 2, 33] = 3 * page + 1      # logical page 3 -> num_blocks, past -1 padding
+    # every position of this row is on a masked page: the row has no key
+    idx[1, 2, :6] = torch.tensor([3, 30, 25, 1, 26, 7], dtype=torch.int32)
+    idx[1, 2, 6:] = -1
+    cache_v = cache.view(-1, 1, d_qk)
+    bt_n = bt.numpy().astype(np.int64)
+    for tl in (None, torch.tensor([[40, 12, 34], [3, 26, 6]], dtype=torch.int32)):
+        out, lse, ml, rl = oracle.sparse_mla_decode_fwd(q, cache, bt, seqlens, idx, 0.21, d_v,
+                                                        attn_sink=sink, topk_length=tl, lib=lib)
+        for b in range(B):
+            n = int(seqlens[b])
+            pos = np.arange(n)
+            pg = bt_n[b][pos // page]
+            on_pool = (pg >= 0) & (pg < num_blocks)
+            phys = np.where(on_pool, pg, 0) * page + pos % page
+            contig = cache_v[torch.from_numpy(phys)]
+            ib = idx[b].numpy().astype(np.int64)
+            in_range = (ib >= 0) & (ib < n)
+            kept = in_range & on_pool[np.where(in_range, ib, 0)]
+            # lengths: the index values against the cache length alone
+            if tl is None:
+                want_len = np.array([(np.nonzero(r)[0][-1] + 1) if r.any() else 0
+                                     for r in in_range])
+            else:
+                want_len = np.clip(tl[b].numpy(), 0, topk)
+            dropped = torch.from_numpy(np.where(kept, ib, -1).astype(np.int32))
+            ro, rls, rml, _ = _multiplicity_reference(
+                q[b], contig, dropped.view(s_q, 1, -1), 0.21, d_v,
+                topk_length=torch.from_numpy(want_len.astype(np.int32)), sink=sink)
+            sl = slice(b * s_q, (b + 1) * s_q)
+            assert np.array_equal(rl[sl], want_len), "decode row length"
+            _close(out[sl], ro, rtol=1e-10, atol=1e-12, what="decode page-range out")
+            _close(lse[sl], rls, what="decode page-range lse")
+            _close(ml[sl], rml, what="decode page-range max_logits")
+        # the row whose keys are all on masked pages gives the empty-row triple
+        assert np.all(out[5] == 0) and np.all(lse[5] == np.inf) and np.all(ml[5] == -np.inf)
+
+
 def pin_row_selection(lib):
     """Evaluating a subset of rows returns exactly those rows of the full run."""
     gen, q, kv = _tiny(81, 7, 30, 2, 16, 16)
@@ -656,6 +724,7 @@ ALL_PINS = [
     pin_length_and_encoding_invariance,
     pin_nan_in_unreferenced_rows,
     pin_decode_equals_gathered_prefill,
+    pin_decode_page_range_mask,
     pin_row_selection,
     pin_bwd_equals_autograd,
     pin_bwd_single_key,

@@ -35,6 +35,12 @@ MUTANTS = [
      "keys[nk++] = kv_cache + (page * page_size + idx[j] / page_size) * (int64_t)d_qk;"),
     ("page_table_row_wrong", "int64_t page = block_table[b * max_blocks_per_seq + idx[j] / page_size];",
      "int64_t page = block_table[idx[j] / page_size];"),
+    ("page_range_drops_page_zero", "if (page < 0 || page >= num_blocks) continue;",
+     "if (page <= 0 || page >= num_blocks) continue;"),
+    ("page_range_drops_last_page", "if (page < 0 || page >= num_blocks) continue;",
+     "if (page < 0 || page >= num_blocks - 1) continue;"),
+    ("page_range_clamps_instead_of_masking", "if (page < 0 || page >= num_blocks) continue;",
+     "if (page < 0 || page >= num_blocks) page = 0;"),
     ("decode_bound_ignored", "if (!is_valid_index(idx[j], bound)) continue;",
      "if (!is_valid_index(idx[j], 1 << 30)) continue;"),
     ("row_bound_not_clamped",
