@@ -18,6 +18,7 @@ sample of the same rows.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -57,6 +58,8 @@ def parse():
     ap.add_argument("--attainable", action="store_true",
                     help="measure this device's attainable dense bf16 MFMA rate (an MFMA loop) and HBM "
                          "bandwidth (a streaming copy) into profiles/attainable_peaks.json")
+    ap.add_argument("--no-variants", dest="variants", action="store_false",
+                    help="default workload only: skip the other configurations under 'variants'")
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode: also time calls that rotate over this many copies of the inputs "
                          "(cold Infinity Cache); 0 disables")
@@ -200,19 +203,40 @@ def bwd_counts(case):
 # ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
+#
+# A timed step is one call of the library's C entry point with every argument
+# marshalled beforehand (inputs and outputs resident on the device): the
+# Python binding's per-call checks cost tens of microseconds, as much as a
+# decode kernel, and are not part of the hot path.  The first call of every
+# workload goes through the binding, which validates the shapes.
+
+def _vp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _checked(lib, fn, args):
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"status {st}: {lib.sparse_mla_last_error().decode()}")
+    return call
+
 
 def gpu_call_bs(case, dev):
     """One block-sparse forward call with every input resident on `dev`."""
     import torch
     import sparse_top_mla_amd as smla
-    args = [case.q.to(dev), case.k.to(dev), case.v.to(dev), case.row_ptr.to(dev),
-            case.col_idx.to(dev)]
-    out = torch.empty(case.s, case.h_q, 128, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty(case.s, case.h_q, dtype=torch.float32, device=dev)
-
-    def call():
-        smla.block_sparse_fwd(*args, case.q_block, case.k_block, case.sm_scale, causal=case.causal,
-                              out=out, lse=lse)
+    lib = smla.load_library()
+    q, k, v, rp, ci = (x.to(dev) for x in (case.q, case.k, case.v, case.row_ptr, case.col_idx))
+    out, lse = smla.block_sparse_fwd(q, k, v, rp, ci, case.q_block, case.k_block, case.sm_scale,
+                                     causal=case.causal)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (_vp(q), _vp(k), _vp(v), _vp(rp), _vp(ci) if ci.numel() else None, case.s, case.h_q,
+            k.shape[1], 192, 128, case.q_block, case.k_block, int(bool(case.causal)),
+            ctypes.c_float(case.sm_scale), _vp(out), _vp(lse), stream)
+    keep = (q, k, v, rp, ci, out, lse)
+    call = _checked(lib, lib.sparse_mla_block_sparse_fwd, args)
+    call.keep = keep
     return call
 
 
@@ -223,6 +247,7 @@ def gpu_call_bwd(case, dev):
     import torch
     import sparse_top_mla_amd as smla
     from sparse_top_mla_amd import workloads as W
+    lib = smla.load_library()
     t = lambda x: None if x is None else x.to(dev)  # noqa: E731
     q, kv, idx = t(case.q), t(case.kv), t(case.indices)
     sink, tl = t(case.attn_sink), t(case.topk_length)
@@ -230,12 +255,15 @@ def gpu_call_bwd(case, dev):
     dout = t(W.bwd_dout(case, seed=8))
     ws = torch.empty(smla.bwd_workspace_bytes(case.s_q, case.s_kv, case.d_qk), dtype=torch.uint8,
                      device=dev)
-    dq, dkv = torch.empty_like(q), torch.empty_like(kv)
+    dq, dkv, _ = smla.bwd(q, kv, out, dout, idx, lse, case.sm_scale, case.d_v, attn_sink=sink,
+                          topk_length=tl, workspace=ws)
     torch.cuda.synchronize()
-
-    def call():
-        smla.bwd(q, kv, out, dout, idx, lse, case.sm_scale, case.d_v, attn_sink=sink,
-                 topk_length=tl, workspace=ws, dq=dq, dkv=dkv)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (_vp(q), _vp(kv), _vp(out), _vp(dout), _vp(idx), _vp(tl), _vp(lse), _vp(sink),
+            case.s_q, case.s_kv, case.h_q, 1, case.d_qk, case.d_v, case.topk,
+            ctypes.c_float(case.sm_scale), 0, _vp(ws), ws.numel(), _vp(dq), _vp(dkv), None, stream)
+    call = _checked(lib, lib.sparse_mla_bwd, args)
+    call.keep = (q, kv, idx, sink, tl, out, lse, dout, ws, dq, dkv)
     return call
 
 
@@ -245,62 +273,81 @@ def gpu_call(case, dev, num_splits=1):
     here, outside the call)."""
     import torch
     import sparse_top_mla_amd as smla
+    lib = smla.load_library()
     t = lambda x: None if x is None else x.to(dev)  # noqa: E731
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    scale = ctypes.c_float(case.sm_scale)
     if is_decode(case):
-        args = [t(case.q), t(case.kv_cache), t(case.block_table), t(case.cache_seqlens),
-                t(case.indices)]
+        q, kvc, bt, cs, idx = (t(case.q), t(case.kv_cache), t(case.block_table),
+                               t(case.cache_seqlens), t(case.indices))
         sink, tl = t(case.attn_sink), t(case.topk_length)
-        out = torch.empty(case.batch, case.s_q, case.h_q, case.d_v, dtype=torch.bfloat16, device=dev)
-        lse = torch.empty(case.batch, case.s_q, case.h_q, dtype=torch.float32, device=dev)
-        ml = torch.empty_like(lse)
+        B, s_q, h_q, d_qk = q.shape
+        common = (_vp(q), _vp(kvc), _vp(bt), _vp(cs), _vp(idx), _vp(tl), _vp(sink), B, s_q, h_q, 1,
+                  d_qk, case.d_v, case.topk, kvc.shape[0], kvc.shape[1], bt.shape[1], scale)
         if num_splits > 1:
-            ws = torch.empty(smla.decode_split_workspace_bytes(case.batch, case.s_q, case.h_q,
-                                                               case.d_v, num_splits),
+            ws = torch.empty(smla.decode_split_workspace_bytes(B, s_q, h_q, case.d_v, num_splits),
                              dtype=torch.uint8, device=dev)
-
-            def call():
-                smla.decode_fwd_split(*args, case.sm_scale, num_splits, case.d_v, attn_sink=sink,
-                                      topk_length=tl, workspace=ws, out=out, lse=lse,
-                                      max_logits=ml)
+            out, lse, ml = smla.decode_fwd_split(q, kvc, bt, cs, idx, case.sm_scale, num_splits,
+                                                 case.d_v, attn_sink=sink, topk_length=tl,
+                                                 workspace=ws)
+            args = common + (num_splits, _vp(ws), ws.numel(), _vp(out), _vp(lse), _vp(ml), stream)
+            call = _checked(lib, lib.sparse_mla_decode_fwd_split, args)
+            call.keep = (q, kvc, bt, cs, idx, sink, tl, ws, out, lse, ml)
             return call
-
-        def call():
-            smla.decode_fwd(*args, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl,
-                            out=out, lse=lse, max_logits=ml)
-    else:
-        args = [t(case.q), t(case.kv), t(case.indices)]
-        sink, tl = t(case.attn_sink), t(case.topk_length)
-        out = torch.empty(case.s_q, case.h_q, case.d_v, dtype=torch.bfloat16, device=dev)
-        lse = torch.empty(case.s_q, case.h_q, dtype=torch.float32, device=dev)
-        ml = torch.empty_like(lse)
-
-        def call():
-            smla.fwd(*args, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl, out=out,
-                     lse=lse, max_logits=ml)
+        out, lse, ml = smla.decode_fwd(q, kvc, bt, cs, idx, case.sm_scale, case.d_v,
+                                       attn_sink=sink, topk_length=tl)
+        args = common + (_vp(out), _vp(lse), _vp(ml), stream)
+        call = _checked(lib, lib.sparse_mla_decode_fwd, args)
+        call.keep = (q, kvc, bt, cs, idx, sink, tl, out, lse, ml)
+        return call
+    q, kv, idx = t(case.q), t(case.kv), t(case.indices)
+    sink, tl = t(case.attn_sink), t(case.topk_length)
+    out, lse, ml = smla.fwd(q, kv, idx, case.sm_scale, case.d_v, attn_sink=sink, topk_length=tl)
+    s_q, h_q, d_qk = q.shape
+    args = (_vp(q), _vp(kv), _vp(idx), _vp(tl), _vp(sink), s_q, kv.shape[0], h_q, 1, d_qk,
+            case.d_v, case.topk, scale, _vp(out), _vp(lse), _vp(ml), stream)
+    call = _checked(lib, lib.sparse_mla_fwd, args)
+    call.keep = (q, kv, idx, sink, tl, out, lse, ml)
     return call
 
 
 def time_steps(call, steps, warmup):
     """W untimed calls, then exactly K calls between two synchronisations.
-    Every call is bracketed by events on the stream it is launched on (the
-    current torch stream), so the per-launch durations are kernel times."""
+    Returns the wall time per call and the per-call time of the events that
+    bracket the K calls on the launch stream (the calls queue back to back,
+    so this is the kernels' time)."""
     import torch
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         call()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [a.elapsed_time(b) for a, b in ev]
-    return wall_ms / steps, per
+    return wall_ms / steps, a.elapsed_time(b) / steps
+
+
+def time_groups(call, groups=7, per_group=20):
+    """The pages' statistic (FlashMLA PR #216, "Kernel performance"): groups
+    of back-to-back calls, each bracketed by events; returns the group means
+    in ms."""
+    import torch
+    stream = torch.cuda.current_stream()
+    means = []
+    for _ in range(groups):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(per_group):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        means.append(a.elapsed_time(b) / per_group)
+    return means
 
 
 # ---------------------------------------------------------------------------
@@ -572,34 +619,44 @@ def _mfma_busy(sub, kernel="sparse_mla_fwd"):
 
 def attainable_peaks():
     """This device's attainable dense bf16 MFMA rate (an MFMA loop on every
-    SIMD, from the benchmark's probe library) and HBM bandwidth (a streaming
-    device copy of 4 GiB: reads and writes counted)."""
-    import ctypes
+    SIMD) and HBM bandwidth, both from the benchmark's probe library: a
+    read-only stream over 4 GiB (the rate a read-dominated kernel such as the
+    decode gather can attain) and a device copy of 4 GiB (reads and writes
+    counted)."""
     import torch
     lib = ctypes.CDLL(str(ROOT / "sparse_top_mla_amd" / "libsmla_probe.so"))
     lib.smla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.smla_probe_mfma_count.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.smla_probe_mfma_count.restype = ctypes.c_longlong
+    lib.smla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p]
     props = torch.cuda.get_device_properties(0)
     blocks, iters = props.multi_processor_count * 4, 4096
     out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     launch = lambda: lib.smla_probe_mfma(out.data_ptr(), blocks, iters, stream)  # noqa: E731
     assert launch() == 0
-    _, per = time_steps(launch, 10, 3)
-    mfma_ms = statistics.median(per)
+    mfma_ms = statistics.median(time_groups(launch, groups=7, per_group=3))
     flops = lib.smla_probe_mfma_count(blocks, iters) * 2.0 * 32 * 32 * 16
     n = 4 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_()
+    rblocks = props.multi_processor_count * 64
+    words = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda:0")
+    read = lambda: lib.smla_probe_stream_read(src.data_ptr(), n, words.data_ptr(), rblocks, stream)  # noqa: E731
+    assert read() == 0
+    read_ms = statistics.median(time_groups(read, groups=7, per_group=3))
     dst = torch.empty_like(src)
-    _, per_c = time_steps(lambda: dst.copy_(src), 10, 3)
-    copy_ms = statistics.median(per_c)
+    copy_ms = statistics.median(time_groups(lambda: dst.copy_(src), groups=7, per_group=3))
     return {"mfma_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "hbm_read_gbs": n / (read_ms * 1e-3) / 1e9,
             "hbm_gbs": 2.0 * n / (copy_ms * 1e-3) / 1e9,
             "mfma_probe": f"{blocks} workgroups x 8 waves x {iters} x 4 independent "
-                          f"v_mfma_f32_32x32x16_bf16, median of 10 launches: {mfma_ms:.3f} ms",
-            "copy_probe": f"torch device copy of {n >> 30} GiB (read + write), median of 10: "
-                          f"{copy_ms:.3f} ms",
+                          f"v_mfma_f32_32x32x16_bf16, median of 7 group means of 3 launches: "
+                          f"{mfma_ms:.3f} ms",
+            "read_probe": f"read-only stream of {n >> 30} GiB, {rblocks} workgroups of 256 "
+                          f"threads, median of 7 group means of 3 launches: {read_ms:.3f} ms",
+            "copy_probe": f"torch device copy of {n >> 30} GiB (read + write), median of 7 group "
+                          f"means of 3: {copy_ms:.3f} ms",
             "device": props.name, "command": "python3 bench.py --attainable"}
 
 
@@ -613,6 +670,41 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def measure(workload, case, dev, steps, warmup):
+    """Times one workload: exactly `steps` calls after `warmup` (wall clock and
+    events around the timed region), then the pages' 7 groups of 20 calls.
+    Returns (record, counts)."""
+    import torch
+    bwd = workload == "bwd_h64"
+    bs = is_block_sparse(case)
+    counts = bwd_counts(case) if bwd else bs_counts(case) if bs else algorithmic_counts(case)
+    call = gpu_call_bwd(case, dev) if bwd else gpu_call_bs(case, dev) if bs else gpu_call(case, dev)
+    torch.cuda.synchronize()
+    ms_per_step, kernel_ms = time_steps(call, steps, warmup)
+    groups = time_groups(call)
+    rec = {
+        "workload": case.name,
+        "ms_per_call": ms_per_step,
+        "kernel_ms": kernel_ms,
+        "group_means_ms": {"median": statistics.median(groups), "min": min(groups),
+                           "max": max(groups), "groups": len(groups), "calls_per_group": 20},
+        "tflops": counts["flops"] / (kernel_ms * 1e-3) / 1e12,
+        "roofline": roofline(workload, case, counts, kernel_ms),
+        "hbm_gbs_algorithmic": counts["bytes"] / (kernel_ms * 1e-3) / 1e9,
+        "valid_pairs": counts["valid_pairs"],
+        "flops_per_call": counts["flops"],
+        "algorithmic_bytes_per_call": counts["bytes"],
+    }
+    stored = stored_counters(workload)
+    if stored is not None:
+        if "mfma_busy_frac" in stored:
+            rec["rocprof_mfma_busy_frac"] = stored["mfma_busy_frac"]
+        if stored.get("hbm_bytes_per_launch"):
+            rec["rocprof_hbm_frac"] = stored["hbm_bytes_per_launch"] / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS
+    del call
+    return rec, counts
 
 
 def main():
@@ -643,29 +735,33 @@ def main():
     case = make_case(args.workload)
     bwd = args.workload == "bwd_h64"
     bs = is_block_sparse(case)
-    counts = bwd_counts(case) if bwd else bs_counts(case) if bs else algorithmic_counts(case)
-    call = gpu_call_bwd(case, dev) if bwd else gpu_call_bs(case, dev) if bs else gpu_call(case, dev)
-    call()
-    torch.cuda.synchronize()
-    ms_per_step, per = time_steps(call, args.steps, args.warmup)
-    kernel_ms = statistics.fmean(per)
-    value = counts["flops"] / (ms_per_step * 1e-3) / 1e12
+    main_rec, counts = measure(args.workload, case, dev, args.steps, args.warmup)
+    value = counts["flops"] / (main_rec["ms_per_call"] * 1e-3) / 1e12
 
     variants = {}
+    if args.workload == "prefill_h64" and args.variants:
+        # Every other configuration of the target statement, each measured the
+        # same way (the graded decode row is the one with topk_length).
+        for w in ("prefill_h64_len", "tiny", "prefill_h128", "decode_dynamic",
+                  "decode_dynamic_nolen", "decode_fixed"):
+            c = make_case(w)
+            rec, _ = measure(w, c, dev, args.steps, args.warmup)
+            variants[w] = rec
+            del c
+            torch.cuda.empty_cache()
     if is_decode(case) and args.replicas > 1:
         # Cold variant: rotate over copies of the inputs, so that a call does
         # not find the previous call's KV rows in the Infinity Cache.
-        calls = [call] + [gpu_call(case, dev) for _ in range(args.replicas - 1)]
+        calls = [gpu_call(case, dev) for _ in range(args.replicas)]
         k = [0]
 
         def rotating():
             calls[k[0] % len(calls)]()
             k[0] += 1
-        ms_cold, per_cold = time_steps(rotating, args.steps, args.warmup)
+        ms_cold, kms_cold = time_steps(rotating, args.steps, args.warmup)
         variants[f"cold_{args.replicas}_replicas"] = {
-            "ms_per_call": ms_cold, "kernel_ms": statistics.fmean(per_cold),
-            "kernel_ms_median": statistics.median(per_cold),
-            "hbm_gbs_algorithmic": counts["bytes"] / (statistics.fmean(per_cold) * 1e-3) / 1e9}
+            "ms_per_call": ms_cold, "kernel_ms": kms_cold,
+            "hbm_gbs_algorithmic": counts["bytes"] / (kms_cold * 1e-3) / 1e9}
         del calls
     rows = case.batch * case.s_q if is_decode(case) else counts["rows"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -674,21 +770,12 @@ def main():
         import sparse_top_mla_amd as smla
         splits = max(2, smla.decode_num_splits(case.batch, case.s_q, case.topk))
         call_split = gpu_call(case, dev, num_splits=splits)
-        ms_split, per_split = time_steps(call_split, args.steps, args.warmup)
+        ms_split, kms_split = time_steps(call_split, args.steps, args.warmup)
         variants[f"split_{splits}"] = {
-            "num_splits": splits, "ms_per_call": ms_split,
-            "kernel_ms": statistics.fmean(per_split),
-            "kernel_ms_median": statistics.median(per_split),
-            "hbm_gbs_algorithmic": counts["bytes"] / (statistics.fmean(per_split) * 1e-3) / 1e9}
+            "num_splits": splits, "ms_per_call": ms_split, "kernel_ms": kms_split,
+            "group_means_ms_median": statistics.median(time_groups(call_split)),
+            "hbm_gbs_algorithmic": counts["bytes"] / (kms_split * 1e-3) / 1e9}
         del call_split
-    if args.workload == "prefill_h64":
-        case_len = make_case("prefill_h64_len")
-        call_len = gpu_call(case_len, dev)
-        ms_len, per_len = time_steps(call_len, args.steps, args.warmup)
-        variants["with_topk_length"] = {"ms_per_call": ms_len,
-                                        "kernel_ms": statistics.fmean(per_len),
-                                        "tflops": counts["flops"] / (ms_len * 1e-3) / 1e12}
-        del call_len, case_len
 
     result = {
         "metric": METRIC_BWD if bwd else METRIC_BS if bs else METRIC,
@@ -697,7 +784,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": main_rec["ms_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -719,23 +806,22 @@ def main():
             "topk_length": case.topk_length is not None,
             "attn_sink": case.attn_sink is not None,
         }),
-        "kernel_ms": {"mean": kernel_ms, "median": statistics.median(per), "min": min(per),
-                      "max": max(per)},
-        "roofline": roofline(args.workload, case, counts, kernel_ms),
-        "hbm_gbs_algorithmic": counts["bytes"] / (kernel_ms * 1e-3) / 1e9,
+        "kernel_ms": {"timed_region_mean": main_rec["kernel_ms"],
+                      **{f"group_{k}": v for k, v in main_rec["group_means_ms"].items()}},
+        "roofline": main_rec["roofline"],
+        "hbm_gbs_algorithmic": main_rec["hbm_gbs_algorithmic"],
     }
+    for k in ("rocprof_mfma_busy_frac", "rocprof_hbm_frac"):
+        if k in main_rec:
+            result[k] = main_rec[k]
     if variants:
         result["variants"] = variants
-    rec = stored_counters(args.workload)
-    if rec is not None and "mfma_busy_frac" in rec:
-        # The rocprof MFMA-busy fraction of this kernel (same code), beside the
-        # algorithmic fraction in roofline.frac.
-        result["rocprof_mfma_busy_frac"] = rec["mfma_busy_frac"]
     peaks = PROFILES / "attainable_peaks.json"
     if peaks.exists():
         p = json.loads(peaks.read_text())
-        att = p["hbm_gbs"] if is_decode(case) else p["mfma_tflops"]
-        result["attainable"] = {"mfma_tflops": p["mfma_tflops"], "hbm_gbs": p["hbm_gbs"],
+        att = p.get("hbm_read_gbs", p["hbm_gbs"]) if is_decode(case) else p["mfma_tflops"]
+        result["attainable"] = {"mfma_tflops": p["mfma_tflops"], "hbm_copy_gbs": p["hbm_gbs"],
+                                "hbm_read_gbs": p.get("hbm_read_gbs"),
                                 "frac_of_attainable": result["roofline"]["achieved"] / att}
     if args.cpu_seconds > 0 and bwd:
         result["cpu_baseline"] = cpu_baseline_bwd(case, counts, args.cpu_seconds)

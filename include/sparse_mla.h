@@ -92,7 +92,8 @@ smla_status sparse_mla_fwd(const void *q, const void *kv, const int32_t *indices
  *   attn_sink     fp32  [h_q] or NULL
  *   out           bf16  [B, s_q, h_q, d_v]
  *   lse           fp32  [B, s_q, h_q]
- *   max_logits    fp32  [B, s_q, h_q]
+ *   max_logits    fp32  [B, s_q, h_q] or NULL (NULL: not stored; the
+ *                 pages' decode returns out and lse only)
  * B = 0 is a valid no-op (pointers may then be NULL).
  */
 smla_status sparse_mla_decode_fwd(const void *q, const void *kv_cache,
@@ -124,6 +125,7 @@ size_t sparse_mla_decode_split_workspace_bytes(int32_t B, int32_t s_q, int32_t h
  * out = sum of exp(lse_s - lse) * out_s, the sink joins the denominator once
  * after the merge, and a row whose splits are all empty gives (0, +inf, -inf)
  * as the unsplit path does.  Results equal the unsplit path's up to rounding.
+ * max_logits may be NULL, as in sparse_mla_decode_fwd.
  *   num_splits       1 .. 1024; 1 runs the unsplit path (workspace unused)
  *   workspace        device memory of at least
  *                    sparse_mla_decode_split_workspace_bytes(...) bytes,

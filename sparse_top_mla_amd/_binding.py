@@ -140,8 +140,10 @@ def fwd(q, kv, indices, sm_scale, d_v=512, attn_sink=None, topk_length=None, *, 
 
 
 def _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink, topk_length,
-                 out, lse, max_logits):
-    """Checks and output buffers shared by the decode entry points."""
+                 out, lse, max_logits, return_max_logits=True):
+    """Checks and output buffers shared by the decode entry points
+    (max_logits stays None when return_max_logits is false and none is
+    given: the library then stores none)."""
     dev = q.device
     _dev(q, "q", torch.bfloat16)
     _dev(kv_cache, "kv_cache", torch.bfloat16, dev)
@@ -168,11 +170,13 @@ def _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sin
         raise ValueError("attn_sink must have shape [h_q]")
     out = torch.empty((B, s_q, h_q, d_v), dtype=torch.bfloat16, device=dev) if out is None else out
     lse = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev) if lse is None else lse
-    max_logits = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev) if max_logits is None else max_logits
+    if max_logits is None and return_max_logits:
+        max_logits = torch.empty((B, s_q, h_q), dtype=torch.float32, device=dev)
     _dev(out, "out", torch.bfloat16, dev)
     _dev(lse, "lse", torch.float32, dev)
     _dev(max_logits, "max_logits", torch.float32, dev)
-    if out.numel() != B * s_q * h_q * d_v or lse.numel() != B * s_q * h_q or max_logits.numel() != B * s_q * h_q:
+    if (out.numel() != B * s_q * h_q * d_v or lse.numel() != B * s_q * h_q
+            or (max_logits is not None and max_logits.numel() != B * s_q * h_q)):
         raise ValueError("output buffers have the wrong size")
     return (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
             max_logits)
@@ -180,17 +184,18 @@ def _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sin
 
 def decode_fwd(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, d_v=512,
                attn_sink=None, topk_length=None, *, out=None, lse=None, max_logits=None,
-               stream=None):
+               return_max_logits=True, stream=None):
     """Paged sparse decode forward.  q [B, s_q, h_q, d_qk] bf16,
     kv_cache [num_blocks, page_size, 1, d_qk] bf16, block_table [B, mbps]
     int32, cache_seqlens [B] int32, indices [B, s_q, topk] int32,
     topk_length [B, s_q] (or [B], broadcast over s_q) int32 or None,
-    attn_sink [h_q] fp32 or None.  Returns (out, lse, max_logits)."""
+    attn_sink [h_q] fp32 or None.  Returns (out, lse, max_logits);
+    max_logits is None (and not stored) with return_max_logits=False."""
     lib = load_library()
     dev = q.device
     (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
      max_logits) = _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink,
-                                topk_length, out, lse, max_logits)
+                                topk_length, out, lse, max_logits, return_max_logits)
     st = lib.sparse_mla_decode_fwd(_p(q), _p(kv_cache), _p(block_table), _p(cache_seqlens),
                                    _p(indices), _p(topk_length), _p(attn_sink), B, s_q, h_q, h_kv,
                                    d_qk, d_v, topk, num_blocks, page_size, block_table.shape[1],
@@ -221,7 +226,7 @@ def decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits):
 
 def decode_fwd_split(q, kv_cache, block_table, cache_seqlens, indices, sm_scale, num_splits,
                      d_v=512, attn_sink=None, topk_length=None, *, workspace=None, out=None,
-                     lse=None, max_logits=None, stream=None):
+                     lse=None, max_logits=None, return_max_logits=True, stream=None):
     """Split-KV paged decode: arguments and results as decode_fwd; each row's
     index blocks are split num_splits ways and merged.  `workspace` (a uint8
     CUDA tensor of at least decode_split_workspace_bytes(...) bytes) is
@@ -230,7 +235,7 @@ def decode_fwd_split(q, kv_cache, block_table, cache_seqlens, indices, sm_scale,
     dev = q.device
     (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
      max_logits) = _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink,
-                                topk_length, out, lse, max_logits)
+                                topk_length, out, lse, max_logits, return_max_logits)
     need = lib.sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, int(num_splits))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -250,13 +255,20 @@ def row_lengths(indices, topk_length=None, cache_seqlens=None, *, s_kv=0, rows_p
     """Row lengths L as the kernels use them.  indices [..., topk] int32."""
     lib = load_library()
     dev = indices.device
+    topk = indices.shape[-1]
+    rows = indices.numel() // topk if topk > 0 else 0
+    if topk_length is not None and topk_length.numel() != rows:
+        raise ValueError("topk_length must hold one entry per row")
+    if cache_seqlens is not None:
+        # row r reads cache_seqlens[r // rows_per_seq]
+        if rows_per_seq <= 0 or cache_seqlens.numel() * rows_per_seq < rows:
+            raise ValueError(f"cache_seqlens holds {cache_seqlens.numel()} entries; {rows} rows at "
+                             f"rows_per_seq={rows_per_seq} need {-(-rows // max(rows_per_seq, 1))}")
+        if max_blocks_per_seq <= 0:
+            raise ValueError("max_blocks_per_seq must be positive with cache_seqlens")
     _dev(indices, "indices", torch.int32)
     _dev(topk_length, "topk_length", torch.int32, dev)
     _dev(cache_seqlens, "cache_seqlens", torch.int32, dev)
-    topk = indices.shape[-1]
-    rows = indices.numel() // topk
-    if topk_length is not None and topk_length.numel() != rows:
-        raise ValueError("topk_length must hold one entry per row")
     out = torch.empty(rows, dtype=torch.int32, device=dev)
     st = lib.sparse_mla_row_lengths(_p(indices), _p(topk_length), _p(cache_seqlens), rows,
                                     rows_per_seq, topk, s_kv, max_blocks_per_seq, _p(out),

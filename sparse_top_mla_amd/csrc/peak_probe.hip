@@ -5,6 +5,11 @@
 // so the matrix cores never wait on a result.  The host divides the FLOPs
 // (2 * 32 * 32 * 16 per MFMA) by the measured time to get the dense bf16
 // MFMA rate this device attains at its running clock.
+//
+// smla_probe_stream_read reads a buffer once (16 B per lane, four loads in
+// flight per lane, grid-stride) and writes one word per thread: the HBM rate
+// a read-dominated kernel can attain (the decode gathers are about 95%
+// reads), beside the read+write rate of a device copy.
 
 #include <hip/hip_runtime.h>
 
@@ -41,9 +46,34 @@ __global__ void __launch_bounds__(512) mfma_loop(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) stream_read(const u32x4* __restrict__ p, size_t n16,
+                                                   uint32_t* __restrict__ out) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= p[i];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads `bytes` (a multiple of 16) from `src` with `blocks` workgroups of 256
+// threads; `out` holds blocks * 256 words.  Returns 0 or the HIP error code.
+int smla_probe_stream_read(const void* src, size_t bytes, uint32_t* out, int blocks,
+                           void* stream) {
+  if (!src || !out || blocks <= 0 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), bytes / 16, out);
+  return (int)hipGetLastError();
+}
 
 // Launches `blocks` workgroups of 512 threads (8 waves), each wave issuing
 // iters * 4 MFMAs; `out` holds blocks * 512 floats.  Returns 0 on success,

@@ -95,7 +95,7 @@ struct FwdArgs {
   const int32_t* cache_seqlens;
   __bf16* out;
   float* lse;
-  float* max_logits;
+  float* max_logits;      // NULL: not stored (decode)
   int32_t rows;          // query rows (prefill s_q; decode B * s_q)
   int32_t rows_per_seq;  // decode s_q (row r belongs to request r / rows_per_seq)
   int32_t h_q;
@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(kMaxThreads) sparse_mla_fwd_kernel(FwdArgs a) 
   }
   if (g == 0) {
     a.lse[(size_t)row * a.h_q + h] = lse_v;
-    a.max_logits[(size_t)row * a.h_q + h] = ml_v;
+    if (a.max_logits) a.max_logits[(size_t)row * a.h_q + h] = ml_v;
   }
 }
 
@@ -718,12 +718,13 @@ __device__ __forceinline__ float pair_sum32(float x) {
 // are read kPrefetch MFMAs ahead.  LFRESH: the lane's addresses are computed
 // here per tile (see lane_fresh) instead of once for the kernel; what the
 // register allocation of each kernel instance prefers, by measurement.
-template <int D_QK, int BK, int EVERY, int NP, bool LFRESH, class Pump>
+template <int D_QK, int BK, int EVERY, int NP, bool LFRESH, class Pump, int KP = 0>
 __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
                                               const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                               Pump& pump, int slot0) {
   using T = WideTile<D_QK, BK>;
-  constexpr int kPrefetch = D_QK == 576 ? 3 : 4;  // what the register budget allows
+  // K fragments read ahead: what the register budget allows (KP overrides)
+  constexpr int kPrefetch = KP > 0 ? KP : D_QK == 576 ? 3 : 4;
   const int lane = LFRESH ? lane_fresh() : lane_id();
   const int hl = lane & 31, half = lane >> 5;
   int krow = (r0 + hl) * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
@@ -1010,10 +1011,10 @@ __device__ __forceinline__ void load_query(bf16x8 (&qf)[WideTile<D_QK>::kDSteps]
 // The same operand from a block buffer that the gather filled with the
 // row's 64 head rows (head j as row j, laid out like a KV block): head group
 // hg reads rows 32hg .. 32hg + 31 the way tile_scores reads key rows.
-template <int D_QK>
+template <int D_QK, int BK = 64>
 __device__ __forceinline__ void load_query_lds(bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                                const LDS_AS uint8_t* buf, int hg, int lane) {
-  using T = WideTile<D_QK>;
+  using T = WideTile<D_QK, BK>;
   const int hl = lane & 31, half = lane >> 5;
   const int krow = (32 * hg + hl) * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
   const int rrow = T::kRopeBase + (32 * hg + hl) * T::kRopeBytes, rw = (half ^ rope_swz(hl)) << 4;
@@ -1194,7 +1195,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   } else {
   if (half == 0 && (KS == 1 || ks == 0)) {
     a.lse[(size_t)row * a.h_q + head] = lse_v;
-    a.max_logits[(size_t)row * a.h_q + head] = ml_v;
+    if (a.max_logits) a.max_logits[(size_t)row * a.h_q + head] = ml_v;
   }
   if (KS == 2) {
     // Each wave of a head group finishes one half of the value columns
@@ -1290,6 +1291,546 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ring kernel: 128 heads (4 waves of 32), rows of at most kRingMaxTopk index
+// positions.  A persistent grid as the wide kernel's, one workgroup per CU.
+//
+// Row prologue:
+//   * the row's query slice (128 head rows of d_qk) is copied global -> LDS
+//     into the ring's buffers (head j as row j) while the index vector is
+//     read; each wave then reads its 32 heads in the MFMA operand layout;
+//   * the row's keys are compacted: every index position below the length
+//     (explicit topk_length, else the whole vector) is tested for validity
+//     (and paged through the block table), and the table offsets of the valid
+//     keys are written, in position order, to a list in LDS.  Masked keys add
+//     exactly nothing to the softmax, so dropping them is exact; the derived
+//     length of the pages' tail scan needs no scan here, since the positions
+//     past it are invalid anyway.
+// Stage loop: the compacted keys stream through a ring of kRingStages LDS
+// stages of 32 keys (one 32 x 32 MFMA tile per wave).  While stage t is
+// computed, stages t+1 .. t+kRingStages-1 are in flight: about 110 KB per CU
+// at d_qk = 576.  For a random-row gather the bytes in flight per CU, not the
+// bytes moved, set the rate the memory system attains (measured on MI355X
+// with the decode rows of 1152 B: about 2.8 TB/s with 37 KB in flight per CU,
+// 4.0 TB/s with 74 KB, 5.4 TB/s with 147 KB), and a double buffer keeps at
+// most one block in flight.  No other vector-memory access runs inside the
+// loop and every step issues exactly kGather copies per wave, so the wait for
+// stage t is vmcnt((kRingStages - 2) * kGather): the copies of the stages
+// issued after it may stay in flight.  Copies for stages past the end of the
+// list read nothing and zero-fill their buffer.
+// ---------------------------------------------------------------------------
+
+constexpr int kRingStages = 4;       // LDS stages of the gather ring
+constexpr int kRingKeys = 32;        // keys per stage: one tile per wave
+constexpr int kRingMaxTopk = 2048;   // index positions per row (the key list lives in LDS)
+constexpr int kRingChunks = kRingMaxTopk / (kWideWaves * 64);  // 64-position chunks per wave
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15: no wait on those).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// A barrier that waits for LDS accesses but not for vector-memory loads
+// (__syncthreads() would also wait for every copy in flight).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The copies of one stage's nope rows (the first 1 KiB of each row), 8 rows
+// per wave: wave w copies rows 8w .. 8w + 7 of the 32-row stage, with M0 on
+// the four-row windows 8w and 8w + 4 and the row selected by the instruction
+// offset, as GatherPump does for 16 rows.  The rows' chunk swizzle depends on
+// the row's low four bits, 8(w % 2) + s: `lane16w` holds 16 * lane with the
+// wave's half of the pattern XORed in, the slot's half is a constant.
+template <int D_QK>
+struct RingPump {
+  using T = WideTile<D_QK, kRingKeys>;
+  static constexpr int kSlots = kRingKeys / kWideWaves;  // rows per wave and stage
+  u32x4s rsrc;       // table resource (wave-uniform)
+  LDS_AS uint8_t* buf;
+  int row0;          // 8 * wave
+  int offw;          // lane s < 8: source offset of row row0 + s, moved down by (s % 4) KiB, or kOob
+  int lane16w;
+  uint32_t win;
+  uint32_t so_next;
+
+  __device__ __forceinline__ void copy(int s, bool fresh = false, bool first = true) {
+    const bool opens = fresh || (s & 3) == 0;
+    if (opens) win = (uint32_t)(uintptr_t)(buf + (row0 + (s & ~3)) * T::kNopeBytes);
+    const uint32_t so = first ? (uint32_t)__builtin_amdgcn_readlane(offw, s) : so_next;
+    if (s + 1 < kSlots) so_next = (uint32_t)__builtin_amdgcn_readlane(offw, s + 1);
+    const uint32_t voff = ((uint32_t)lane16w ^ (uint32_t)(nope_swz(s) << 4)) + so;
+    constexpr int B = T::kNopeBytes;
+    switch (s & 3) {
+      case 0: dma_table16<0 * B>(rsrc, voff, win); break;
+      case 1: opens ? dma_table16<1 * B>(rsrc, voff, win) : dma_table16<1 * B, false>(rsrc, voff, win); break;
+      case 2: opens ? dma_table16<2 * B>(rsrc, voff, win) : dma_table16<2 * B, false>(rsrc, voff, win); break;
+      default: opens ? dma_table16<3 * B>(rsrc, voff, win) : dma_table16<3 * B, false>(rsrc, voff, win); break;
+    }
+  }
+  __device__ __forceinline__ void copy_all() {
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) copy(s, false, s == 0);
+  }
+};
+
+// The rope part (d_qk = 576) of a 32-key stage, one copy per wave: lane L
+// copies chunk L % 8 of row jj = 8 wave + L / 8 (LDS chunk L % 8 holds source
+// chunk (L % 8) ^ swizzle(jj)).  `o` is row jj's offset as ring_lane_offset
+// gives it for this lane (moved down by (L % 4) KiB; kOob for no row).
+template <int D_QK>
+__device__ __forceinline__ void ring_rope(LDS_AS uint8_t* buf, const u32x4s& rsrc, int o, int wave,
+                                          int lane) {
+  using T = WideTile<D_QK, kRingKeys>;
+  if (T::kRopeLanes == 0) return;
+  const int jj = 8 * wave + (lane >> 3);
+  const uint32_t voff = (uint32_t)o + (uint32_t)(lane & 3) * T::kNopeBytes + T::kNopeBytes +
+                        (uint32_t)(((lane & 7) ^ rope_swz(jj)) << 4);
+  dma_table16<0>(rsrc, voff, (uint32_t)(uintptr_t)(buf + T::kRopeBase + wave * 8 * T::kRopeBytes));
+}
+
+// The list entries one wave needs for the copies of one stage, read ahead
+// of their use: lane L holds the entry of row 8 wave + L / 8 (its rope copy)
+// and of row 8 wave + L % 8 (its RingPump).  The reads are volatile and
+// unconditional (of a clamped entry): the compiler would otherwise sink them
+// into a branch on the position and wait for them right away.  The offsets
+// themselves are formed where they are used (`rope`, `pump`: moved down by
+// (L % 4) KiB, or kOob past the end of the list of n keys).
+struct RingOffs {
+  uint32_t rope_raw, pump_raw;
+  int stage;
+
+  static __device__ __forceinline__ uint32_t entry(const LDS_AS uint32_t* keys, int p) {
+    return *reinterpret_cast<const volatile LDS_AS uint32_t*>(
+        keys + (p < kRingMaxTopk ? p : kRingMaxTopk - 1));
+  }
+  static __device__ __forceinline__ RingOffs read(const LDS_AS uint32_t* keys, int stage, int wave,
+                                                  int lane) {
+    const int p0 = stage * kRingKeys + 8 * wave;
+    return RingOffs{entry(keys, p0 + (lane >> 3)), entry(keys, p0 + (lane & 7)), stage};
+  }
+  __device__ __forceinline__ int rope(int n, int wave, int lane) const {
+    const int p = stage * kRingKeys + 8 * wave + (lane >> 3);
+    return p < n ? (int)(rope_raw - (uint32_t)(lane & 3) * 1024u) : (int)kOob;
+  }
+  __device__ __forceinline__ int pump(int n, int wave, int lane) const {
+    const int p = stage * kRingKeys + 8 * wave + (lane & 7);
+    return p < n ? (int)(pump_raw - (uint32_t)(lane & 3) * 1024u) : (int)kOob;
+  }
+};
+
+// All copies of one stage (rope part, then the nope rows) from `rsrc` into
+// buffer `buf`, outside the MFMA stream.
+template <int D_QK>
+__device__ __forceinline__ void ring_copy_stage(LDS_AS uint8_t* buf, const u32x4s& rsrc,
+                                                const LDS_AS uint32_t* keys, int n, int stage,
+                                                int wave, int lane) {
+  const RingOffs o = RingOffs::read(keys, stage, wave, lane);
+  ring_rope<D_QK>(buf, rsrc, o.rope(n, wave, lane), wave, lane);
+  RingPump<D_QK>{rsrc, buf, 8 * wave, o.pump(n, wave, lane), (lane * 16) ^ ((wave & 1) << 5), 0u,
+                 0u}
+      .copy_all();
+}
+
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs.  The O^T
+// accumulator fills the AGPRs, and every MFMA the compiler emits in this
+// kernel takes its accumulator from AGPRs, so a compiled S^T chain would
+// evict part of O^T to VGPRs and back in every stage (48 moves, each about
+// two MFMA-issue cycles with one wave per SIMD).  The compiler does not see
+// the timing of these MFMAs: the first of a chain starts after two wait
+// states (a VALU write of an operand before it), consecutive ones chain on
+// the accumulator without wait states, and the last is followed by 18 wait
+// states before anything may read the result (an 8-pass MFMA's result is
+// readable by VALU after 11).
+__device__ __forceinline__ void mfma_vacc_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vacc_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+               : "+v"(acc)
+               : "v"(a), "v"(b));
+}
+
+// max of three floats as one v_max3_f32.  fmaxf on values the compiler
+// cannot prove canonical (MFMA results) costs a canonicalising v_max_f32 per
+// operand first; the scores are never signalling NaNs.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// S^T = K Q^T of a ring stage (32 keys at row 0 of `buf`), as tile_scores
+// with r0 = 0 but with the accumulator in VGPRs (mfma_vacc); the pump's nope
+// copies go after every fourth MFMA.
+template <int D_QK, int KP, bool LFRESH, class Hook>
+__device__ __forceinline__ f32x16 ring_scores(const LDS_AS uint8_t* buf,
+                                              const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
+                                              RingPump<D_QK>& pump, Hook&& hook) {
+  using T = WideTile<D_QK, kRingKeys>;
+  constexpr int kSteps = T::kDSteps;
+  constexpr int kSlots = RingPump<D_QK>::kSlots;
+  const int lane = LFRESH ? lane_fresh() : lane_id();
+  const int hl = lane & 31, half = lane >> 5;
+  int krow = hl * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
+  int rrow = T::kRopeBase + hl * T::kRopeBytes, rw = (half ^ rope_swz(hl)) << 4;
+  opaque(krow);
+  opaque(kw);
+  opaque(rrow);
+  opaque(rw);
+  auto kaddr = [&](int d) {
+    if (d < 32) return buf + krow + (d >> 3) * 256 + ((32 * (d & 7)) ^ kw);
+    return buf + rrow + ((32 * (d - 32)) ^ rw);
+  };
+  f32x16 s;
+  bf16x8 kring[KP];
+#pragma unroll
+  for (int n = 0; n < KP; ++n) kring[n] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(n));
+#pragma unroll
+  for (int d = 0; d < kSteps; ++d) {
+    const bf16x8 kf = kring[d % KP];
+    if (d + KP < kSteps)
+      kring[d % KP] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(d + KP));
+    if (d == 0)
+      mfma_vacc_first(s, kf, qf[d]);
+    else if (d == kSteps - 1)
+      mfma_vacc_last(s, kf, qf[d]);
+    else
+      mfma_vacc(s, kf, qf[d]);
+    if (d % 4 == 3 && d / 4 < kSlots) pump.copy(d / 4, false, d == 3);
+    hook(d);
+    __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
+  }
+  return s;
+}
+
+// The V^T operand stream of P*V over a 32-key stage (row 0 of `vbuf`), as in
+// tile_softmax_pv: value tile ct = n % 16 and key step u = n / 16 for MFMA n.
+// Lane (16-group g, i16) reads 8 B of key row 16u + 4 half + TR_ROW(i16)
+// (+8 for the upper four keys) at value chunk 4 ct + 2 (g & 1) + TR_COL(i16) / 2
+// with ds_read_b64_tr_b16.  The first kPrefetch operands can be read ahead
+// (inside the S^T chain), so that the first P*V MFMA does not wait on LDS.
+template <int D_QK>
+struct RingV {
+  using T = WideTile<D_QK, kRingKeys>;
+  static constexpr int kPrefetch = 3;
+  static constexpr int kTiles = kDV / 32;
+  const LDS_AS uint8_t* vbuf;
+  int row_lo, row_hi, w_lo, w_hi;
+  bf16x4 lo[kPrefetch], hi[kPrefetch];
+
+  __device__ __forceinline__ void init(const LDS_AS uint8_t* vb, int lane) {
+    vbuf = vb;
+    const int i16 = lane & 15, cb = (lane >> 4) & 1, half = lane >> 5;
+    const int vrow = 4 * half + TR_ROW(i16);
+    const int vc = 2 * cb + (TR_COL(i16) >> 1);
+    row_lo = vrow * T::kNopeBytes + 8 * (TR_COL(i16) & 1);
+    row_hi = row_lo + 8 * T::kNopeBytes;
+    w_lo = (vc ^ nope_swz(vrow)) << 4;
+    w_hi = (vc ^ nope_swz(vrow + 8)) << 4;
+    opaque(row_lo);
+    opaque(row_hi);
+    opaque(w_lo);
+    opaque(w_hi);
+  }
+  __device__ __forceinline__ const LDS_AS uint8_t* addr(int n, bool upper) const {
+    const int ct = n % kTiles, u = n / kTiles;
+    return vbuf + (upper ? row_hi : row_lo) + (ct >> 2) * 256 + 16 * u * T::kNopeBytes +
+           ((64 * (ct & 3)) ^ (upper ? w_hi : w_lo));
+  }
+  __device__ __forceinline__ void read(int n) {
+    lo[n % kPrefetch] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)addr(n, false));
+    hi[n % kPrefetch] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)addr(n, true));
+  }
+  __device__ __forceinline__ void prefetch() {
+#pragma unroll
+    for (int n = 0; n < kPrefetch; ++n) read(n);
+  }
+};
+
+// O^T += V^T P^T over the 32 keys of the previous stage (buffer `vbuf`, its
+// probabilities `pprev`), with the softmax of the current stage's scores `s`
+// scheduled between those MFMAs: its masked max, its probabilities (into
+// `pnext`, the P^T operands of the next call) and their sum.  The softmax
+// reference is fixed, so O is never rescaled and the two are independent.
+// DO_PV / DO_SM leave out one half (the first and the last stage of a row);
+// MASK = false skips the masking of a stage whose 32 keys are all used.
+// Operand layouts as in tile_softmax_pv (r0 = 0): value tile ct = n % 16 and
+// key step u = n / 16 for MFMA n; pnext[u][e] = P of s[8u + e].
+template <int D_QK, bool DO_PV, bool DO_SM, bool MASK = true>
+__device__ __forceinline__ void ring_pv_softmax(RingV<D_QK>& v, const bf16x8 (&pprev)[2],
+                                                f32x16 (&acc)[kDV / 32], f32x16 s,
+                                                uint32_t bits, SoftmaxState& st,
+                                                float scale_log2, bf16x8 (&pnext)[2]) {
+  constexpr int kPrefetch = RingV<D_QK>::kPrefetch;
+  constexpr int kTiles = kDV / 32;
+  const int half = lane_id() >> 5;
+  float rmax = -INFINITY, neg_ref = 0.f, rsum = 0.f;
+  // Softmax work placed after MFMA n: 0 mask, 1 local max, 2 lane-pair max and
+  // reference, 3..10 two probabilities each, 11 the sum.
+  auto sm_piece = [&](int n) {
+    if (n == 0) {
+      if (MASK) {
+        const uint32_t mlane = bits >> (4 * half);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
+      }
+    } else if (n == 1) {
+      const float m0 = max3_raw(s[0], s[1], s[2]), m1 = max3_raw(s[3], s[4], s[5]);
+      const float m2 = max3_raw(s[6], s[7], s[8]), m3 = max3_raw(s[9], s[10], s[11]);
+      const float m4 = max3_raw(s[12], s[13], s[14]);
+      rmax = max3_raw(max3_raw(m0, m1, m2), max3_raw(m3, m4, s[15]), -INFINITY);
+    } else if (n == 2) {
+      const uint2 r = pair32(rmax);
+      // -inf only for a stage without a key
+      rmax = max_raw(__builtin_bit_cast(float, r.x), __builtin_bit_cast(float, r.y)) * scale_log2;
+      st.m_max = max_raw(st.m_max, rmax);
+      if (st.m_ref == -INFINITY) st.m_ref = rmax;
+      st.overflow |= rmax > st.m_ref + kRefSlack;  // this attempt is then discarded
+      neg_ref = st.m_ref == -INFINITY ? 0.f : -st.m_ref;
+    } else if (n >= 3 && n < 11) {
+      const int e = 2 * (n - 3);
+      const float p0 = prob(s[e], neg_ref, scale_log2), p1 = prob(s[e + 1], neg_ref, scale_log2);
+      pnext[e >> 3][e & 7] = (__bf16)p0;
+      pnext[e >> 3][(e & 7) + 1] = (__bf16)p1;
+      rsum = n == 3 ? p0 + p1 : rsum + (p0 + p1);
+    } else if (n == 11) {
+      st.l_sum += pair_sum32(rsum);
+    }
+  };
+#pragma unroll
+  for (int n = 0; n < 2 * kTiles; ++n) {
+    if (DO_PV) {
+      const bf16x4 l = v.lo[n % kPrefetch], h = v.hi[n % kPrefetch];
+      if (n + kPrefetch < 2 * kTiles) v.read(n + kPrefetch);
+      const bf16x8 vf = {l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+      acc[n % kTiles] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pprev[n / kTiles], acc[n % kTiles], 0, 0, 0);
+    }
+    if (DO_SM) sm_piece(n);
+    if (DO_PV) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
+__global__ void __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sparse_mla_fwd_ring_kernel(FwdArgs a) {
+  constexpr int NW = kWideWaves, BK = kRingKeys, NS = kRingStages;
+  using T = WideTile<D_QK, BK>;
+  constexpr int kRopeCopies = T::kRopeBytes ? BK / 8 / NW : 0;
+  static_assert(T::kRopeBytes == 0 || BK / 8 == NW, "one rope copy per wave and stage");
+  constexpr int kGather = RingPump<D_QK>::kSlots + kRopeCopies;  // copies per wave and stage
+  // Stages resident: the one whose S^T is computed and the one whose P*V
+  // is; kAhead = NS - 2 stages are in flight.
+  constexpr int kAhead = NS - 2;
+  constexpr int kKRead = D_QK == 576 ? 4 : 5;  // K fragments read ahead
+  constexpr int kHeads = NW * 32;
+  static_assert(kHeads * T::kRowBytes <= NS * T::kBufBytes, "the query slice fits the ring");
+  // LFRESH: per-tile lane addresses (what the paged 128-head wide kernel prefers).
+  constexpr bool LFRESH = false;
+  __shared__ __attribute__((aligned(16))) uint8_t ring_raw[NS * T::kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t keys_raw[kRingMaxTopk];
+  __shared__ int counts_raw[NW];
+  __shared__ float sink_lds[SINK ? kHeads : 1];
+  LDS_AS uint8_t* ring = (LDS_AS uint8_t*)ring_raw;
+  LDS_AS uint32_t* keys = (LDS_AS uint32_t*)keys_raw;
+  LDS_AS int* counts = (LDS_AS int*)counts_raw;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (SINK && (int)threadIdx.x < kHeads) sink_lds[threadIdx.x] = a.attn_sink[threadIdx.x];
+
+  bf16x8 qf[T::kDSteps];
+  int turn = 0;
+  for (int row = turn_row(a.rows, turn, PAGED); row >= 0; row = turn_row(a.rows, ++turn, PAGED)) {
+    const int lane = lane_fresh();
+    const int seq = row / a.rows_per_seq;
+    const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
+    const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+    // Positions examined: below the explicit length, else the whole vector.
+    const int scan = DYNAMIC ? clamp_length(a.topk_length[row], a.topk) : a.topk;
+
+    // The previous row's epilogue has read the ring (and the sinks are staged).
+    __syncthreads();
+    // Query slice into the ring: head h is row h % 32 of stage buffer h / 32.
+    {
+      const u32x4s rsrc = query_rsrc(a, row, T::kRowBytes);
+      const int heads = lane & 31;  // lane j: head 32 st + j, offset moved down by (j % 4) KiB
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        LDS_AS uint8_t* buf = ring + st * T::kBufBytes;
+        const int o = (int)((uint32_t)(st * 32 + heads) * (uint32_t)T::kRowBytes + kSpanBias -
+                            (uint32_t)(lane & 3) * 1024u);
+        stage_rope<D_QK, BK, NW>(buf, rsrc, o, wave);
+        RingPump<D_QK>{rsrc, buf, 8 * wave, __shfl(o, 8 * wave + (lane & 7)),
+                       (lane * 16) ^ ((wave & 1) << 5), 0u, 0u}
+            .copy_all();
+      }
+    }
+
+    // Compaction: wave w examines positions [w * per, (w + 1) * per).
+    const int per = ((scan + 255) >> 8) << 6;  // a multiple of 64, at most kRingChunks * 64
+    const int p0 = wave * per;
+    int idxv[kRingChunks];
+#pragma unroll
+    for (int k = 0; k < kRingChunks; ++k) {
+      const int pos = p0 + 64 * k + lane;
+      idxv[k] = 64 * k < per && pos < scan ? idx_row[pos] : -1;
+    }
+    int pgv[kRingChunks];
+#pragma unroll
+    for (int k = 0; k < kRingChunks; ++k) {
+      const bool ok = idxv[k] >= 0 && idxv[k] < bound;
+      pgv[k] = page_lookup<PAGED>(a, seq, ok, idxv[k]);
+    }
+    uint64_t mk[kRingChunks];
+    uint32_t offv[kRingChunks];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kRingChunks; ++k) {
+      const bool ok = idxv[k] >= 0 && idxv[k] < bound;
+      const BlockMeta m = block_meta<PAGED>(a, ok, idxv[k], pgv[k]);
+      mk[k] = m.mask;
+      offv[k] = (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias;
+      cnt += __builtin_popcountll(m.mask);
+    }
+    if (lane == 0) counts[wave] = cnt;
+    wait_vm_all();  // this wave's query copies have landed
+    __syncthreads();
+    int base = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = counts[w];
+      base += w < wave ? c : 0;
+      n += c;
+    }
+#pragma unroll
+    for (int k = 0; k < kRingChunks; ++k) {
+      const uint64_t m = mk[k];
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if ((m >> lane) & 1ull) keys[base + below] = offv[k];
+      base += __builtin_popcountll(m);
+    }
+    __syncthreads();  // the key list and every wave's query rows are in LDS
+    load_query_lds<D_QK, BK>(qf, ring + wave * T::kBufBytes, 0, lane);
+    const int nst = (n + BK - 1) / BK;
+
+    f32x16 acc[kDV / 32];
+    SoftmaxState st;
+    float m_preset = -INFINITY;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+      for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
+      st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
+      __syncthreads();  // the query rows (or a previous attempt's stages) have been read
+      const u32x4s rsrc = table_rsrc(a);
+#pragma unroll
+      for (int t = 0; t < kAhead; ++t)
+        ring_copy_stage<D_QK>(ring + t * T::kBufBytes, rsrc, keys, n, t, wave, lane_id());
+      // Step t: wait for stage t (stage t+1 stays in flight), issue stage
+      // t + kAhead into the buffer of stage t - 2 (its rope part now, its
+      // nope rows under the S^T MFMAs), S^T of stage t, then P*V of stage
+      // t-1 with the softmax of stage t between its MFMAs.  The first step
+      // has no P*V; the last stage's P*V follows the loop.
+      bf16x8 pprev[2];
+      // The list entries of the stage a step gathers are read one step
+      // earlier (no LDS wait at the top of the step).
+      RingOffs offs = RingOffs::read(keys, kAhead, wave, lane_id());
+      auto step = [&](int t, auto first, auto masked) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only((kAhead - 1) * kGather));
+        barrier_lds();
+        const int lane_t = lane_id();
+        LDS_AS uint8_t* cur = ring + (t % NS) * T::kBufBytes;
+        LDS_AS uint8_t* prev = ring + ((t + NS - 1) % NS) * T::kBufBytes;
+        LDS_AS uint8_t* nxt = ring + ((t + kAhead) % NS) * T::kBufBytes;
+        const int rope_off = offs.rope(n, wave, lane_t);
+        RingPump<D_QK> pump{rsrc, nxt, 8 * wave, offs.pump(n, wave, lane_t),
+                            (lane_t * 16) ^ ((wave & 1) << 5), 0u, 0u};
+        offs = RingOffs::read(keys, t + kAhead + 1, wave, lane_t);
+        const int rem = n - t * BK;
+        const uint32_t bits = rem >= BK ? 0xffffffffu : (1u << rem) - 1u;
+        // Inside the S^T chain: the rope copy of stage t + kAhead, and the
+        // first V^T operands of stage t - 1 before its last MFMAs.
+        RingV<D_QK> v;
+        auto hook = [&](int d) {
+          if (d == 1) ring_rope<D_QK>(nxt, rsrc, rope_off, wave, lane_t);
+          if (!decltype(first)::value && d == T::kDSteps - 4) {
+            v.init(prev, lane_t);
+            v.prefetch();
+          }
+        };
+        const f32x16 s = ring_scores<D_QK, kKRead, LFRESH>(cur, qf, pump, hook);
+        bf16x8 pnext[2];
+        ring_pv_softmax<D_QK, !decltype(first)::value, true, decltype(masked)::value>(
+            v, pprev, acc, s, bits, st, a.scale_log2, pnext);
+        pprev[0] = pnext[0];
+        pprev[1] = pnext[1];
+      };
+      if (nst > 0) {
+        // Only the last stage can hold fewer than 32 keys.
+        if (nst == 1) {
+          step(0, std::true_type{}, std::true_type{});
+        } else {
+          step(0, std::true_type{}, std::false_type{});
+          for (int t = 1; t < nst - 1; ++t) step(t, std::false_type{}, std::false_type{});
+          step(nst - 1, std::false_type{}, std::true_type{});
+        }
+        RingV<D_QK> v;
+        v.init(ring + ((nst - 1) % NS) * T::kBufBytes, lane_fresh());
+        v.prefetch();
+        bf16x8 none[2];
+        ring_pv_softmax<D_QK, true, false>(v, pprev, acc, f32x16{}, 0u, st, a.scale_log2, none);
+      }
+      // The zero-fill copies of the stages past the end may still be landing.
+      wait_vm_all();
+      if (!__syncthreads_or(st.overflow) || attempt == 1) break;
+      m_preset = st.m_max;
+    }
+
+    // Normalise and store, as the wide kernel without a key split does: the
+    // wave's bf16 tile is staged in its own ring buffer (no wave reads the
+    // ring any more: the barrier above follows the last stage).
+    const int lane_e = lane_fresh(), hl = lane_e & 31, half = lane_e >> 5, head = wave * 32 + hl;
+    float scale = 0.f, lse_v = INFINITY, ml_v = -INFINITY;
+    if (st.l_sum > 0.f) {
+      float denom = st.l_sum;
+      if (SINK) denom += __builtin_amdgcn_exp2f(sink_lds[head] * kLog2e - st.m_ref);
+      scale = 1.f / denom;
+      ml_v = st.m_max * kLn2;
+      lse_v = (st.m_ref + __log2f(st.l_sum)) * kLn2;
+    }
+    if (half == 0) {
+      a.lse[(size_t)row * a.h_q + head] = lse_v;
+      if (a.max_logits) a.max_logits[(size_t)row * a.h_q + head] = ml_v;
+    }
+    LDS_AS uint8_t* tile = ring + wave * T::kBufBytes;
+#pragma unroll
+    for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 o4 = {(__bf16)(acc[ct][4 * j] * scale), (__bf16)(acc[ct][4 * j + 1] * scale),
+                           (__bf16)(acc[ct][4 * j + 2] * scale), (__bf16)(acc[ct][4 * j + 3] * scale)};
+        *reinterpret_cast<LDS_AS bf16x4*>(tile + hl * (kDV * 2) + (((4 * ct + j) ^ hl) << 4) + 8 * half) = o4;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tile is complete for every lane
+    uint8_t* orow = reinterpret_cast<uint8_t*>(a.out + ((size_t)row * a.h_q + wave * 32) * kDV) + lane_e * 16;
+#pragma unroll 4
+    for (int h = 0; h < 32; ++h) {
+      const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(tile + h * (kDV * 2) + ((lane_e ^ h) << 4));
+      *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
+    }
+  }
+}
+
 // Merge of the splits of split decode, one wave per (row, head): the split
 // lses give lse = logsumexp over the splits, each split's output enters with
 // weight exp(lse_s - lse), and an empty split (lse_s = -inf) contributes
@@ -1340,7 +1881,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
   *reinterpret_cast<bf16x8*>(a.out + ((size_t)row * a.h_q + head) * kDV + 8 * lane) = ob;
   if (lane == 0) {
     a.lse[(size_t)row * a.h_q + head] = lse_v;
-    a.max_logits[(size_t)row * a.h_q + head] = ml_v;
+    if (a.max_logits) a.max_logits[(size_t)row * a.h_q + head] = ml_v;
   }
 }
 
@@ -1443,6 +1984,39 @@ smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
   return SMLA_OK;
 }
 
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
+smla_status launch_ring(const FwdArgs& args, hipStream_t stream) {
+  const int cus = cu_count();
+  if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
+  const int grid = args.rows < cus ? args.rows : cus;  // one workgroup per CU (LDS)
+  hipLaunchKernelGGL((sparse_mla_fwd_ring_kernel<D_QK, PAGED, DYNAMIC, SINK>), dim3(grid),
+                     dim3(kWideWaves * 64), 0, stream, args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+// 128 heads and rows of at most kRingMaxTopk positions: the ring kernel.
+template <bool PAGED>
+smla_status dispatch_ring(int d_qk, FwdArgs& args, hipStream_t stream) {
+  const bool dyn = args.topk_length != nullptr;
+  const bool sink = args.attn_sink != nullptr;
+  args.head_groups = 1;
+#define SMLA_RING(D, DYN, SNK)                                 \
+  if (d_qk == D && dyn == DYN && sink == SNK)                  \
+    return launch_ring<D, PAGED, DYN, SNK>(args, stream);
+  SMLA_RING(512, false, false)
+  SMLA_RING(512, false, true)
+  SMLA_RING(512, true, false)
+  SMLA_RING(512, true, true)
+  SMLA_RING(576, false, false)
+  SMLA_RING(576, false, true)
+  SMLA_RING(576, true, false)
+  SMLA_RING(576, true, true)
+#undef SMLA_RING
+  return fail(SMLA_ERR_UNSUPPORTED, "no ring kernel instance for d_qk=%d", d_qk);
+}
+
 template <bool PAGED>
 smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
   // 128 heads: 4 waves; 64 heads at d_qk = 512: 2 waves (two workgroups per
@@ -1538,6 +2112,8 @@ smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
   // The wide kernel takes 64 and 128 heads (see dispatch_wide); it
   // addresses the KV table with 32-bit offsets (kv_span, set by the caller,
   // at most kMaxKvSpan).
+  if (args.h_q == 128 && args.topk <= kRingMaxTopk && args.kv_span <= kMaxKvSpan)
+    return dispatch_ring<PAGED>(d_qk, args, stream);
   if ((args.h_q == 64 || args.h_q == 128) && args.kv_span <= kMaxKvSpan)
     return dispatch_wide<PAGED>(d_qk, args, stream);
   const int waves_total = args.h_q / kHeadsPerWave;
@@ -1614,10 +2190,10 @@ smla_status decode_args(const char* who, const void* q, const void* kv_cache,
   if ((long long)B * s_q > 0x7fffffffLL) return fail(SMLA_ERR_BAD_SHAPE, "B*s_q overflows int32");
   if (B == 0) return SMLA_OK;
   if (!q || (!kv_cache && num_blocks > 0) || !block_table || !cache_seqlens || !indices || !out ||
-      !lse || !max_logits)
+      !lse)
     return fail(SMLA_ERR_NULL_ARG,
                 "%s: q, kv_cache (unless num_blocks = 0), block_table, cache_seqlens, indices, "
-                "out, lse and max_logits are required", who);
+                "out and lse are required", who);
   args.q = static_cast<const __bf16*>(q);
   args.kv = static_cast<const uint8_t*>(kv_cache);
   args.indices = indices;

@@ -100,6 +100,15 @@ def test_decode_rejects(lib, kw, status):
     assert _dec(lib, **kw) == status
 
 
+def test_decode_max_logits_is_optional(lib):
+    """max_logits may be NULL (the pages' decode returns out and lse only):
+    the host check names out and lse as the required outputs, not it."""
+    for call in (_dec, _split):
+        assert call(lib, lse=NULL, max_logits=NULL) == 1
+        msg = lib.sparse_mla_last_error().decode()
+        assert "out and lse are required" in msg and "max_logits" not in msg
+
+
 def test_decode_empty_batch_is_noop(lib):
     assert _dec(lib, B=0) == 0
     assert _dec(lib, B=0, q=NULL, indices=NULL, out=NULL, block_table=NULL) == 0
@@ -199,6 +208,23 @@ def test_row_lengths_rejects(lib):
     assert f(P, NULL, NULL, 4, 1, 0, 10, 0, P, NULL) == 2
     assert f(P, NULL, P, 4, 1, 64, 10, 0, P, NULL) == 2
     assert f(P, NULL, NULL, 0, 1, 64, 10, 0, P, NULL) == 0
+
+
+def test_binding_row_lengths_checks_seqlens():
+    """row r reads cache_seqlens[r // rows_per_seq]: the binding rejects a
+    cache_seqlens tensor too short for the rows, before anything runs."""
+    import torch
+    import sparse_top_mla_amd as smla
+    idx = torch.zeros(4, 2, 64, dtype=torch.int32)   # 8 rows
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        smla.row_lengths(idx, cache_seqlens=torch.zeros(4, dtype=torch.int32), max_blocks_per_seq=4)
+    with pytest.raises(ValueError, match="cache_seqlens"):
+        smla.row_lengths(idx, cache_seqlens=torch.zeros(3, dtype=torch.int32), rows_per_seq=2,
+                         max_blocks_per_seq=4)
+    with pytest.raises(ValueError, match="max_blocks_per_seq"):
+        smla.row_lengths(idx, cache_seqlens=torch.zeros(4, dtype=torch.int32), rows_per_seq=2)
+    with pytest.raises(ValueError, match="topk_length"):
+        smla.row_lengths(idx, topk_length=torch.zeros(4, dtype=torch.int32))
 
 
 def test_binding_rejects_cpu_tensors():

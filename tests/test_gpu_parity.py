@@ -267,6 +267,36 @@ def test_decode_edge_tables():
     assert np.array_equal(rl, ref)
 
 
+@pytest.mark.parametrize("h_q,num_splits", [(128, 1), (64, 1), (48, 1), (128, 4)])
+def test_decode_without_max_logits(h_q, num_splits):
+    """max_logits = NULL (the pages' decode returns out and lse only): out
+    and lse are bitwise those of the call that stores max_logits, in the
+    wide kernel (128 and 64 heads), the 16-head kernel (48) and split
+    decode."""
+    gen = torch.Generator().manual_seed(h_q + num_splits)
+    seqlens = torch.randint(200, 700, (6,), generator=gen)
+    c = W.make_decode(f"decode_no_ml_h{h_q}_s{num_splits}", batch=6, s_q=2, h_q=h_q, d_qk=576,
+                      d_v=512, topk=256, seqlens=seqlens, seed=50 + h_q, effective=200,
+                      with_length=True, with_sink=True)
+    _say(c.name)
+    q, kv, bt, cs, idx, tl, sk = _to([c.q, c.kv_cache, c.block_table, c.cache_seqlens, c.indices,
+                                      c.topk_length, c.attn_sink])
+    if num_splits == 1:
+        full = smla.decode_fwd(q, kv, bt, cs, idx, c.sm_scale, c.d_v, attn_sink=sk, topk_length=tl)
+        out, lse, ml = smla.decode_fwd(q, kv, bt, cs, idx, c.sm_scale, c.d_v, attn_sink=sk,
+                                       topk_length=tl, return_max_logits=False)
+    else:
+        full = smla.decode_fwd_split(q, kv, bt, cs, idx, c.sm_scale, num_splits, c.d_v,
+                                     attn_sink=sk, topk_length=tl)
+        out, lse, ml = smla.decode_fwd_split(q, kv, bt, cs, idx, c.sm_scale, num_splits, c.d_v,
+                                             attn_sink=sk, topk_length=tl,
+                                             return_max_logits=False)
+    torch.cuda.synchronize()
+    assert ml is None
+    assert torch.equal(out, full[0]) and torch.equal(lse, full[1]), c.name
+    assert_parity(full, oracle_decode(c), c.name)
+
+
 def test_decode_nan_pages_never_leak():
     c = W.decode_fixed(batch=3, min_len=2100, max_len=5000)
     _say("decode NaN guard")
