@@ -149,6 +149,36 @@ smla_status sparse_mla_decode_fwd_split(const void *q, const void *kv_cache,
                                         float *max_logits, smla_stream_t stream);
 
 /*
+ * Split-KV paged decode that allocates nothing, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments and results as
+ * sparse_mla_decode_fwd_split without the workspace: the partials live in a
+ * static device array of sparse_mla_decode_split_noalloc_max_bytes() bytes
+ * (256 (row, split) units at h_q = 128), which each GPU the library runs on
+ * holds until the process ends.  Its device address is looked up on the
+ * first call on a device.  The array needs no initialisation (every split
+ * writes its partials before the merge reads them) and keeps the last
+ * call's contents.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU race.  Partials larger than the array are rejected
+ * with SMLA_ERR_BAD_SHAPE before anything is launched; num_splits = 1 runs
+ * the unsplit path.  No allocation, free or synchronisation is made.
+ */
+size_t sparse_mla_decode_split_noalloc_max_bytes(void);
+
+smla_status sparse_mla_decode_fwd_split_noalloc(const void *q, const void *kv_cache,
+                                                const int32_t *block_table,
+                                                const int32_t *cache_seqlens,
+                                                const int32_t *indices,
+                                                const int32_t *topk_length,
+                                                const float *attn_sink, int32_t B, int32_t s_q,
+                                                int32_t h_q, int32_t h_kv, int32_t d_qk,
+                                                int32_t d_v, int32_t topk, int32_t num_blocks,
+                                                int32_t page_size, int32_t max_blocks_per_seq,
+                                                float sm_scale, int32_t num_splits, void *out,
+                                                float *lse, float *max_logits,
+                                                smla_stream_t stream);
+
+/*
  * The row length L every kernel above uses (FlashMLA PR #196, "Fix": tail
  * scan for the last valid entry; PR #216, "Summary": explicit lengths), from
  * the same device routine.

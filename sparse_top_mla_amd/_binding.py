@@ -19,8 +19,10 @@ _STATUS = {0: "SMLA_OK", 1: "SMLA_ERR_NULL_ARG", 2: "SMLA_ERR_BAD_SHAPE", 3: "SM
            4: "SMLA_ERR_LAUNCH"}
 
 EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_decode_split_workspace_bytes",
-           "sparse_mla_decode_fwd_split", "sparse_mla_row_lengths", "sparse_mla_bwd_workspace_bytes",
-           "sparse_mla_bwd", "sparse_mla_block_sparse_fwd", "sparse_mla_last_error")
+           "sparse_mla_decode_fwd_split", "sparse_mla_decode_split_noalloc_max_bytes",
+           "sparse_mla_decode_fwd_split_noalloc", "sparse_mla_row_lengths",
+           "sparse_mla_bwd_workspace_bytes", "sparse_mla_bwd", "sparse_mla_block_sparse_fwd",
+           "sparse_mla_last_error")
 
 _lib = None
 
@@ -58,6 +60,12 @@ def _declare(lib):
                                                 i32, i32, i32, i32, i32, f32, i32, vp,
                                                 ctypes.c_size_t, vp, vp, vp, vp]
     lib.sparse_mla_decode_fwd_split.restype = ctypes.c_int
+    lib.sparse_mla_decode_split_noalloc_max_bytes.argtypes = []
+    lib.sparse_mla_decode_split_noalloc_max_bytes.restype = ctypes.c_size_t
+    lib.sparse_mla_decode_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                                        i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                        vp, vp, vp, vp]
+    lib.sparse_mla_decode_fwd_split_noalloc.restype = ctypes.c_int
     lib.sparse_mla_row_lengths.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.sparse_mla_row_lengths.restype = ctypes.c_int
     lib.sparse_mla_bwd_workspace_bytes.argtypes = [i32, i32, i32]
@@ -246,6 +254,31 @@ def decode_fwd_split(q, kv_cache, block_table, cache_seqlens, indices, sm_scale,
                                          block_table.shape[1], float(sm_scale), int(num_splits),
                                          _p(workspace), workspace.numel(), _p(out), _p(lse),
                                          _p(max_logits), _stream(dev, stream))
+    _check(lib, st)
+    return out, lse, max_logits
+
+
+def decode_split_noalloc_max_bytes():
+    """Bytes of the static partials array of decode_fwd_split_noalloc."""
+    return int(load_library().sparse_mla_decode_split_noalloc_max_bytes())
+
+
+def decode_fwd_split_noalloc(q, kv_cache, block_table, cache_seqlens, indices, sm_scale,
+                             num_splits, d_v=512, attn_sink=None, topk_length=None, *, out=None,
+                             lse=None, max_logits=None, return_max_logits=True, stream=None):
+    """Split-KV paged decode whose partials live in the library's static
+    device array (the entry point allocates nothing; outputs are allocated
+    here when not given).  Arguments and results as decode_fwd_split."""
+    lib = load_library()
+    dev = q.device
+    (B, s_q, h_q, d_qk, num_blocks, page_size, h_kv, topk, topk_length, out, lse,
+     max_logits) = _decode_prep(q, kv_cache, block_table, cache_seqlens, indices, d_v, attn_sink,
+                                topk_length, out, lse, max_logits, return_max_logits)
+    st = lib.sparse_mla_decode_fwd_split_noalloc(
+        _p(q), _p(kv_cache), _p(block_table), _p(cache_seqlens), _p(indices), _p(topk_length),
+        _p(attn_sink), B, s_q, h_q, h_kv, d_qk, d_v, topk, num_blocks, page_size,
+        block_table.shape[1], float(sm_scale), int(num_splits), _p(out), _p(lse), _p(max_logits),
+        _stream(dev, stream))
     _check(lib, st)
     return out, lse, max_logits
 

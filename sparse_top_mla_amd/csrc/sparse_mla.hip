@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -2269,6 +2270,86 @@ extern "C" smla_status sparse_mla_decode_fwd_split(
     return fail(SMLA_ERR_BAD_SHAPE, "workspace must be 16-byte aligned");
   args.splits = num_splits;
   args.ws_o = static_cast<float*>(workspace);
+  args.ws_stats = args.ws_o + (size_t)args.rows * num_splits * h_q * kDV;
+  return dispatch_split(d_qk, args, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Split decode without allocation: the partials live in a static device
+// array instead of a caller-owned workspace.  Each GPU the library runs on
+// holds its own copy of the array until the process ends; in host code the
+// array's name is only a stand-in, so its device address is looked up once
+// per device (with that device current) and kept.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// 256 (row, split) units at 128 heads: (512 + 2) fp32 per unit and head.
+constexpr size_t kNoAllocScratchBytes = (size_t)256 * 128 * (kDV + 2) * sizeof(float);
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, or nullptr (the
+// error text is set).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(SMLA_ERR_LAUNCH, "cannot identify the current device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(SMLA_ERR_LAUNCH, "hipGetSymbolAddress of the scratch array failed: %s",
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t sparse_mla_decode_split_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" smla_status sparse_mla_decode_fwd_split_noalloc(
+    const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* cache_seqlens,
+    const int32_t* indices, const int32_t* topk_length, const float* attn_sink, int32_t B,
+    int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t topk,
+    int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale,
+    int32_t num_splits, void* out, float* lse, float* max_logits, smla_stream_t stream) {
+  g_last_error.clear();
+  FwdArgs args;
+  smla_status st = decode_args("sparse_mla_decode_fwd_split_noalloc", q, kv_cache, block_table,
+                               cache_seqlens, indices, topk_length, attn_sink, B, s_q, h_q, h_kv,
+                               d_qk, d_v, topk, num_blocks, page_size, max_blocks_per_seq, sm_scale,
+                               out, lse, max_logits, args);
+  if (st != SMLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(SMLA_ERR_BAD_SHAPE, "num_splits=%d (1 .. %d)", num_splits, kMaxSplits);
+  if ((long long)B * s_q * num_splits > 0x7fffffffLL)
+    return fail(SMLA_ERR_BAD_SHAPE, "B*s_q*num_splits overflows int32");
+  if ((long long)B * s_q * h_q > 0x7fffffffLL)
+    return fail(SMLA_ERR_BAD_SHAPE, "B*s_q*h_q overflows int32");
+  const size_t need = sparse_mla_decode_split_workspace_bytes(B, s_q, h_q, d_v, num_splits);
+  if (need > kNoAllocScratchBytes)
+    return fail(SMLA_ERR_BAD_SHAPE,
+                "the partials of %d x %d rows x %d splits x %d heads take %zu bytes; the static "
+                "scratch array holds %zu (use sparse_mla_decode_fwd_split with a workspace)",
+                B, s_q, num_splits, h_q, need, kNoAllocScratchBytes);
+  if (args.rows == 0) return SMLA_OK;
+  if (num_splits == 1) return dispatch_fwd<true>(d_qk, args, static_cast<hipStream_t>(stream));
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return SMLA_ERR_LAUNCH;
+  args.splits = num_splits;
+  args.ws_o = static_cast<float*>(ws);
   args.ws_stats = args.ws_o + (size_t)args.rows * num_splits * h_q * kDV;
   return dispatch_split(d_qk, args, static_cast<hipStream_t>(stream));
 }

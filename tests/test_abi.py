@@ -29,6 +29,8 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == ["sparse_mla_block_sparse_fwd", "sparse_mla_bwd",
                                      "sparse_mla_bwd_workspace_bytes",
                                      "sparse_mla_decode_fwd", "sparse_mla_decode_fwd_split",
+                                     "sparse_mla_decode_fwd_split_noalloc",
+                                     "sparse_mla_decode_split_noalloc_max_bytes",
                                      "sparse_mla_decode_split_workspace_bytes", "sparse_mla_fwd",
                                      "sparse_mla_last_error", "sparse_mla_row_lengths"]
 
@@ -145,6 +147,39 @@ def test_split_decode_rejects(lib, kw, status):
 
 def test_split_decode_empty_batch_is_noop(lib):
     assert _split(lib, B=0, workspace=NULL, workspace_bytes=0) == 0
+
+
+def _split_noalloc(lib, **kw):
+    a = dict(q=P, kv_cache=P, block_table=P, cache_seqlens=P, indices=P, topk_length=NULL,
+             attn_sink=NULL, B=2, s_q=1, h_q=128, h_kv=1, d_qk=576, d_v=512, topk=64,
+             num_blocks=8, page_size=64, max_blocks_per_seq=4, sm_scale=0.1, num_splits=4,
+             out=P, lse=P, max_logits=P, stream=NULL)
+    a.update(kw)
+    return lib.sparse_mla_decode_fwd_split_noalloc(*a.values())
+
+
+def test_split_noalloc_limit(lib):
+    """The static partials array holds 256 (row, split) units at 128 heads;
+    larger requests are rejected on the host before any device work."""
+    cap = lib.sparse_mla_decode_split_noalloc_max_bytes()
+    assert cap == 256 * 128 * 514 * 4
+    assert lib.sparse_mla_decode_split_workspace_bytes(64, 1, 128, 512, 4) <= cap
+    assert _split_noalloc(lib, B=65, num_splits=4) == 2
+    assert "static scratch array" in lib.sparse_mla_last_error().decode()
+    assert _split_noalloc(lib, B=2, s_q=2, num_splits=65) == 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_splits=0), 2), (dict(num_splits=1025), 2), (dict(q=NULL), 1), (dict(lse=NULL), 1),
+    (dict(page_size=32), 3), (dict(B=-1), 2),
+])
+def test_split_noalloc_rejects(lib, kw, status):
+    assert _split_noalloc(lib, **kw) == status
+    assert lib.sparse_mla_last_error().decode()
+
+
+def test_split_noalloc_empty_batch_is_noop(lib):
+    assert _split_noalloc(lib, B=0, out=NULL, lse=NULL, max_logits=NULL) == 0
 
 
 def _bwd(lib, **kw):
