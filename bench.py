@@ -58,6 +58,13 @@ def parse():
     ap.add_argument("--attainable", action="store_true",
                     help="measure this device's attainable dense bf16 MFMA rate (an MFMA loop) and HBM "
                          "bandwidth (a streaming copy) into profiles/attainable_peaks.json")
+    ap.add_argument("--groups", type=int, default=7,
+                    help="groups of 20 back-to-back calls for the pages' statistic (0: none, e.g. "
+                         "under a profiler)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/<kernel>_<workload>.md from rocprofv3 kernel traces under "
+                         "DIR (trace_<workload>/ with the bench.py line in bench_<workload>.json); "
+                         "no GPU needed")
     ap.add_argument("--no-variants", dest="variants", action="store_false",
                     help="default workload only: skip the other configurations under 'variants'")
     ap.add_argument("--replicas", type=int, default=3,
@@ -571,7 +578,7 @@ def ingest_counters(d):
                "dispatches": [len(f), len(wr)],
                "copy_calibration_factor": {"FETCH_SIZE": cal["FETCH_SIZE"], "WRITE_SIZE": cal["WRITE_SIZE"]},
                "command": f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -o run --output-format csv -- "
-                          f"python3 -u bench.py --workload {w} --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0; "
+                          f"python3 -u bench.py --workload {w} --no-variants --groups 0 --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0; "
                           f"calibration: ... -- python3 -u bench.py --calibrate-copy",
                "kernel_source_sha256_16": digest}
         busy = _mfma_busy(d / f"pmc_{w}_MFMA", kernel_name(w))
@@ -581,6 +588,57 @@ def ingest_counters(d):
         (PROFILES / f"traffic_{w}.json").write_text(json.dumps(rec, indent=1) + "\n")
         print(f"{w}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per launch "
               f"(fetch {fetch / 1e6:.1f}, write {write / 1e6:.1f})")
+    write_counter_summary(d, cal)
+
+
+def write_counter_summary(d, cal):
+    """profiles/counters_summary.md: the traffic and MFMA-busy records of
+    every workload beside the kernel time of the same workload's trace run
+    (bench_<workload>.json under `d`, the pages' group statistic)."""
+    rows = []
+    for f in sorted(PROFILES.glob("traffic_*.json")):
+        rec = json.loads(f.read_text())
+        w = rec["workload"]
+        if rec.get("kernel_source_sha256_16") != kernel_source_digest(w):
+            continue
+        bench_f = Path(d) / f"bench_{w}.json"
+        ms = alg = None
+        if bench_f.exists():
+            line = json.loads(bench_f.read_text().strip().splitlines()[-1])
+            ms = line["kernel_ms"].get("group_median")
+            alg = line["config"]["algorithmic_bytes_per_call"]
+        rows.append((w, rec, ms, alg))
+    out = ["# HBM traffic and MFMA busy of each workload's dominant kernel", "",
+           "Per workload, one rocprofv3 run per counter pass (FETCH_SIZE; WRITE_SIZE; "
+           "SQ_VALU_MFMA_BUSY_CYCLES with GRBM_GUI_ACTIVE), from the repository root with "
+           "`export TMPDIR=/tmp`:", "", "```",
+           "rocprofv3 --pmc <counters> -d <dir>/pmc_<workload>_<FETCH_SIZE|WRITE_SIZE|MFMA> -o run "
+           "--output-format csv -- python3 -u bench.py --workload <workload> --no-variants --groups 0 "
+           "--steps 3 --warmup 1 --cpu-seconds 0 --replicas 0",
+           "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -d <dir>/pmc_copy_<counter> -o run --output-format "
+           "csv -- python3 -u bench.py --calibrate-copy",
+           "python3 bench.py --ingest-counters <dir>", "```", "",
+           f"A plain 1 GiB device copy calibrates the counters: FETCH_SIZE x {cal['FETCH_SIZE']:.4f}, "
+           f"WRITE_SIZE x {cal['WRITE_SIZE']:.4f}.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+           "((GRBM_GUI_ACTIVE / XCDs) x SIMDs).  The kernel time is the median of 7 group means of 20 "
+           "calls from the trace run of the same workload "
+           "(`rocprofv3 --kernel-trace --stats ... bench.py --workload <workload> --no-variants`).", "",
+           "| workload | HBM bytes per launch | algorithmic bytes | ratio | HBM GB/s at the kernel time | "
+           "MFMA busy | kernel time (group median) |", "|---|---|---|---|---|---|---|"]
+    for w, rec, ms, alg in rows:
+        b = rec["hbm_bytes_per_launch"]
+        gbs = f"{b / (ms * 1e-3) / 1e9:.0f}" if ms else "-"
+        ratio = f"{b / alg:.2f}" if alg else "-"
+        algs = f"{alg / 1e6:.1f} MB" if alg else "-"
+        busy = f"{rec['mfma_busy_frac']:.3f}" if "mfma_busy_frac" in rec else "-"
+        t = f"{ms * 1e3:.1f} us" if ms else "-"
+        out.append(f"| {w} | {b / 1e6:.1f} MB | {algs} | {ratio} | {gbs} | {busy} | {t} |")
+    out += ["", "FETCH_SIZE counts L2 -> fabric reads, so KV rows served by the 256 MB Infinity Cache "
+            "after an L2 miss count as fetched bytes too: the prefill KV tables (8.4 MB, 4.7 MB) fit "
+            "the Infinity Cache but not one XCD's 4 MB L2, which is why prefill fetches 2-3x its "
+            "algorithmic bytes.  The decode pools (1.2 GB and more) do not fit it."]
+    (PROFILES / "counters_summary.md").write_text("\n".join(out) + "\n")
+    print("wrote profiles/counters_summary.md")
 
 
 def _mfma_busy(sub, kernel="sparse_mla_fwd"):
@@ -614,7 +672,64 @@ def _mfma_busy(sub, kernel="sparse_mla_fwd"):
             "mfma_busy_cycles_mean": busy, "grbm_gui_active_mean": gui,
             "mfma_busy_command": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -o run "
                                  f"--output-format csv -- python3 -u bench.py --workload "
-                                 f"{sub.name[len('pmc_'):-len('_MFMA')]} --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0"}
+                                 f"{sub.name[len('pmc_'):-len('_MFMA')]} --no-variants --groups 0 --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0"}
+
+
+TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d <dir>/trace_{w} -o run --output-format csv -- "
+                 "python3 -u bench.py --workload {w} --no-variants --cpu-seconds 0 --replicas 0")
+
+
+def summarize_traces(d):
+    """profiles/<kernel>_<workload>.md from the rocprofv3 kernel trace of one
+    bench.py run per workload: the per-kernel statistics, the dominant
+    kernel's timed region (its last `steps` dispatches before the group
+    calls) and the bench.py line of the same run."""
+    import csv
+    d = Path(d)
+    for sub in sorted(d.glob("trace_*")):
+        w = sub.name[len("trace_"):]
+        stats_f, trace_f = sub / "run_kernel_stats.csv", sub / "run_kernel_trace.csv"
+        bench_f = d / f"bench_{w}.json"
+        if not stats_f.exists() or not trace_f.exists() or not bench_f.exists():
+            continue
+        line = json.loads(bench_f.read_text().strip().splitlines()[-1])
+        stats = [r for r in csv.DictReader(open(stats_f))
+                 if "sparse_mla" in r["Name"] or "block_sparse" in r["Name"] or "combine" in r["Name"]
+                 or "row_lengths" in r["Name"] or "dkv" in r["Name"]]
+        name_frag = kernel_name(w)
+        disp = sorted((r for r in csv.DictReader(open(trace_f)) if name_frag in r["Kernel_Name"]),
+                      key=lambda r: int(r["Start_Timestamp"]))
+        groups = line.get("kernel_ms", {}).get("group_groups", 0) or 0
+        steps = line["steps"]
+        timed = disp[len(disp) - groups * 20 - steps:len(disp) - groups * 20] if disp else []
+        dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        kname = disp[0]["Kernel_Name"] if disp else name_frag
+        short = kname.replace("(anonymous namespace)::", "").replace("void ", "").split("<")[0]
+        out = [f"# {short} — {line['config']['workload']}", "",
+               "Command (from the repository root on one MI355X; `export TMPDIR=/tmp` first):", "",
+               "```", TRACE_COMMAND.format(w=w), "```", "",
+               f"bench.py timed {steps} calls after {line['warmup']} warmups through the C entry point "
+               f"(and {groups} groups of 20 calls after them).", "",
+               "rocprofv3 kernel statistics (run_kernel_stats.csv):", "",
+               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        for r in stats:
+            out.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                       f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        if dur:
+            out += ["", f"Timed region of `{kname}` (its {len(dur)} dispatches of the timed steps in "
+                        f"run_kernel_trace.csv): mean {statistics.fmean(dur):.1f} us, median "
+                        f"{statistics.median(dur):.1f} us."]
+        rf = line["roofline"]
+        out += ["", "bench.py line of the same run (under the profiler):", "",
+                f"- kernel time per call over the timed region: {line['kernel_ms']['timed_region_mean'] * 1e3:.1f} us",
+                f"- roofline: {rf['achieved']:.1f} {rf['unit']} of {rf['peak']} ({rf['bound']}), "
+                f"frac {rf['frac']:.3f}",
+                f"- algorithmic bytes per call {line['config']['algorithmic_bytes_per_call'] / 1e6:.1f} MB, "
+                f"FLOPs per call {line['config']['flops_per_call']:.4g}"]
+        fname = PROFILES / f"{short}_{w}.md"
+        PROFILES.mkdir(exist_ok=True)
+        fname.write_text("\n".join(out) + "\n")
+        print(f"wrote {fname.relative_to(ROOT)}")
 
 
 def attainable_peaks():
@@ -672,7 +787,7 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
-def measure(workload, case, dev, steps, warmup):
+def measure(workload, case, dev, steps, warmup, groups=7):
     """Times one workload: exactly `steps` calls after `warmup` (wall clock and
     events around the timed region), then the pages' 7 groups of 20 calls.
     Returns (record, counts)."""
@@ -683,13 +798,13 @@ def measure(workload, case, dev, steps, warmup):
     call = gpu_call_bwd(case, dev) if bwd else gpu_call_bs(case, dev) if bs else gpu_call(case, dev)
     torch.cuda.synchronize()
     ms_per_step, kernel_ms = time_steps(call, steps, warmup)
-    groups = time_groups(call)
+    gm = time_groups(call, groups=groups) if groups > 0 else [kernel_ms]
     rec = {
         "workload": case.name,
         "ms_per_call": ms_per_step,
         "kernel_ms": kernel_ms,
-        "group_means_ms": {"median": statistics.median(groups), "min": min(groups),
-                           "max": max(groups), "groups": len(groups), "calls_per_group": 20},
+        "group_means_ms": {"median": statistics.median(gm), "min": min(gm),
+                           "max": max(gm), "groups": groups, "calls_per_group": 20},
         "tflops": counts["flops"] / (kernel_ms * 1e-3) / 1e12,
         "roofline": roofline(workload, case, counts, kernel_ms),
         "hbm_gbs_algorithmic": counts["bytes"] / (kernel_ms * 1e-3) / 1e9,
@@ -711,6 +826,9 @@ def main():
     args = parse()
     if args.ingest_counters:
         ingest_counters(args.ingest_counters)
+        return
+    if args.summarize_trace:
+        summarize_traces(args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library has no "
@@ -735,7 +853,7 @@ def main():
     case = make_case(args.workload)
     bwd = args.workload == "bwd_h64"
     bs = is_block_sparse(case)
-    main_rec, counts = measure(args.workload, case, dev, args.steps, args.warmup)
+    main_rec, counts = measure(args.workload, case, dev, args.steps, args.warmup, args.groups)
     value = counts["flops"] / (main_rec["ms_per_call"] * 1e-3) / 1e12
 
     variants = {}
@@ -745,7 +863,7 @@ def main():
         for w in ("prefill_h64_len", "tiny", "prefill_h128", "decode_dynamic",
                   "decode_dynamic_nolen", "decode_fixed"):
             c = make_case(w)
-            rec, _ = measure(w, c, dev, args.steps, args.warmup)
+            rec, _ = measure(w, c, dev, args.steps, args.warmup, args.groups)
             variants[w] = rec
             del c
             torch.cuda.empty_cache()

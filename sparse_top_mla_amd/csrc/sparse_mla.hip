@@ -704,6 +704,43 @@ __device__ __forceinline__ float pair_sum32(float x) {
 }
 
 
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs.  The O^T
+// accumulator fills the AGPRs, and every MFMA the compiler emits in this
+// kernel takes its accumulator from AGPRs, so a compiled S^T chain would
+// evict part of O^T to VGPRs and back in every stage (48 moves, each about
+// two MFMA-issue cycles with one wave per SIMD).  The compiler does not see
+// the timing of these MFMAs: the first of a chain starts after two wait
+// states (a VALU write of an operand before it), consecutive ones chain on
+// the accumulator without wait states, and the last is followed by 18 wait
+// states before anything may read the result (an 8-pass MFMA's result is
+// readable by VALU after 11).
+__device__ __forceinline__ void mfma_vacc_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vacc_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
+               : "+v"(acc)
+               : "v"(a), "v"(b));
+}
+
+// max of three floats as one v_max3_f32.  fmaxf on values the compiler
+// cannot prove canonical (MFMA results) costs a canonicalising v_max_f32 per
+// operand first; the scores are never signalling NaNs.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // A wave works on 32-key tiles: keys [r0, r0 + 32) of the block in LDS, with
 // validity bits `bits` (bit i <-> key r0 + i).  Every function below that
 // issues MFMAs copies one row of the next block's gather (gather slots
@@ -738,7 +775,7 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
     if (d < 32) return buf + krow + (d >> 3) * 256 + ((32 * (d & 7)) ^ kw);
     return buf + rrow + ((32 * (d - 32)) ^ rw);
   };
-  f32x16 s = f32x16{};
+  f32x16 s;
   bf16x8 kring[kPrefetch];
 #pragma unroll
   for (int n = 0; n < kPrefetch; ++n) kring[n] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(n));
@@ -747,7 +784,13 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
     const bf16x8 kf = kring[d % kPrefetch];
     if (d + kPrefetch < T::kDSteps)
       kring[d % kPrefetch] = *reinterpret_cast<const LDS_AS bf16x8*>(kaddr(d + kPrefetch));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[d], s, 0, 0, 0);
+    // VGPR accumulator: O^T fills the AGPRs (see mfma_vacc)
+    if (d == 0)
+      mfma_vacc_first(s, kf, qf[d]);
+    else if (d == T::kDSteps - 1)
+      mfma_vacc_last(s, kf, qf[d]);
+    else
+      mfma_vacc(s, kf, qf[d]);
     if (d % EVERY == EVERY - 1 && d / EVERY < NP) pump.copy(slot0 + d / EVERY, false, d / EVERY == 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance
   }
@@ -762,15 +805,20 @@ __device__ __forceinline__ f32x16 tile_scores(const LDS_AS uint8_t* buf, int r0,
 // MFMA streams this code is scheduled into.
 __device__ __forceinline__ float tile_max(f32x16& s, uint32_t bits, SoftmaxState& st,
                                           float scale_log2) {
-  const uint32_t mlane = bits >> (4 * (lane_id() >> 5));
+  if (bits != 0xffffffffu) {  // wave-uniform: full tiles (almost all) skip the masking
+    const uint32_t mlane = bits >> (4 * (lane_id() >> 5));
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
-  float rmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, s[i]);
-  rmax = pair_max32(rmax) * scale_log2;  // -inf only for a tile without a valid key
-  st.m_max = fmaxf(st.m_max, rmax);
+    for (int i = 0; i < 16; ++i)
+      s[i] = ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[i] : -INFINITY;
+  }
+  const float m0 = max3_raw(s[0], s[1], s[2]), m1 = max3_raw(s[3], s[4], s[5]);
+  const float m2 = max3_raw(s[6], s[7], s[8]), m3 = max3_raw(s[9], s[10], s[11]);
+  const float m4 = max3_raw(s[12], s[13], s[14]);
+  float rmax = max3_raw(max3_raw(m0, m1, m2), max3_raw(m3, m4, s[15]), -INFINITY);
+  const uint2 pr = pair32(rmax);
+  // -inf only for a tile without a valid key
+  rmax = max_raw(__builtin_bit_cast(float, pr.x), __builtin_bit_cast(float, pr.y)) * scale_log2;
+  st.m_max = max_raw(st.m_max, rmax);
   if (st.m_ref == -INFINITY) st.m_ref = rmax;
   st.overflow |= rmax > st.m_ref + kRefSlack;  // this attempt is then discarded
   return st.m_ref == -INFINITY ? 0.f : -st.m_ref;
@@ -1430,43 +1478,6 @@ __device__ __forceinline__ void ring_copy_stage(LDS_AS uint8_t* buf, const u32x4
   RingPump<D_QK>{rsrc, buf, 8 * wave, o.pump(n, wave, lane), (lane * 16) ^ ((wave & 1) << 5), 0u,
                  0u}
       .copy_all();
-}
-
-// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs.  The O^T
-// accumulator fills the AGPRs, and every MFMA the compiler emits in this
-// kernel takes its accumulator from AGPRs, so a compiled S^T chain would
-// evict part of O^T to VGPRs and back in every stage (48 moves, each about
-// two MFMA-issue cycles with one wave per SIMD).  The compiler does not see
-// the timing of these MFMAs: the first of a chain starts after two wait
-// states (a VALU write of an operand before it), consecutive ones chain on
-// the accumulator without wait states, and the last is followed by 18 wait
-// states before anything may read the result (an 8-pass MFMA's result is
-// readable by VALU after 11).
-__device__ __forceinline__ void mfma_vacc_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vacc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_vacc_last(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 1"
-               : "+v"(acc)
-               : "v"(a), "v"(b));
-}
-
-// max of three floats as one v_max3_f32.  fmaxf on values the compiler
-// cannot prove canonical (MFMA results) costs a canonicalising v_max_f32 per
-// operand first; the scores are never signalling NaNs.
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
 }
 
 // S^T = K Q^T of a ring stage (32 keys at row 0 of `buf`), as tile_scores
