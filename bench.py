@@ -70,7 +70,30 @@ def parse():
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode: also time calls that rotate over this many copies of the inputs "
                          "(cold Infinity Cache); 0 disables")
+    ap.add_argument("--big-pool-gib", type=float, default=0.0,
+                    help="decode: also time the same call with its pages scattered over a pool of "
+                         "this many GiB (above 4 GiB the kernels rebase a resource per copied row)")
     return ap.parse_args()
+
+
+def big_pool_case(case, gib, dev, seed=11):
+    """The decode case with its pages moved to random pages of a pool of
+    `gib` GiB on `dev` (the pool's other pages are zero and never read), the
+    block table remapped to match."""
+    import dataclasses
+    import torch
+    n, page, _, d = case.kv_cache.shape
+    pages = int(gib * (1 << 30)) // (page * d * 2)
+    if pages < n:
+        raise ValueError("pool smaller than the case's pages")
+    gen = torch.Generator().manual_seed(seed)
+    new_page = torch.randperm(pages, generator=gen)[:n].to(torch.int32)
+    bt = case.block_table.clone()
+    bt[bt >= 0] = new_page[bt[bt >= 0].long()]
+    pool = torch.zeros((pages, page, 1, d), dtype=case.kv_cache.dtype, device=dev)
+    pool[new_page.long().to(dev)] = case.kv_cache.to(dev)
+    return dataclasses.replace(case, name=f"{case.name}_pool{gib:g}gib", kv_cache=pool,
+                               block_table=bt)
 
 
 # ---------------------------------------------------------------------------
@@ -881,6 +904,18 @@ def main():
             "ms_per_call": ms_cold, "kernel_ms": kms_cold,
             "hbm_gbs_algorithmic": counts["bytes"] / (kms_cold * 1e-3) / 1e9}
         del calls
+    if is_decode(case) and args.big_pool_gib > 0:
+        big = big_pool_case(case, args.big_pool_gib, dev)
+        call_big = gpu_call(big, dev)
+        ms_big, kms_big = time_steps(call_big, args.steps, args.warmup)
+        import sparse_top_mla_amd as smla
+        variants[f"pool_{args.big_pool_gib:g}gib"] = {
+            "kernel": smla.last_kernel(), "pool_bytes": big.kv_cache.numel() * 2,
+            "ms_per_call": ms_big, "kernel_ms": kms_big,
+            "group_means_ms_median": statistics.median(time_groups(call_big)),
+            "hbm_gbs_algorithmic": counts["bytes"] / (kms_big * 1e-3) / 1e9}
+        del call_big, big
+        torch.cuda.empty_cache()
     rows = case.batch * case.s_q if is_decode(case) else counts["rows"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if is_decode(case) and rows < cus and case.h_q == 128:

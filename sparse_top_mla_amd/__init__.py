@@ -8,9 +8,9 @@ from ._binding import (EXPORTS, SparseMLAError, block_sparse_fwd, bwd,  # noqa: 
                        bwd_workspace_bytes, decode_fwd, decode_fwd_split,
                        decode_fwd_split_noalloc, decode_num_splits,
                        decode_split_noalloc_max_bytes, decode_split_workspace_bytes, fwd,
-                       load_library, row_lengths)
+                       last_kernel, load_library, row_lengths)
 
 __all__ = ["fwd", "bwd", "block_sparse_fwd", "bwd_workspace_bytes", "decode_fwd",
            "decode_fwd_split", "decode_fwd_split_noalloc", "decode_num_splits",
            "decode_split_noalloc_max_bytes", "decode_split_workspace_bytes", "row_lengths",
-           "load_library", "SparseMLAError", "EXPORTS"]
+           "last_kernel", "load_library", "SparseMLAError", "EXPORTS"]

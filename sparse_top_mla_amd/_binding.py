@@ -22,7 +22,7 @@ EXPORTS = ("sparse_mla_fwd", "sparse_mla_decode_fwd", "sparse_mla_decode_split_w
            "sparse_mla_decode_fwd_split", "sparse_mla_decode_split_noalloc_max_bytes",
            "sparse_mla_decode_fwd_split_noalloc", "sparse_mla_row_lengths",
            "sparse_mla_bwd_workspace_bytes", "sparse_mla_bwd", "sparse_mla_block_sparse_fwd",
-           "sparse_mla_last_error")
+           "sparse_mla_last_error", "sparse_mla_last_kernel")
 
 _lib = None
 
@@ -78,6 +78,8 @@ def _declare(lib):
     lib.sparse_mla_block_sparse_fwd.restype = ctypes.c_int
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
+    lib.sparse_mla_last_kernel.argtypes = []
+    lib.sparse_mla_last_kernel.restype = ctypes.c_char_p
     return lib
 
 
@@ -402,3 +404,10 @@ def block_sparse_fwd(q, k, v, q2k_row_ptr, q2k_col_idx, q_block, k_block, sm_sca
                                          _stream(dev, stream))
     _check(lib, st)
     return out, lse
+
+
+def last_kernel():
+    """Name of the attention kernel the last forward or decode call on this
+    thread launched ("ring", "wide", "split", "heads16", the first three with
+    "_big" for KV tables above 4 GiB; "" for none)."""
+    return load_library().sparse_mla_last_kernel().decode()

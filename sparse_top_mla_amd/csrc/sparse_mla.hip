@@ -106,7 +106,8 @@ struct FwdArgs {
   int32_t mbps;          // decode max_blocks_per_seq
   int32_t head_groups;   // workgroups per row (1 or 2)
   float scale_log2;      // sm_scale * log2(e)
-  uint32_t kv_span;      // bytes of the KV table (wide kernel: at most kMaxKvSpan)
+  uint32_t kv_span;      // bytes of the KV table (wide and ring kernels: at most kMaxKvSpan)
+  int32_t table_mode;    // 0: kv_span addressing; 1: BIG entries; 2: 64-bit (16-head kernel)
   int32_t splits;        // split decode: key-range splits per row (else 1)
   float* ws_o;           // split decode: [rows][splits][h_q][d_v] partial outputs
   float* ws_stats;       // split decode: [rows][splits][h_q][2] lse and max of each split
@@ -532,6 +533,59 @@ __device__ __forceinline__ u32x4s query_rsrc(const FwdArgs& a, int row, int row_
   return rs;
 }
 
+// Tables above kMaxKvSpan bytes (BIG instances).  A key is then its row's
+// byte offset in units of kBigUnit (d_qk * 2 is a multiple; a 32-bit entry
+// reaches 512 GiB), or kBigNone for no row, and each copy of a whole row
+// reads through a resource rebased on that row: base = row - OFF, where OFF
+// is the instruction offset the copy uses, and records OFF + 1 KiB, so the
+// copy's lane offsets (below 1 KiB) plus OFF stay inside; a kBigNone row
+// gets no records and is zero-filled as a masked row of a small table is.
+// The resource is built in scalar registers per copy (shift, 64-bit add,
+// select).  A base below 2^48 leaves the stride bits of word 1 clear.
+// big_table_rsrc carries the table's address in words 0 and 1.
+constexpr uint32_t kBigUnit = 128;
+constexpr uint32_t kBigNone = 0xFFFFFFFFu;
+
+__device__ __forceinline__ u32x4s big_table_rsrc(const FwdArgs& a) {
+  const uint64_t b = (uint64_t)(uintptr_t)a.kv;
+  u32x4s rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  rs[2] = 0u;
+  rs[3] = 0u;
+  return rs;
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4s big_row_rsrc(const u32x4s& tb, uint32_t e) {
+  const uint64_t b = ((((uint64_t)tb[1]) << 32) | tb[0]) + ((uint64_t)e * kBigUnit) - (uint64_t)OFF;
+  u32x4s rs;
+  rs[0] = (uint32_t)b;
+  rs[1] = (uint32_t)(b >> 32);
+  rs[2] = e == kBigNone ? 0u : (uint32_t)(OFF + 1024);
+  rs[3] = 0x00020000u;
+  return rs;
+}
+
+// Zeros for the BIG rope copies of masked rows (a per-lane global copy has
+// no records to fall outside of).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_chunks[128];
+
+// The BIG rope copy of one lane: 16 bytes at byte `col` of row entry `e`
+// (zeros for kBigNone) to LDS [lds + 16 lane, +16).  Inline assembly, as the
+// table copies: the compiler would count a builtin LDS copy as a store that
+// every later LDS read must wait for.
+__device__ __forceinline__ void big_rope_copy(const u32x4s& tb, uint32_t e, uint32_t col,
+                                              LDS_AS uint8_t* lds) {
+  const uint64_t base = (((uint64_t)tb[1]) << 32) | tb[0];
+  const uint64_t src = e == kBigNone ? (uint64_t)(uintptr_t)(g_zero_chunks + (col & 127u))
+                                     : base + (uint64_t)e * kBigUnit + col;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+
 // NOP: the wait state an LDS DMA needs after an M0 write (the compiler writes
 // M0 for the operand only when its value changes).
 template <int OFF, bool NOP = true>
@@ -548,6 +602,31 @@ __device__ __forceinline__ void dma_table16(const u32x4s& rs, uint32_t voff, uin
                  : "memory");
 }
 
+// The copy of one 1 KiB row (nope part) at instruction offset K KiB, lane
+// byte `lp` of the row: small tables take `so`, the row's offset moved down
+// by K KiB, through the table resource `rs`; BIG tables take `so` as the
+// row's entry and `rs` as big_table_rsrc.
+template <int K, bool NOP, bool BIG>
+__device__ __forceinline__ void copy_row(const u32x4s& rs, uint32_t so, uint32_t lp, uint32_t win) {
+  if constexpr (BIG)
+    dma_table16<K * 1024, NOP>(big_row_rsrc<K * 1024>(rs, so), lp, win);
+  else
+    dma_table16<K * 1024, NOP>(rs, lp + so, win);
+}
+
+// copy_row with K = s % 4 (s a constant once unrolled); `opens`: M0 was just
+// written for this copy.
+template <bool BIG>
+__device__ __forceinline__ void copy_slot(int s, bool opens, const u32x4s& rs, uint32_t so,
+                                          uint32_t lp, uint32_t win) {
+  switch (s & 3) {
+    case 0: copy_row<0, true, BIG>(rs, so, lp, win); break;
+    case 1: opens ? copy_row<1, true, BIG>(rs, so, lp, win) : copy_row<1, false, BIG>(rs, so, lp, win); break;
+    case 2: opens ? copy_row<2, true, BIG>(rs, so, lp, win) : copy_row<2, false, BIG>(rs, so, lp, win); break;
+    default: opens ? copy_row<3, true, BIG>(rs, so, lp, win) : copy_row<3, false, BIG>(rs, so, lp, win); break;
+  }
+}
+
 // Nope part (the first 512 columns, also V) of a block, one 1 KiB row per
 // call, so that the copies can be spread over the MFMA work of the previous
 // block: the issuing wave stalls while the memory pipeline is full, and a
@@ -562,12 +641,14 @@ __device__ __forceinline__ void dma_table16(const u32x4s& rs, uint32_t voff, uin
 // or any row of a block past the end of the query row, has offset kOob and
 // is zero-filled.  Lane L fills LDS chunk L of the row, so it fetches source
 // chunk L ^ swizzle(row); the swizzle depends on the row's low four bits
-// only, i.e. on s.
-template <int D_QK>
+// only, i.e. on s.  BIG tables: `offw` holds the rows' entries (kBigUnit
+// offsets, or kBigNone) and each copy rebases a resource on its row.
+template <int D_QK, bool BIG = false>
 struct GatherPump {
   using T = WideTile<D_QK>;
   static constexpr int kSlots = 16;  // rows per wave and block
-  u32x4s rsrc;       // table resource (wave-uniform)
+  static_assert(T::kNopeBytes == 1024, "copy_row copies 1 KiB rows");
+  u32x4s rsrc;       // table resource, or big_table_rsrc (wave-uniform)
   LDS_AS uint8_t* buf;
   int row0;          // first row of this wave (wave-uniform)
   int offw;          // lane s: source offset of row row0 + s (see row_offsets)
@@ -576,8 +657,11 @@ struct GatherPump {
   uint32_t win;      // M0 of the current four-row window
   uint32_t so_next;  // offset of the next slot, read one copy ahead
 
-  // Lane j of the result: offset of key j's row for slot j % 4, or kOob.
+  // Lane j of the result: offset of key j's row for slot j % 4, or kOob
+  // (BIG: the row's entry, or kBigNone).
   static __device__ __forceinline__ int row_offsets(const BlockMeta& m) {
+    if constexpr (BIG)
+      return (int)(m.ok ? (uint32_t)m.phys * (uint32_t)(T::kRowBytes / kBigUnit) : kBigNone);
     const uint32_t off = (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias -
                          (uint32_t)(lane_id() & 3) * T::kNopeBytes;
     return (int)(m.ok ? off : kOob);
@@ -598,14 +682,7 @@ struct GatherPump {
     if (opens) win = (uint32_t)(uintptr_t)(buf + (row0 + (s & ~3)) * T::kNopeBytes);
     const uint32_t so = first ? (uint32_t)__builtin_amdgcn_readlane(offw, s) : so_next;
     if (s + 1 < kSlots) so_next = (uint32_t)__builtin_amdgcn_readlane(offw, s + 1);
-    const uint32_t voff = ((uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4)) + so;
-    constexpr int B = T::kNopeBytes;
-    switch (s & 3) {
-      case 0: dma_table16<0 * B>(rsrc, voff, win); break;
-      case 1: opens ? dma_table16<1 * B>(rsrc, voff, win) : dma_table16<1 * B, false>(rsrc, voff, win); break;
-      case 2: opens ? dma_table16<2 * B>(rsrc, voff, win) : dma_table16<2 * B, false>(rsrc, voff, win); break;
-      default: opens ? dma_table16<3 * B>(rsrc, voff, win) : dma_table16<3 * B, false>(rsrc, voff, win); break;
-    }
+    copy_slot<BIG>(s, opens, rsrc, so, (uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4), win);
     issued |= 1u << s;
   }
   // Copies every slot in order (a block gathered outside the MFMA stream).
@@ -639,14 +716,7 @@ struct GatherPump {
   __device__ __forceinline__ void copy_any(int s) {
     win = (uint32_t)(uintptr_t)(buf + (row0 + (s & ~3)) * T::kNopeBytes);
     const uint32_t so = (uint32_t)__builtin_amdgcn_readlane(offw, s);
-    const uint32_t voff = ((uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4)) + so;
-    constexpr int B = T::kNopeBytes;
-    switch (s & 3) {
-      case 0: dma_table16<0 * B>(rsrc, voff, win); break;
-      case 1: dma_table16<1 * B>(rsrc, voff, win); break;
-      case 2: dma_table16<2 * B>(rsrc, voff, win); break;
-      default: dma_table16<3 * B>(rsrc, voff, win); break;
-    }
+    copy_slot<BIG>(s, true, rsrc, so, (uint32_t)lane16 ^ (uint32_t)(nope_swz(s) << 4), win);
   }
 };
 
@@ -655,7 +725,8 @@ struct GatherPump {
 // which holds source chunk (L%8) ^ swizzle(jj); `offs` are the per-key
 // offsets of GatherPump::row_offsets (moved down by (jj % 4) KiB, which is
 // added back), so masked rows stay outside the records and read zeros.
-template <int D_QK, int BK, int NW>
+// BIG: `offs` are entries, and each lane copies from its own row's address.
+template <int D_QK, int BK, int NW, bool BIG = false>
 __device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const u32x4s& rsrc, int offs,
                                            int wave) {
   using T = WideTile<D_QK, BK>;
@@ -666,9 +737,12 @@ __device__ __forceinline__ void stage_rope(LDS_AS uint8_t* buf, const u32x4s& rs
     const int g = g0 + wave;
     const int jj = 8 * g + (lane >> 3);
     const uint32_t o = (uint32_t)__shfl(offs, jj);
-    const uint32_t voff = o + (uint32_t)(jj & 3) * T::kNopeBytes + T::kNopeBytes +
-                          (uint32_t)(((lane & 7) ^ rope_swz(jj)) << 4);
-    dma_table16<0>(rsrc, voff, (uint32_t)(uintptr_t)(buf + T::kRopeBase + g * 8 * T::kRopeBytes));
+    const uint32_t col = T::kNopeBytes + (uint32_t)(((lane & 7) ^ rope_swz(jj)) << 4);
+    LDS_AS uint8_t* dst = buf + T::kRopeBase + g * 8 * T::kRopeBytes;
+    if constexpr (BIG)
+      big_rope_copy(rsrc, o, col, dst);
+    else
+      dma_table16<0>(rsrc, o + (uint32_t)(jj & 3) * T::kNopeBytes + col, (uint32_t)(uintptr_t)dst);
   }
 }
 
@@ -913,13 +987,13 @@ __device__ __forceinline__ void tile_softmax_pv(const LDS_AS uint8_t* buf, int r
 // first tile takes every gather slot of the wave, as many under S^T as its
 // MFMAs allow at one per EVERY and the rest under P*V, so that the copies
 // leave early.
-template <int D_QK, int BK, int KS, int EVERY, bool LFRESH>
+template <int D_QK, int BK, int KS, int EVERY, bool LFRESH, class Pump>
 __device__ __forceinline__ void wide_block(const LDS_AS uint8_t* buf, uint64_t mask, int koff,
                                            const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
                                            f32x16 (&acc)[kDV / 32], SoftmaxState& st,
-                                           float scale_log2, GatherPump<D_QK>& pump) {
+                                           float scale_log2, Pump& pump) {
   constexpr int kTiles = BK / KS / 32;
-  constexpr int kSlots = GatherPump<D_QK>::kSlots;
+  constexpr int kSlots = Pump::kSlots;
   constexpr int kSteps = WideTile<D_QK>::kDSteps;
   constexpr int NS = kSteps / EVERY < kSlots ? kSteps / EVERY : kSlots;  // under S^T
   constexpr int NV = kSlots - NS;                                       // under P*V
@@ -946,10 +1020,11 @@ struct Ahead {
   int idx1, page1, idx2;
 };
 
-template <int D_QK, int NW, int KS, bool PAGED>
+template <int D_QK, int NW, int KS, bool PAGED, bool BIG>
 struct WidePipe {
   static constexpr int BK = 16 * NW;
   using T = WideTile<D_QK, BK>;
+  using Pump = GatherPump<D_QK, BIG>;
   // Per-tile lane addresses: fewer spills and faster in the paged 128-head
   // kernels, slower in the others (measured).
   static constexpr bool LFRESH = PAGED && NW == 4 && KS == 1;
@@ -978,23 +1053,24 @@ struct WidePipe {
     // buffer) into `nxt` instead, head j as row j.  (Wave-uniform;
     // readfirstlane says so to the compiler, which must keep the selected
     // resource in scalar registers.)
+    // (BIG tables: the copies address rows by entry, so the query slice
+    // is loaded into registers instead, and q_row is -1.)
     const bool q_nxt =
-        KS == 2 && __builtin_amdgcn_readfirstlane((int)(!have_nxt && q_row >= 0)) != 0;
+        KS == 2 && !BIG && __builtin_amdgcn_readfirstlane((int)(!have_nxt && q_row >= 0)) != 0;
     BlockMeta mn = block_meta<PAGED>(a, index_ok<BK>(ah.idx1, t + 1, L, bound), ah.idx1, ah.page1);
     if (q_nxt) mn = BlockMeta{~0ull, lane_id(), true};
-    u32x4s rsrc = q_nxt ? query_rsrc(a, q_row, T::kRowBytes) : table_rsrc(a);
+    u32x4s rsrc = BIG ? big_table_rsrc(a) : q_nxt ? query_rsrc(a, q_row, T::kRowBytes) : table_rsrc(a);
 #pragma unroll
     for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
-    const int offs = GatherPump<D_QK>::row_offsets(mn);
-    if (have_nxt || q_nxt) stage_rope<D_QK, BK, NW>(nxt, rsrc, offs, wave);
+    const int offs = Pump::row_offsets(mn);
+    if (have_nxt || q_nxt) stage_rope<D_QK, BK, NW, BIG>(nxt, rsrc, offs, wave);
     const bool ok2 = index_ok<BK>(ah.idx2, t + 2, L, bound);
     const int page2 = page_lookup<PAGED>(a, seq, ok2, ah.idx2);
     const int idx3 = load_index<BK>(idx_row, t + 3, a.topk);
     // Past the last block (without a query slice to gather) the mask is
     // empty: the copies zero-fill `nxt`, which nothing reads any more.
-    const int row0 = GatherPump<D_QK>::kSlots * wave;
-    GatherPump<D_QK> pump{rsrc, nxt, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
-                          lane_id() * 16, 0u, 0u, 0u};
+    const int row0 = Pump::kSlots * wave;
+    Pump pump{rsrc, nxt, row0, Pump::wave_offsets(offs, row0), lane_id() * 16, 0u, 0u, 0u};
     const uint64_t wmask = KS == 1 ? mask_cur : ((mask_cur >> koff) & 0xffffffffull);
     if (wmask != 0)
       wide_block<D_QK, BK, KS, kEvery, LFRESH>(cur, mask_cur, koff, qf, acc, st, a.scale_log2,
@@ -1078,7 +1154,9 @@ __device__ __forceinline__ void load_query_lds(bf16x8 (&qf)[WideTile<D_QK>::kDSt
 // covering blocks [split * nblk / splits, (split + 1) * nblk / splits) of the
 // row; it writes its partial output normalised by its own sum, with its lse
 // and max, to the workspace, and split_combine_kernel merges the splits.
-template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK, bool SPLIT = false>
+// BIG: a KV table above kMaxKvSpan bytes (copies rebased per row).
+template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK, bool SPLIT = false,
+          bool BIG = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_wide_kernel(FwdArgs a) {
   static_assert(!SPLIT || (PAGED && KS == 1), "split decode: paged, without a key split");
@@ -1134,7 +1212,7 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
   // the last block step gathers it there (contiguous 1 KiB rows; loaded
   // straight into the MFMA operand layout, each load would touch 32 head
   // rows).
-  const int q_row = KS == 2 && nblk > t0 ? next : -1;
+  const int q_row = KS == 2 && !BIG && nblk > t0 ? next : -1;
 
   f32x16 acc[kDV / 32];
   SoftmaxState st;
@@ -1153,15 +1231,15 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
       Ahead ah{idx1, pg1, idx2};
       __syncthreads();  // a previous attempt or row may still read the buffers
       {
-        const u32x4s rsrc = table_rsrc(a);
-        const int offs = GatherPump<D_QK>::row_offsets(m0);
-        const int row0 = GatherPump<D_QK>::kSlots * wave;
-        stage_rope<D_QK, BK, NW>(buf0, rsrc, offs, wave);
-        GatherPump<D_QK>{rsrc, buf0, row0, GatherPump<D_QK>::wave_offsets(offs, row0),
-                         lane_id() * 16, 0u, 0u, 0u}
+        using Pump = GatherPump<D_QK, BIG>;
+        const u32x4s rsrc = BIG ? big_table_rsrc(a) : table_rsrc(a);
+        const int offs = Pump::row_offsets(m0);
+        const int row0 = Pump::kSlots * wave;
+        stage_rope<D_QK, BK, NW, BIG>(buf0, rsrc, offs, wave);
+        Pump{rsrc, buf0, row0, Pump::wave_offsets(offs, row0), lane_id() * 16, 0u, 0u, 0u}
             .copy_all();
       }
-      using P = WidePipe<D_QK, NW, KS, PAGED>;
+      using P = WidePipe<D_QK, NW, KS, PAGED, BIG>;
       for (int t = t0; t < nblk; t += 2) {
         P::step(a, buf0, buf1, t, nblk, L, bound, seq, idx_row, wave, koff, mask_cur, ah, qf, acc,
                 st, q_row);
@@ -1389,11 +1467,13 @@ __device__ __forceinline__ void barrier_lds() {
 // the four-row windows 8w and 8w + 4 and the row selected by the instruction
 // offset, as GatherPump does for 16 rows.  The rows' chunk swizzle depends on
 // the row's low four bits, 8(w % 2) + s: `lane16w` holds 16 * lane with the
-// wave's half of the pattern XORed in, the slot's half is a constant.
-template <int D_QK>
+// wave's half of the pattern XORed in, the slot's half is a constant.  BIG
+// tables: `offw` holds entries and `rsrc` is big_table_rsrc (see copy_row).
+template <int D_QK, bool BIG = false>
 struct RingPump {
   using T = WideTile<D_QK, kRingKeys>;
   static constexpr int kSlots = kRingKeys / kWideWaves;  // rows per wave and stage
+  static_assert(T::kNopeBytes == 1024, "copy_row copies 1 KiB rows");
   u32x4s rsrc;       // table resource (wave-uniform)
   LDS_AS uint8_t* buf;
   int row0;          // 8 * wave
@@ -1407,14 +1487,7 @@ struct RingPump {
     if (opens) win = (uint32_t)(uintptr_t)(buf + (row0 + (s & ~3)) * T::kNopeBytes);
     const uint32_t so = first ? (uint32_t)__builtin_amdgcn_readlane(offw, s) : so_next;
     if (s + 1 < kSlots) so_next = (uint32_t)__builtin_amdgcn_readlane(offw, s + 1);
-    const uint32_t voff = ((uint32_t)lane16w ^ (uint32_t)(nope_swz(s) << 4)) + so;
-    constexpr int B = T::kNopeBytes;
-    switch (s & 3) {
-      case 0: dma_table16<0 * B>(rsrc, voff, win); break;
-      case 1: opens ? dma_table16<1 * B>(rsrc, voff, win) : dma_table16<1 * B, false>(rsrc, voff, win); break;
-      case 2: opens ? dma_table16<2 * B>(rsrc, voff, win) : dma_table16<2 * B, false>(rsrc, voff, win); break;
-      default: opens ? dma_table16<3 * B>(rsrc, voff, win) : dma_table16<3 * B, false>(rsrc, voff, win); break;
-    }
+    copy_slot<BIG>(s, opens, rsrc, so, (uint32_t)lane16w ^ (uint32_t)(nope_swz(s) << 4), win);
   }
   __device__ __forceinline__ void copy_all() {
 #pragma unroll
@@ -1425,16 +1498,21 @@ struct RingPump {
 // The rope part (d_qk = 576) of a 32-key stage, one copy per wave: lane L
 // copies chunk L % 8 of row jj = 8 wave + L / 8 (LDS chunk L % 8 holds source
 // chunk (L % 8) ^ swizzle(jj)).  `o` is row jj's offset as ring_lane_offset
-// gives it for this lane (moved down by (L % 4) KiB; kOob for no row).
-template <int D_QK>
+// gives it for this lane (moved down by (L % 4) KiB; kOob for no row; BIG:
+// the row's entry, or kBigNone).
+template <int D_QK, bool BIG = false>
 __device__ __forceinline__ void ring_rope(LDS_AS uint8_t* buf, const u32x4s& rsrc, int o, int wave,
                                           int lane) {
   using T = WideTile<D_QK, kRingKeys>;
   if (T::kRopeLanes == 0) return;
   const int jj = 8 * wave + (lane >> 3);
-  const uint32_t voff = (uint32_t)o + (uint32_t)(lane & 3) * T::kNopeBytes + T::kNopeBytes +
-                        (uint32_t)(((lane & 7) ^ rope_swz(jj)) << 4);
-  dma_table16<0>(rsrc, voff, (uint32_t)(uintptr_t)(buf + T::kRopeBase + wave * 8 * T::kRopeBytes));
+  const uint32_t col = T::kNopeBytes + (uint32_t)(((lane & 7) ^ rope_swz(jj)) << 4);
+  LDS_AS uint8_t* dst = buf + T::kRopeBase + wave * 8 * T::kRopeBytes;
+  if constexpr (BIG)
+    big_rope_copy(rsrc, (uint32_t)o, col, dst);
+  else
+    dma_table16<0>(rsrc, (uint32_t)o + (uint32_t)(lane & 3) * T::kNopeBytes + col,
+                   (uint32_t)(uintptr_t)dst);
 }
 
 // The list entries one wave needs for the copies of one stage, read ahead
@@ -1443,7 +1521,8 @@ __device__ __forceinline__ void ring_rope(LDS_AS uint8_t* buf, const u32x4s& rsr
 // unconditional (of a clamped entry): the compiler would otherwise sink them
 // into a branch on the position and wait for them right away.  The offsets
 // themselves are formed where they are used (`rope`, `pump`: moved down by
-// (L % 4) KiB, or kOob past the end of the list of n keys).
+// (L % 4) KiB, or kOob past the end of the list of n keys; BIG: the entry,
+// or kBigNone).
 struct RingOffs {
   uint32_t rope_raw, pump_raw;
   int stage;
@@ -1457,39 +1536,43 @@ struct RingOffs {
     const int p0 = stage * kRingKeys + 8 * wave;
     return RingOffs{entry(keys, p0 + (lane >> 3)), entry(keys, p0 + (lane & 7)), stage};
   }
+  template <bool BIG>
   __device__ __forceinline__ int rope(int n, int wave, int lane) const {
     const int p = stage * kRingKeys + 8 * wave + (lane >> 3);
+    if constexpr (BIG) return p < n ? (int)rope_raw : (int)kBigNone;
     return p < n ? (int)(rope_raw - (uint32_t)(lane & 3) * 1024u) : (int)kOob;
   }
+  template <bool BIG>
   __device__ __forceinline__ int pump(int n, int wave, int lane) const {
     const int p = stage * kRingKeys + 8 * wave + (lane & 7);
+    if constexpr (BIG) return p < n ? (int)pump_raw : (int)kBigNone;
     return p < n ? (int)(pump_raw - (uint32_t)(lane & 3) * 1024u) : (int)kOob;
   }
 };
 
 // All copies of one stage (rope part, then the nope rows) from `rsrc` into
 // buffer `buf`, outside the MFMA stream.
-template <int D_QK>
+template <int D_QK, bool BIG>
 __device__ __forceinline__ void ring_copy_stage(LDS_AS uint8_t* buf, const u32x4s& rsrc,
                                                 const LDS_AS uint32_t* keys, int n, int stage,
                                                 int wave, int lane) {
   const RingOffs o = RingOffs::read(keys, stage, wave, lane);
-  ring_rope<D_QK>(buf, rsrc, o.rope(n, wave, lane), wave, lane);
-  RingPump<D_QK>{rsrc, buf, 8 * wave, o.pump(n, wave, lane), (lane * 16) ^ ((wave & 1) << 5), 0u,
-                 0u}
+  ring_rope<D_QK, BIG>(buf, rsrc, o.template rope<BIG>(n, wave, lane), wave, lane);
+  RingPump<D_QK, BIG>{rsrc, buf, 8 * wave, o.template pump<BIG>(n, wave, lane),
+                      (lane * 16) ^ ((wave & 1) << 5), 0u, 0u}
       .copy_all();
 }
 
 // S^T = K Q^T of a ring stage (32 keys at row 0 of `buf`), as tile_scores
 // with r0 = 0 but with the accumulator in VGPRs (mfma_vacc); the pump's nope
 // copies go after every fourth MFMA.
-template <int D_QK, int KP, bool LFRESH, class Hook>
+template <int D_QK, int KP, bool LFRESH, class Pump, class Hook>
 __device__ __forceinline__ f32x16 ring_scores(const LDS_AS uint8_t* buf,
                                               const bf16x8 (&qf)[WideTile<D_QK>::kDSteps],
-                                              RingPump<D_QK>& pump, Hook&& hook) {
+                                              Pump& pump, Hook&& hook) {
   using T = WideTile<D_QK, kRingKeys>;
   constexpr int kSteps = T::kDSteps;
-  constexpr int kSlots = RingPump<D_QK>::kSlots;
+  constexpr int kSlots = Pump::kSlots;
   const int lane = LFRESH ? lane_fresh() : lane_id();
   const int hl = lane & 31, half = lane >> 5;
   int krow = hl * T::kNopeBytes, kw = (half ^ nope_swz(hl)) << 4;
@@ -1633,7 +1716,7 @@ __device__ __forceinline__ void ring_pv_softmax(RingV<D_QK>& v, const bf16x8 (&p
   }
 }
 
-template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK, bool BIG>
 __global__ void __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_ring_kernel(FwdArgs a) {
   constexpr int NW = kWideWaves, BK = kRingKeys, NS = kRingStages;
@@ -1711,7 +1794,8 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
       const bool ok = idxv[k] >= 0 && idxv[k] < bound;
       const BlockMeta m = block_meta<PAGED>(a, ok, idxv[k], pgv[k]);
       mk[k] = m.mask;
-      offv[k] = (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias;
+      offv[k] = BIG ? (uint32_t)m.phys * (uint32_t)(T::kRowBytes / kBigUnit)
+                    : (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias;
       cnt += __builtin_popcountll(m.mask);
     }
     if (lane == 0) counts[wave] = cnt;
@@ -1744,10 +1828,10 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
       for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
       st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
       __syncthreads();  // the query rows (or a previous attempt's stages) have been read
-      const u32x4s rsrc = table_rsrc(a);
+      const u32x4s rsrc = BIG ? big_table_rsrc(a) : table_rsrc(a);
 #pragma unroll
       for (int t = 0; t < kAhead; ++t)
-        ring_copy_stage<D_QK>(ring + t * T::kBufBytes, rsrc, keys, n, t, wave, lane_id());
+        ring_copy_stage<D_QK, BIG>(ring + t * T::kBufBytes, rsrc, keys, n, t, wave, lane_id());
       // Step t: wait for stage t (stage t+1 stays in flight), issue stage
       // t + kAhead into the buffer of stage t - 2 (its rope part now, its
       // nope rows under the S^T MFMAs), S^T of stage t, then P*V of stage
@@ -1764,9 +1848,9 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
         LDS_AS uint8_t* cur = ring + (t % NS) * T::kBufBytes;
         LDS_AS uint8_t* prev = ring + ((t + NS - 1) % NS) * T::kBufBytes;
         LDS_AS uint8_t* nxt = ring + ((t + kAhead) % NS) * T::kBufBytes;
-        const int rope_off = offs.rope(n, wave, lane_t);
-        RingPump<D_QK> pump{rsrc, nxt, 8 * wave, offs.pump(n, wave, lane_t),
-                            (lane_t * 16) ^ ((wave & 1) << 5), 0u, 0u};
+        const int rope_off = offs.template rope<BIG>(n, wave, lane_t);
+        RingPump<D_QK, BIG> pump{rsrc, nxt, 8 * wave, offs.template pump<BIG>(n, wave, lane_t),
+                                 (lane_t * 16) ^ ((wave & 1) << 5), 0u, 0u};
         offs = RingOffs::read(keys, t + kAhead + 1, wave, lane_t);
         const int rem = n - t * BK;
         const uint32_t bits = rem >= BK ? 0xffffffffu : (1u << rem) - 1u;
@@ -1774,7 +1858,7 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
         // first V^T operands of stage t - 1 before its last MFMAs.
         RingV<D_QK> v;
         auto hook = [&](int d) {
-          if (d == 1) ring_rope<D_QK>(nxt, rsrc, rope_off, wave, lane_t);
+          if (d == 1) ring_rope<D_QK, BIG>(nxt, rsrc, rope_off, wave, lane_t);
           if (!decltype(first)::value && d == T::kDSteps - 4) {
             v.init(prev, lane_t);
             v.prefetch();
@@ -1950,6 +2034,10 @@ smla_status check_common(int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v, i
   return SMLA_OK;
 }
 
+// The attention kernel the last forward or decode call on this thread
+// launched (for tests and tools).
+thread_local const char* g_last_kernel = "";
+
 template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
 smla_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   const int waves_total = args.h_q / kHeadsPerWave;
@@ -1957,6 +2045,7 @@ smla_status launch_fwd(const FwdArgs& args, hipStream_t stream) {
   const int grid = args.head_groups == 1 ? args.rows : ((args.rows + 7) / 8) * 16;
   hipLaunchKernelGGL((sparse_mla_fwd_kernel<D_QK, PAGED, DYNAMIC, SINK>), dim3(grid),
                      dim3(nwaves * 64), 0, stream, args);
+  g_last_kernel = "heads16";
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
@@ -1978,7 +2067,7 @@ int cu_count() {
   return n;
 }
 
-template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK>
+template <int D_QK, int NW, int KS, bool PAGED, bool DYNAMIC, bool SINK, bool BIG>
 smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
   if (args.h_q != 32 * NW / KS)
     return fail(SMLA_ERR_UNSUPPORTED, "wide kernel with %d waves and %d key splits needs h_q=%d",
@@ -1989,34 +2078,36 @@ smla_status launch_wide(const FwdArgs& args, hipStream_t stream) {
   // looping over rows.
   const long long slots = (long long)cus * (kWideWaves / NW);
   const int grid = args.rows < slots ? args.rows : (int)slots;
-  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, NW, KS, PAGED, DYNAMIC, SINK>), dim3(grid),
-                     dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, NW, KS, PAGED, DYNAMIC, SINK, false, BIG>),
+                     dim3(grid), dim3(NW * 64), 0, stream, args);
+  g_last_kernel = BIG ? "wide_big" : "wide";
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }
 
-template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK>
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK, bool BIG>
 smla_status launch_ring(const FwdArgs& args, hipStream_t stream) {
   const int cus = cu_count();
   if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
   const int grid = args.rows < cus ? args.rows : cus;  // one workgroup per CU (LDS)
-  hipLaunchKernelGGL((sparse_mla_fwd_ring_kernel<D_QK, PAGED, DYNAMIC, SINK>), dim3(grid),
+  hipLaunchKernelGGL((sparse_mla_fwd_ring_kernel<D_QK, PAGED, DYNAMIC, SINK, BIG>), dim3(grid),
                      dim3(kWideWaves * 64), 0, stream, args);
+  g_last_kernel = BIG ? "ring_big" : "ring";
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }
 
 // 128 heads and rows of at most kRingMaxTopk positions: the ring kernel.
-template <bool PAGED>
+template <bool PAGED, bool BIG>
 smla_status dispatch_ring(int d_qk, FwdArgs& args, hipStream_t stream) {
   const bool dyn = args.topk_length != nullptr;
   const bool sink = args.attn_sink != nullptr;
   args.head_groups = 1;
 #define SMLA_RING(D, DYN, SNK)                                 \
   if (d_qk == D && dyn == DYN && sink == SNK)                  \
-    return launch_ring<D, PAGED, DYN, SNK>(args, stream);
+    return launch_ring<D, PAGED, DYN, SNK, BIG>(args, stream);
   SMLA_RING(512, false, false)
   SMLA_RING(512, false, true)
   SMLA_RING(512, true, false)
@@ -2029,7 +2120,7 @@ smla_status dispatch_ring(int d_qk, FwdArgs& args, hipStream_t stream) {
   return fail(SMLA_ERR_UNSUPPORTED, "no ring kernel instance for d_qk=%d", d_qk);
 }
 
-template <bool PAGED>
+template <bool PAGED, bool BIG>
 smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
   // 128 heads: 4 waves; 64 heads at d_qk = 512: 2 waves (two workgroups per
   // CU, 32-key blocks); 64 heads at d_qk = 576: 4 waves as 2 head groups x 2
@@ -2041,7 +2132,7 @@ smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
   args.head_groups = 1;
 #define SMLA_WIDE(D, W, K, DYN, SNK)                                     \
   if (d_qk == D && nw == W && ks == K && dyn == DYN && sink == SNK)      \
-    return launch_wide<D, W, K, PAGED, DYN, SNK>(args, stream);
+    return launch_wide<D, W, K, PAGED, DYN, SNK, BIG>(args, stream);
   SMLA_WIDE(512, 4, 1, false, false)
   SMLA_WIDE(512, 4, 1, false, true)
   SMLA_WIDE(512, 4, 1, true, false)
@@ -2065,15 +2156,16 @@ smla_status dispatch_wide(int d_qk, FwdArgs& args, hipStream_t stream) {
 // Split decode: the wide kernel over (row, split) units writing partials to
 // the workspace, then the merge.  Only layouts without a key split (128
 // heads, or 64 heads at d_qk = 512).
-template <int D_QK, int NW, bool DYNAMIC, bool SINK>
+template <int D_QK, int NW, bool DYNAMIC, bool SINK, bool BIG>
 smla_status launch_split(const FwdArgs& args, hipStream_t stream) {
   const int cus = cu_count();
   if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
   const long long units = (long long)args.rows * args.splits;
   const long long slots = (long long)cus * (kWideWaves / NW);
   const int grid = (int)(units < slots ? units : slots);
-  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, NW, 1, true, DYNAMIC, SINK, true>),
+  hipLaunchKernelGGL((sparse_mla_fwd_wide_kernel<D_QK, NW, 1, true, DYNAMIC, SINK, true, BIG>),
                      dim3(grid), dim3(NW * 64), 0, stream, args);
+  g_last_kernel = BIG ? "split_big" : "split";
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   const long long waves = (long long)args.rows * args.h_q;
@@ -2089,14 +2181,16 @@ smla_status dispatch_split(int d_qk, FwdArgs& args, hipStream_t stream) {
     return fail(SMLA_ERR_UNSUPPORTED,
                 "split decode supports h_q=128, or h_q=64 at d_qk=512 (got h_q=%d, d_qk=%d)",
                 args.h_q, d_qk);
-  if (args.kv_span > kMaxKvSpan)
-    return fail(SMLA_ERR_UNSUPPORTED, "split decode: KV pool above %u bytes", kMaxKvSpan);
+  if (args.table_mode == 2)
+    return fail(SMLA_ERR_UNSUPPORTED, "split decode: KV pool rows beyond 32-bit row entries");
   const int nw = args.h_q / 32;
   const bool dyn = args.topk_length != nullptr;
   const bool sink = args.attn_sink != nullptr;
+  const bool big = args.table_mode == 1;
 #define SMLA_SPLIT(D, W, DYN, SNK)                              \
   if (d_qk == D && nw == W && dyn == DYN && sink == SNK)        \
-    return launch_split<D, W, DYN, SNK>(args, stream);
+    return big ? launch_split<D, W, DYN, SNK, true>(args, stream) \
+               : launch_split<D, W, DYN, SNK, false>(args, stream);
   SMLA_SPLIT(512, 4, false, false)
   SMLA_SPLIT(512, 4, false, true)
   SMLA_SPLIT(512, 4, true, false)
@@ -2113,21 +2207,31 @@ smla_status dispatch_split(int d_qk, FwdArgs& args, hipStream_t stream) {
   return fail(SMLA_ERR_UNSUPPORTED, "no split decode instance for d_qk=%d", d_qk);
 }
 
-// KV table bytes for FwdArgs::kv_span; a table the wide kernel cannot address
-// with 32-bit offsets gets a value above kMaxKvSpan.
-uint32_t span_or_max(uint64_t bytes) {
-  return bytes <= kMaxKvSpan ? (uint32_t)bytes : 0xFFFFFFFFu;
+// Table addressing of the wide and ring kernels for a KV table of `rows`
+// rows: 32-bit byte offsets (kv_span) up to kMaxKvSpan bytes; above that,
+// BIG entries while every row's entry stays below kBigNone (tables up to
+// about 550 GB at d_qk = 576); beyond, the 16-head kernel's 64-bit
+// addresses.
+void set_table(FwdArgs& args, uint64_t rows, int d_qk) {
+  const uint64_t bytes = rows * (uint64_t)d_qk * 2u;
+  args.kv_span = bytes <= kMaxKvSpan ? (uint32_t)bytes : 0xFFFFFFFFu;
+  args.table_mode = bytes <= kMaxKvSpan                                        ? 0
+                    : rows * (uint64_t)(d_qk * 2 / kBigUnit) < (uint64_t)kBigNone ? 1
+                                                                                : 2;
 }
 
 template <bool PAGED>
 smla_status dispatch_fwd(int d_qk, FwdArgs& args, hipStream_t stream) {
-  // The wide kernel takes 64 and 128 heads (see dispatch_wide); it
-  // addresses the KV table with 32-bit offsets (kv_span, set by the caller,
-  // at most kMaxKvSpan).
-  if (args.h_q == 128 && args.topk <= kRingMaxTopk && args.kv_span <= kMaxKvSpan)
-    return dispatch_ring<PAGED>(d_qk, args, stream);
-  if ((args.h_q == 64 || args.h_q == 128) && args.kv_span <= kMaxKvSpan)
-    return dispatch_wide<PAGED>(d_qk, args, stream);
+  // The ring kernel takes 128 heads with rows of at most kRingMaxTopk
+  // positions, the wide kernel 64 and 128 heads (see dispatch_wide); both
+  // address the KV table as set_table decided.
+  const bool big = args.table_mode == 1;
+  if (args.table_mode != 2 && args.h_q == 128 && args.topk <= kRingMaxTopk)
+    return big ? dispatch_ring<PAGED, true>(d_qk, args, stream)
+               : dispatch_ring<PAGED, false>(d_qk, args, stream);
+  if (args.table_mode != 2 && (args.h_q == 64 || args.h_q == 128))
+    return big ? dispatch_wide<PAGED, true>(d_qk, args, stream)
+               : dispatch_wide<PAGED, false>(d_qk, args, stream);
   const int waves_total = args.h_q / kHeadsPerWave;
   args.head_groups = (waves_total > 4 && waves_total % 2 == 0) ? 2 : 1;
   const bool dyn = args.topk_length != nullptr;
@@ -2155,6 +2259,7 @@ extern "C" smla_status sparse_mla_fwd(const void* q, const void* kv, const int32
                                       void* out, float* lse, float* max_logits,
                                       smla_stream_t stream) {
   g_last_error.clear();
+  g_last_kernel = "";
   if (s_q < 0 || s_kv < 0) return fail(SMLA_ERR_BAD_SHAPE, "negative s_q=%d or s_kv=%d", s_q, s_kv);
   smla_status st = check_common(h_q, h_kv, d_qk, d_v, topk, sm_scale);
   if (st != SMLA_OK) return st;
@@ -2177,7 +2282,7 @@ extern "C" smla_status sparse_mla_fwd(const void* q, const void* kv, const int32
   args.topk = topk;
   args.s_kv = s_kv;
   args.scale_log2 = sm_scale * kLog2e;
-  args.kv_span = span_or_max((uint64_t)s_kv * (uint64_t)d_qk * 2u);
+  set_table(args, (uint64_t)s_kv, d_qk);
   return dispatch_fwd<false>(d_qk, args, static_cast<hipStream_t>(stream));
 }
 
@@ -2223,7 +2328,7 @@ smla_status decode_args(const char* who, const void* q, const void* kv_cache,
   args.num_blocks = num_blocks;
   args.mbps = max_blocks_per_seq;
   args.scale_log2 = sm_scale * kLog2e;
-  args.kv_span = span_or_max((uint64_t)num_blocks * kPage * (uint64_t)d_qk * 2u);
+  set_table(args, (uint64_t)num_blocks * kPage, d_qk);
   args.splits = 1;
   return SMLA_OK;
 }
@@ -2235,6 +2340,7 @@ extern "C" smla_status sparse_mla_decode_fwd(
     int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale, void* out,
     float* lse, float* max_logits, smla_stream_t stream) {
   g_last_error.clear();
+  g_last_kernel = "";
   FwdArgs args;
   const smla_status st = decode_args("sparse_mla_decode_fwd", q, kv_cache, block_table,
                                      cache_seqlens, indices, topk_length, attn_sink, B, s_q, h_q,
@@ -2259,6 +2365,7 @@ extern "C" smla_status sparse_mla_decode_fwd_split(
     int32_t num_splits, void* workspace, size_t workspace_bytes, void* out, float* lse,
     float* max_logits, smla_stream_t stream) {
   g_last_error.clear();
+  g_last_kernel = "";
   FwdArgs args;
   smla_status st = decode_args("sparse_mla_decode_fwd_split", q, kv_cache, block_table,
                                cache_seqlens, indices, topk_length, attn_sink, B, s_q, h_q, h_kv,
@@ -2337,6 +2444,7 @@ extern "C" smla_status sparse_mla_decode_fwd_split_noalloc(
     int32_t num_blocks, int32_t page_size, int32_t max_blocks_per_seq, float sm_scale,
     int32_t num_splits, void* out, float* lse, float* max_logits, smla_stream_t stream) {
   g_last_error.clear();
+  g_last_kernel = "";
   FwdArgs args;
   smla_status st = decode_args("sparse_mla_decode_fwd_split_noalloc", q, kv_cache, block_table,
                                cache_seqlens, indices, topk_length, attn_sink, B, s_q, h_q, h_kv,
@@ -2371,6 +2479,7 @@ extern "C" smla_status sparse_mla_row_lengths(const int32_t* indices, const int3
                                               int32_t max_blocks_per_seq, int32_t* row_len,
                                               smla_stream_t stream) {
   g_last_error.clear();
+  g_last_kernel = "";
   if (rows < 0 || topk <= 0 || rows_per_seq <= 0 || s_kv < 0)
     return fail(SMLA_ERR_BAD_SHAPE, "bad sizes (rows=%d topk=%d rows_per_seq=%d s_kv=%d)", rows,
                 topk, rows_per_seq, s_kv);
@@ -2388,6 +2497,8 @@ extern "C" smla_status sparse_mla_row_lengths(const int32_t* indices, const int3
 }
 
 extern "C" const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* sparse_mla_last_kernel(void) { return g_last_kernel; }
 
 // Error reporting for the library's other translation units (the backward).
 __attribute__((visibility("hidden"))) smla_status smla_report(smla_status s, const char* msg) {

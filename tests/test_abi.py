@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                                      "sparse_mla_decode_fwd_split_noalloc",
                                      "sparse_mla_decode_split_noalloc_max_bytes",
                                      "sparse_mla_decode_split_workspace_bytes", "sparse_mla_fwd",
-                                     "sparse_mla_last_error", "sparse_mla_row_lengths"]
+                                     "sparse_mla_last_error", "sparse_mla_last_kernel",
+                                     "sparse_mla_row_lengths"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -270,3 +271,9 @@ def test_binding_rejects_cpu_tensors():
     idx = torch.zeros(2, 1, 64, dtype=torch.int32)
     with pytest.raises(TypeError):
         smla.fwd(q, kv, idx, 0.1)
+
+
+def test_last_kernel_is_empty_after_a_rejected_call(lib):
+    from sparse_top_mla_amd import _binding
+    assert _fwd(lib, s_q=-1) != 0
+    assert _binding.last_kernel() == ""

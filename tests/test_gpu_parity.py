@@ -498,34 +498,49 @@ def test_recompute_in_split_decode():
 
 
 # ---------------------------------------------------------------------------
-# KV tables past 4 GiB (beyond the wide kernel's 32-bit buffer offsets): the
-# rows of a small case are placed at rows or pages of a larger table, many of
-# them past the 4 GiB mark, and the results must be the small case's
+# KV tables past 4 GiB (beyond 32-bit buffer offsets: the ring, wide and split
+# kernels then rebase a resource per copied row): the rows of a small case are
+# placed at rows or pages of a larger table, many of them past the 4 GiB mark,
+# and the results must be the small case's
 # ---------------------------------------------------------------------------
 
 BIG_ROWS = (1 << 32) // 1152 + 40_000  # ~4.35 GB at d_qk = 576
 
 
-@pytest.mark.parametrize("h_q", [64, 128])
-def test_kv_table_past_4gib(h_q):
-    small = W.make_prefill(f"big_kv_h{h_q}", s_q=6, s_kv=768, h_q=h_q, d_qk=576, d_v=512, topk=128,
-                           layout="scattered", invalid_frac=0.2, seed=5 + h_q, with_sink=True)
+# (h_q, d_qk, s_q, topk): one row per workgroup, and rows beyond the
+# persistent grid (each workgroup walks two or three rows: the 64-head
+# d_qk = 576 layout then loads the next row's query slice into registers);
+# 128 heads with rows longer than the ring kernel takes run the wide kernel
+@pytest.mark.parametrize("h_q,d_qk,s_q,topk", [(64, 576, 6, 128), (128, 576, 6, 128),
+                                               (64, 576, 300, 128), (64, 512, 600, 128),
+                                               (128, 512, 300, 128), (128, 576, 6, 2112)])
+def test_kv_table_past_4gib(h_q, d_qk, s_q, topk):
+    small = W.make_prefill(f"big_kv_h{h_q}_d{d_qk}_s{s_q}_k{topk}", s_q=s_q, s_kv=max(768, topk + 64),
+                           h_q=h_q, d_qk=d_qk, d_v=512, topk=topk, layout="scattered",
+                           invalid_frac=0.2, seed=5 + h_q + s_q, with_sink=True)
+    rows = (1 << 32) // (2 * d_qk) + 40_000
     gen = torch.Generator().manual_seed(6)
-    pos = torch.randperm(BIG_ROWS - 700_000, generator=gen)[:small.s_kv]
-    pos[::2] = BIG_ROWS - 1 - torch.arange(0, small.s_kv, 2)  # half of them in the last rows
+    pos = torch.randperm(rows - 700_000, generator=gen)[:small.s_kv]
+    pos[::2] = rows - 1 - torch.arange(0, small.s_kv, 2)  # half of them in the last rows
     idx = small.indices.long()
     ok = (idx >= 0) & (idx < small.s_kv)
     # invalid entries stay invalid in the big table (-1; an out-of-range value
     # of the small table may be a row of the big one)
     big_idx = torch.where(ok, pos[idx.clamp(0, small.s_kv - 1)], -1).to(torch.int32)
-    kv_big = torch.zeros((BIG_ROWS, 1, 576), dtype=torch.bfloat16, device=DEV)
+    kv_big = torch.zeros((rows, 1, d_qk), dtype=torch.bfloat16, device=DEV)
     kv_big[pos.to(DEV)] = small.kv.to(DEV)
     _say(small.name)
     sk = small.attn_sink.to(DEV)
     res = smla.fwd(small.q.to(DEV), kv_big, big_idx.to(DEV), small.sm_scale, small.d_v,
                    attn_sink=sk)
+    ring = h_q == 128 and topk <= 2048
+    assert smla.last_kernel() == ("ring_big" if ring else "wide_big")
     torch.cuda.synchronize()
     assert_parity(res, oracle_prefill(small), small.name + " in a >4 GiB table")
+    # the same case in its own small table takes the 32-bit form
+    smla.fwd(small.q.to(DEV), small.kv.to(DEV), small.indices.to(DEV), small.sm_scale, small.d_v,
+             attn_sink=sk)
+    assert smla.last_kernel() == ("ring" if ring else "wide")
     del kv_big
     torch.cuda.empty_cache()
 
@@ -546,8 +561,16 @@ def test_decode_pool_past_4gib():
     t = lambda x: None if x is None else x.to(DEV)  # noqa: E731
     res = smla.decode_fwd(t(c.q), pool, t(bt), t(c.cache_seqlens), t(c.indices), c.sm_scale,
                           c.d_v, attn_sink=t(c.attn_sink), topk_length=t(c.topk_length))
+    assert smla.last_kernel() == "ring_big"
     torch.cuda.synchronize()
-    assert_parity(res, oracle_decode(c), c.name + " in a >4 GiB pool")
+    ref = oracle_decode(c)
+    assert_parity(res, ref, c.name + " in a >4 GiB pool")
+    # split decode over the same pool (the wide kernel's BIG form)
+    res = smla.decode_fwd_split(t(c.q), pool, t(bt), t(c.cache_seqlens), t(c.indices), c.sm_scale,
+                                3, c.d_v, attn_sink=t(c.attn_sink), topk_length=t(c.topk_length))
+    assert smla.last_kernel() == "split_big"
+    torch.cuda.synchronize()
+    assert_parity(res, ref, c.name + " split in a >4 GiB pool")
     del pool
     torch.cuda.empty_cache()
 
