@@ -274,12 +274,14 @@ const char *sparse_mla_last_error(void);
  * sparse_mla_fwd, sparse_mla_decode_fwd, sparse_mla_decode_fwd_split or
  * sparse_mla_decode_fwd_split_noalloc on this thread launched ("" if it
  * launched none, or the last such call was another entry point):
- *   "ring"      128 heads, rows of at most 2048 index positions
- *   "wide"      64 heads, or 128 heads with longer rows
- *   "split"     split decode (the merge kernel follows it)
- *   "heads16"   every other head count, and KV tables whose rows the others
- *               cannot address (above about 550 GB)
- * with a suffix "_big" on the first three for KV tables above 4 GiB, which
+ *   "ring"        128 heads, rows of at most 2048 index positions
+ *   "wide"        64 heads, or 128 heads with longer rows
+ *   "ring_split"  split decode at 128 heads, at most 2048 positions per
+ *                 split (the merge kernel follows it)
+ *   "split"       other split decode (the wide kernel's split units)
+ *   "heads16"     every other head count, and KV tables whose rows the
+ *                 others cannot address (above about 550 GB)
+ * with a suffix "_big" on all but the last for KV tables above 4 GiB, which
  * those kernels address through a buffer resource rebased per copied row.
  * The string is static; it is for tests and tools and is not an error
  * channel. */

@@ -1716,7 +1716,14 @@ __device__ __forceinline__ void ring_pv_softmax(RingV<D_QK>& v, const bf16x8 (&p
   }
 }
 
-template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK, bool BIG>
+// SPLIT (split decode): a unit is a (row, split) pair that takes the row's
+// index blocks [split * n / S, (split + 1) * n / S) of 64 positions, n =
+// ceil(L / 64) for the row length L (S splits; at most kRingMaxTopk
+// positions per unit), the partition the wide kernel's split units use, so
+// that derived and explicit lengths give the same units; it writes its
+// output normalised by its own sum, with its lse and max, to the workspace;
+// split_combine_kernel merges the splits.
+template <int D_QK, bool PAGED, bool DYNAMIC, bool SINK, bool BIG, bool SPLIT = false>
 __global__ void __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_fwd_ring_kernel(FwdArgs a) {
   constexpr int NW = kWideWaves, BK = kRingKeys, NS = kRingStages;
@@ -1745,13 +1752,26 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
 
   bf16x8 qf[T::kDSteps];
   int turn = 0;
-  for (int row = turn_row(a.rows, turn, PAGED); row >= 0; row = turn_row(a.rows, ++turn, PAGED)) {
+  const int units = SPLIT ? a.rows * a.splits : a.rows;
+  for (int unit = turn_row(units, turn, PAGED); unit >= 0; unit = turn_row(units, ++turn, PAGED)) {
+    const int row = SPLIT ? unit / a.splits : unit;
     const int lane = lane_fresh();
     const int seq = row / a.rows_per_seq;
     const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
     const int32_t* idx_row = a.indices + (size_t)row * a.topk;
-    // Positions examined: below the explicit length, else the whole vector.
-    const int scan = DYNAMIC ? clamp_length(a.topk_length[row], a.topk) : a.topk;
+    // Positions examined: below the explicit length, else the whole vector
+    // (a split unit: its blocks' positions [lo, scan) below the row length).
+    int lo = 0, scan = DYNAMIC ? clamp_length(a.topk_length[row], a.topk) : a.topk;
+    if constexpr (SPLIT) {
+      const int L = DYNAMIC ? scan
+                            : finish_tail_scan(load_tail_round(idx_row, a.topk, lane), idx_row,
+                                               a.topk, bound);
+      const int nblk = (L + 63) / 64, split = unit % a.splits;
+      lo = (int)((long long)split * nblk / a.splits) * 64;
+      const int hi = (int)((long long)(split + 1) * nblk / a.splits) * 64;
+      scan = hi < L ? hi : L;
+      scan = scan > lo ? scan : lo;
+    }
 
     // The previous row's epilogue has read the ring (and the sinks are staged).
     __syncthreads();
@@ -1771,9 +1791,9 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
       }
     }
 
-    // Compaction: wave w examines positions [w * per, (w + 1) * per).
-    const int per = ((scan + 255) >> 8) << 6;  // a multiple of 64, at most kRingChunks * 64
-    const int p0 = wave * per;
+    // Compaction: wave w examines positions [lo + w * per, lo + (w + 1) * per).
+    const int per = ((scan - lo + 255) >> 8) << 6;  // a multiple of 64, at most kRingChunks * 64
+    const int p0 = lo + wave * per;
     int idxv[kRingChunks];
 #pragma unroll
     for (int k = 0; k < kRingChunks; ++k) {
@@ -1892,10 +1912,52 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
       m_preset = st.m_max;
     }
 
+    const int lane_e = lane_fresh(), hl = lane_e & 31, half = lane_e >> 5, head = wave * 32 + hl;
+    if constexpr (SPLIT) {
+      // The unit's output normalised by its own sum (the sink joins once,
+      // in the merge); an empty unit has lse = -inf (no contribution).  The
+      // wave's fp32 tile (32 heads x 512) leaves in two halves of 256
+      // columns through its own ring buffer: the accumulator layout
+      // acc[ct][i] = O[head][32 ct + 8 (i / 4) + 4 half + i % 4] puts 16 B
+      // chunk 8 (ct % 8) + 2 (i / 4) + half of the head's 1 KiB half row in
+      // a lane, written at chunk c ^ hl of LDS row hl; then each store
+      // instruction writes one head's half row, 1 KiB contiguous (stored
+      // from the accumulator layout, an instruction would touch 32 rows
+      // with 32 B each).
+      const size_t u = (size_t)unit * a.h_q + head;
+      const float inv = st.l_sum > 0.f ? 1.f / st.l_sum : 0.f;
+      LDS_AS uint8_t* tile = ring + wave * T::kBufBytes;
+      static_assert(T::kBufBytes >= 32 * 1024, "a 32 x 256 fp32 half tile fits a ring buffer");
+      float* obase = a.ws_o + ((size_t)unit * a.h_q + wave * 32) * kDV + 4 * lane_e;
+#pragma unroll
+      for (int K = 0; K < 2; ++K) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ct = 8 * K + c, chunk = 8 * c + 2 * j + half;
+            *reinterpret_cast<LDS_AS f32x4*>(tile + hl * 1024 + ((chunk ^ hl) << 4)) =
+                f32x4{acc[ct][4 * j] * inv, acc[ct][4 * j + 1] * inv, acc[ct][4 * j + 2] * inv,
+                      acc[ct][4 * j + 3] * inv};
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the half tile is complete
+#pragma unroll 4
+        for (int h = 0; h < 32; ++h) {
+          const f32x4 v = *reinterpret_cast<const LDS_AS f32x4*>(tile + h * 1024 + ((lane_e ^ h) << 4));
+          // non-temporal: the merge kernel reads the partials once
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(obase + (size_t)h * kDV + 256 * K));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next half overwrites it
+      }
+      if (half == 0) {
+        a.ws_stats[2 * u] = st.l_sum > 0.f ? (st.m_ref + __log2f(st.l_sum)) * kLn2 : -INFINITY;
+        a.ws_stats[2 * u + 1] = st.l_sum > 0.f ? st.m_max * kLn2 : -INFINITY;
+      }
+      continue;
+    }
     // Normalise and store, as the wide kernel without a key split does: the
     // wave's bf16 tile is staged in its own ring buffer (no wave reads the
     // ring any more: the barrier above follows the last stage).
-    const int lane_e = lane_fresh(), hl = lane_e & 31, half = lane_e >> 5, head = wave * 32 + hl;
     float scale = 0.f, lse_v = INFINITY, ml_v = -INFINITY;
     if (st.l_sum > 0.f) {
       float denom = st.l_sum;
@@ -1922,7 +1984,7 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
 #pragma unroll 4
     for (int h = 0; h < 32; ++h) {
       const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(tile + h * (kDV * 2) + ((lane_e ^ h) << 4));
-      *reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(orow + (size_t)h * (kDV * 2)));
     }
   }
 }
@@ -1932,7 +1994,11 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
 // weight exp(lse_s - lse), and an empty split (lse_s = -inf) contributes
 // nothing; the sink joins the denominator once, after the merge; a row
 // whose splits are all empty gives out = 0, lse = +inf, max_logits = -inf.
-// Lane l takes value columns 8l .. 8l + 7.
+// Lane l takes value columns 8l .. 8l + 7.  The splits are read eight at a
+// time, every load of a round issued before any is used (a loop over single
+// splits waits one memory latency per split); the statistics are
+// wave-uniform loads.  Rounds past the last split re-read that split with
+// weight 0 (it is finite), so the sums keep the split order.
 template <bool SINK>
 __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
   const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1941,35 +2007,104 @@ __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
   const int S = a.splits;
   const float* st = a.ws_stats + ((size_t)row * S * a.h_q + head) * 2;
   const size_t sstride = (size_t)a.h_q * 2;  // between the splits of one head
-  float m = -INFINITY, mx = -INFINITY;
-  for (int s = 0; s < S; ++s) {
-    m = fmaxf(m, st[s * sstride]);
-    mx = fmaxf(mx, st[s * sstride + 1]);
-  }
+  constexpr int R = 8;                       // splits per round
+  const float* o = a.ws_o + ((size_t)row * S * a.h_q + head) * kDV + 8 * lane;
+  const size_t ostride = (size_t)a.h_q * kDV;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float lse_v = INFINITY, ml_v = -INFINITY;
-  if (m != -INFINITY) {
-    float z = 0.f;
-    for (int s = 0; s < S; ++s) z += expf(st[s * sstride] - m);  // exp(-inf) = 0
-    const float lse = m + logf(z);
-    const float* o = a.ws_o + ((size_t)row * S * a.h_q + head) * kDV + 8 * lane;
-    const size_t ostride = (size_t)a.h_q * kDV;
-    for (int s = 0; s < S; ++s) {
-      const float wgt = expf(st[s * sstride] - lse);
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(o + s * ostride);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
+  if (S <= R) {
+    // One round: every statistic and partial loaded before any is used.
+    float l8[R], x8[R];
+    f32x4 v0[R], v1[R];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wgt * v0[e];
-        acc[4 + e] += wgt * v1[e];
+    for (int j = 0; j < R; ++j) {
+      const int s = j < S ? j : S - 1;
+      l8[j] = st[s * sstride];
+      x8[j] = st[s * sstride + 1];
+      v0[j] = *reinterpret_cast<const f32x4*>(o + s * ostride);
+      v1[j] = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
+    }
+    float m = -INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      m = fmaxf(m, l8[j]);
+      mx = fmaxf(mx, x8[j]);
+    }
+    if (m != -INFINITY) {
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (j < S) z += expf(l8[j] - m);
+      const float lse = m + logf(z);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float wgt = j < S ? expf(l8[j] - lse) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += wgt * v0[j][e];
+          acc[4 + e] += wgt * v1[j][e];
+        }
+      }
+      lse_v = lse;
+      ml_v = mx;
+    }
+  } else {
+    // Rounds of R splits: the maxima, the sum, then the weighted partials.
+    float m = -INFINITY, mx = -INFINITY;
+    for (int s0 = 0; s0 < S; s0 += R) {
+      float l8[R], x8[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int s = s0 + j < S ? s0 + j : S - 1;
+        l8[j] = st[s * sstride];
+        x8[j] = st[s * sstride + 1];
+      }
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        m = fmaxf(m, l8[j]);
+        mx = fmaxf(mx, x8[j]);
       }
     }
+    if (m != -INFINITY) {
+      float z = 0.f;
+      for (int s0 = 0; s0 < S; s0 += R) {
+        float e8[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) e8[j] = st[(s0 + j < S ? s0 + j : S - 1) * sstride];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+          if (s0 + j < S) z += expf(e8[j] - m);  // exp(-inf) = 0
+      }
+      const float lse = m + logf(z);
+      for (int s0 = 0; s0 < S; s0 += R) {
+        f32x4 v0[R], v1[R];
+        float wg[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int s = s0 + j < S ? s0 + j : S - 1;
+          wg[j] = st[s * sstride];
+          v0[j] = *reinterpret_cast<const f32x4*>(o + s * ostride);
+          v1[j] = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const float wgt = s0 + j < S ? expf(wg[j] - lse) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] += wgt * v0[j][e];
+            acc[4 + e] += wgt * v1[j][e];
+          }
+        }
+      }
+      lse_v = lse;
+      ml_v = mx;
+    }
+  }
+  if (lse_v != INFINITY) {
     float f = 1.f;
-    if (SINK) f = 1.f / (1.f + expf(a.attn_sink[head] - lse));
+    if (SINK) f = 1.f / (1.f + expf(a.attn_sink[head] - lse_v));
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= f;
-    lse_v = lse;
-    ml_v = mx;
   }
   bf16x8 ob;
 #pragma unroll
@@ -2176,6 +2311,27 @@ smla_status launch_split(const FwdArgs& args, hipStream_t stream) {
   return SMLA_OK;
 }
 
+// Split decode at 128 heads with at most kRingMaxTopk positions per unit:
+// the ring kernel over (row, split) units, then the merge.
+template <int D_QK, bool DYNAMIC, bool SINK, bool BIG>
+smla_status launch_ring_split(const FwdArgs& args, hipStream_t stream) {
+  const int cus = cu_count();
+  if (cus <= 0) return fail(SMLA_ERR_LAUNCH, "cannot read the device's compute-unit count");
+  const long long units = (long long)args.rows * args.splits;
+  const int grid = (int)(units < cus ? units : cus);
+  hipLaunchKernelGGL((sparse_mla_fwd_ring_kernel<D_QK, true, DYNAMIC, SINK, BIG, true>), dim3(grid),
+                     dim3(kWideWaves * 64), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_kernel = BIG ? "ring_split_big" : "ring_split";
+  const long long waves = (long long)args.rows * args.h_q;
+  hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     stream, args);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 smla_status dispatch_split(int d_qk, FwdArgs& args, hipStream_t stream) {
   if (!(args.h_q == 128 || (args.h_q == 64 && d_qk == 512)))
     return fail(SMLA_ERR_UNSUPPORTED,
@@ -2187,6 +2343,22 @@ smla_status dispatch_split(int d_qk, FwdArgs& args, hipStream_t stream) {
   const bool dyn = args.topk_length != nullptr;
   const bool sink = args.attn_sink != nullptr;
   const bool big = args.table_mode == 1;
+  // (A unit then takes at most ceil(ceil(topk / 64) / splits) blocks of 64.)
+  if (args.h_q == 128 && (args.topk + 63) / 64 <= (kRingMaxTopk / 64) * args.splits) {
+#define SMLA_RSPLIT(D, DYN, SNK)                                          \
+    if (d_qk == D && dyn == DYN && sink == SNK)                         \
+      return big ? launch_ring_split<D, DYN, SNK, true>(args, stream)   \
+                 : launch_ring_split<D, DYN, SNK, false>(args, stream);
+    SMLA_RSPLIT(512, false, false)
+    SMLA_RSPLIT(512, false, true)
+    SMLA_RSPLIT(512, true, false)
+    SMLA_RSPLIT(512, true, true)
+    SMLA_RSPLIT(576, false, false)
+    SMLA_RSPLIT(576, false, true)
+    SMLA_RSPLIT(576, true, false)
+    SMLA_RSPLIT(576, true, true)
+#undef SMLA_RSPLIT
+  }
 #define SMLA_SPLIT(D, W, DYN, SNK)                              \
   if (d_qk == D && nw == W && dyn == DYN && sink == SNK)        \
     return big ? launch_split<D, W, DYN, SNK, true>(args, stream) \

@@ -447,6 +447,22 @@ def test_split_decode_short_and_empty_rows():
     assert_bitwise(a, run_decode_split(c, 9, topk_length=tl, workspace=ws), "workspace reused")
 
 
+def test_split_decode_wide_units_at_128_heads():
+    """128 heads with more than 2048 positions per split run the wide
+    kernel's split units; the ring's split units take the rest."""
+    seqlens = torch.tensor([5000, 4500])
+    c = W.make_decode("split_wide_h128", batch=2, s_q=2, h_q=128, d_qk=576, d_v=512, topk=4160,
+                      seqlens=seqlens, seed=77, effective=4100, with_length=True, with_sink=True)
+    _say(c.name)
+    ref = oracle_decode(c)
+    got = run_decode_split(c, 2)
+    assert smla.last_kernel() == "split"
+    assert_parity(got, ref, c.name + " x2")
+    got = run_decode_split(c, 3)
+    assert smla.last_kernel() == "ring_split"
+    assert_parity(got, ref, c.name + " x3")
+
+
 def test_split_decode_unsupported_layout_raises():
     c = _small_batch_decode(h_q=64, d_qk=576)
     with pytest.raises(smla.SparseMLAError):
@@ -568,7 +584,7 @@ def test_decode_pool_past_4gib():
     # split decode over the same pool (the wide kernel's BIG form)
     res = smla.decode_fwd_split(t(c.q), pool, t(bt), t(c.cache_seqlens), t(c.indices), c.sm_scale,
                                 3, c.d_v, attn_sink=t(c.attn_sink), topk_length=t(c.topk_length))
-    assert smla.last_kernel() == "split_big"
+    assert smla.last_kernel() == "ring_split_big"
     torch.cuda.synchronize()
     assert_parity(res, ref, c.name + " split in a >4 GiB pool")
     del pool
