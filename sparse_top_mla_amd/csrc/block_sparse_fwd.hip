@@ -12,21 +12,21 @@
 // without keys gives out = 0, lse = +inf.
 //
 // Layout of work: one workgroup per (ROWS query rows, query head), waves of
-// 16 rows: ROWS = 128 (8 waves) when the query block is a multiple of 128,
-// else 64 (4 waves); the larger group shares each K and V tile between
-// twice the rows.  Work items are numbered head-major (neighbouring items share
-// a head and their key tiles), and the launch hands each XCD a contiguous
-// range of them: workgroups are dispatched to the 8 XCDs in turn, so
-// workgroup L runs item (L % 8) * ceil(N / 8) + L / 8, and the items that
+// 32 rows: ROWS = 256 (8 waves) when the query block is a multiple of 256,
+// else 128 (4 waves) or 64 (2 waves); a larger group shares each K and V
+// tile between more rows.  Work items are numbered head-major (neighbouring
+// items share a head and their key tiles), and the launch hands each XCD a
+// contiguous range of them: workgroups are dispatched to the 8 XCDs in turn,
+// so workgroup L runs item (L % 8) * ceil(N / 8) + L / 8, and the items that
 // read the same K and V tiles meet in one XCD's L2.  The key blocks of the
 // query block are walked in 64-key tiles (a tile wholly after the
 // workgroup's last row is skipped under `causal`):
 //   K and V of the tile go to LDS (padded rows; keys past the block or s as
 //   zeros); the next tile's K and V are loaded into registers while this
 //   one is computed;
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the query rows' slice in
-//   registers as the B operand, so each lane owns one query row and keeps
-//   its online-softmax state (running max, sum) as scalars;
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16, the wave's 32 query rows'
+//   slice in registers as the B operand, so lanes j and j + 32 own row j and
+//   keep its online-softmax state (running max, sum);
 //   O^T += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T taken straight
 //   from the S^T accumulators (the key order of both operands is permuted
 //   alike).
@@ -48,6 +48,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -56,7 +57,6 @@ constexpr int kDV = 128;
 constexpr int kTile = 64;       // keys per tile
 constexpr int kKRow = 2 * kDQK + 16;   // padded LDS row of K
 constexpr int kVRow = 2 * kDV + 16;    // padded LDS row of V
-constexpr int kSteps = kDQK / 32;      // MFMA K steps over d_qk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -75,17 +75,6 @@ struct BsArgs {
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// ds_read_b64_tr_b16: in each 16-lane group, lane i gives the address of four
-// consecutive 16-bit values at row (i >> 2), columns 4 (i & 3) .. +3 of a
-// 4 x 16 tile, and lane n receives column n of the four rows.
-__device__ __forceinline__ bf16x8 tr_pair(const LDS_AS uint8_t* tile, int row_bytes, int r0,
-                                          int c0, int g, int i) {
-  const LDS_AS uint8_t* p = tile + (r0 + 4 * g + (i >> 2)) * row_bytes + (c0 + 4 * (i & 3)) * 2;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 16 * row_bytes));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 
 // Moves (e, t0, kend) to the tile after the current one (t0 < 0: to the
 // first tile of the list from entry e on): the next 64 keys of the current
@@ -153,14 +142,28 @@ __device__ __forceinline__ void store_tile(LDS_AS uint8_t* ks, LDS_AS uint8_t* v
   }
 }
 
-// ROWS = 128: 4 waves per SIMD (two workgroups per CU, at most 128 registers;
-// a few spills, measured about 12% faster than one workgroup at 170); ROWS =
-// 64: 2 waves per SIMD.
+// 32 query rows per wave on v_mfma_f32_32x32x16_bf16: each K or V fragment
+// read from LDS serves 32 rows, half the LDS reads per FLOP of 16-row waves
+// on the 16x16 shape, at the registers of one row group.  ROWS = 128 (4
+// waves, two per SIMD) or 64 (2 waves, whose tile prefetch takes twice the
+// registers per thread: one per SIMD) rows per workgroup.
+//   S^T (32 keys x 32 rows) = K Q^T per 32-key half of the 64-key tile: lane
+//   (half, j) holds row j and keys 8 (i / 4) + 4 half + i % 4 in s[i].
+//   P^T operand of key step u (16 keys): element e is key
+//   16 u + 8 (e / 4) + 4 half + e % 4, i.e. s[8 (u % 2) + e] of half u / 2;
+//   the V^T operand reads its key rows in the same order (ds_read_b64_tr_b16:
+//   lane (16-group g, i16) takes 8 B of key row 16 u + 4 half + TR_ROW(i16),
+//   and +8 for the upper four keys, at value chunk 4 ct + 2 (g % 2) +
+//   TR_COL(i16) / 2).
+//   O^T (32 value columns x 32 rows) per value tile ct: lane (half, j) holds
+//   row j, columns 32 ct + 8 (i / 4) + 4 half + i % 4.
 template <bool CAUSAL, int ROWS>
-__global__ void __launch_bounds__(ROWS * 4)
-    __attribute__((amdgpu_waves_per_eu(ROWS / 32, ROWS / 32))) block_sparse_fwd_kernel(BsArgs a) {
+__global__ void __launch_bounds__(ROWS * 2)
+    __attribute__((amdgpu_waves_per_eu(ROWS == 64 ? 1 : 2, ROWS == 64 ? 1 : 2)))
+    block_sparse_fwd_kernel(BsArgs a) {
   constexpr int kRows = ROWS;
-  constexpr int kThreads = ROWS * 4;  // 16 rows per wave
+  constexpr int kThreads = ROWS * 2;  // 32 rows per wave
+  constexpr int kSteps16 = kDQK / 16;  // 32x32x16 K steps over d_qk
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kTile * (kKRow + kVRow)];
   LDS_AS uint8_t* ks = (LDS_AS uint8_t*)lds_raw;
   LDS_AS uint8_t* vs = ks + kTile * kKRow;
@@ -168,27 +171,30 @@ __global__ void __launch_bounds__(ROWS * 4)
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4;
-  const int hl = lane & 15;
+  const int j32 = lane & 31, half = lane >> 5;
   const int item = (int)(blockIdx.x % 8u) * a.per_xcd + (int)(blockIdx.x / 8u);
   if (item >= a.n_sub * a.h_q) return;  // padding of the last XCD range (whole workgroup)
   const int head = item / a.n_sub;
   const int kvh = head / (a.h_q / a.h_kv);
   const int row0 = (item % a.n_sub) * kRows;
-  const int row = row0 + wave * 16 + hl;           // this lane's query row
+  const int row = row0 + wave * 32 + j32;          // this lane's query row
   const int row_last = min(row0 + kRows, a.s) - 1;  // last row of the workgroup
 
-  bf16x8 qf[kSteps];
+  bf16x8 qf[kSteps16];
   {
-    const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * kDQK + g * 8;
+    const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * kDQK + half * 8;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      qf[s] = row < a.s ? *reinterpret_cast<const bf16x8*>(qp + s * 32) : bf16x8{};
+    for (int s = 0; s < kSteps16; ++s)
+      qf[s] = row < a.s ? *reinterpret_cast<const bf16x8*>(qp + s * 16) : bf16x8{};
   }
+  // V^T read: key row offset and chunk byte of this lane (see above).
+  const int i16 = lane & 15, cb = (lane >> 4) & 1;
+  const int vrow = 4 * half + (i16 >> 2);
+  const int vcol = (2 * cb + ((i16 & 3) >> 1)) * 16 + 8 * (i16 & 1);
 
-  f32x4 acc[kDV / 16];
+  f32x16 acc[kDV / 32];
 #pragma unroll
-  for (int ct = 0; ct < kDV / 16; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
   float m_run = -INFINITY;  // running max of the log2-scaled logits
   float l_run = 0.f;        // running sum of exp2(logit - m_run)
 
@@ -199,96 +205,90 @@ __global__ void __launch_bounds__(ROWS * 4)
   TileRegs<kThreads> regs;
   if (have) load_tile(a, kvh, t0, kend, tid, regs);
   while (have) {
-    {
-      __syncthreads();  // the previous tile's readers are done
-      store_tile(ks, vs, tid, regs);
-      __syncthreads();
-      const int key_end = kend;
-      const int tile0 = t0;
-      have = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
-      if (have) load_tile(a, kvh, t0, kend, tid, regs);  // in flight during this tile
+    __syncthreads();  // the previous tile's readers are done
+    store_tile(ks, vs, tid, regs);
+    __syncthreads();
+    const int key_end = kend;
+    const int tile0 = t0;
+    have = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+    if (have) load_tile(a, kvh, t0, kend, tid, regs);  // in flight during this tile
 
-      // S^T: lane (g, hl) gets keys 16 kt + 4g + r of row `row`.
-      f32x4 st[4];
+    f32x16 st[2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 2; ++kt) {
+      st[kt] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 kf =
-              *reinterpret_cast<const LDS_AS bf16x8*>(ks + (kt * 16 + hl) * kKRow + s * 64 + g * 16);
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[kt], 0, 0, 0);
-        }
+      for (int s = 0; s < kSteps16; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(ks + (kt * 32 + j32) * kKRow +
+                                                                  s * 32 + half * 16);
+        st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kt], 0, 0, 0);
       }
-
-      // Mask (keys past the block or the sequence; with CAUSAL keys after
-      // the row), then the online softmax in log2 units.
-      float rmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = tile0 + kt * 16 + 4 * g + r;
-          const bool ok = key < key_end && (!CAUSAL || key <= row);
-          const float x = ok ? st[kt][r] * a.scale_log2 : -INFINITY;
-          st[kt][r] = x;
-          rmax = fmaxf(rmax, x);
-        }
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-      const float m_new = fmaxf(m_run, rmax);
-      // A row with no key yet keeps m = -inf: nothing to add, nothing to scale.
-      const bool live = m_new != -INFINITY;
-      const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      float rsum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = live ? __builtin_amdgcn_exp2f(st[kt][r] - m_new) : 0.f;
-          st[kt][r] = p;
-          rsum += p;
-        }
-      rsum += __shfl_xor(rsum, 16);
-      rsum += __shfl_xor(rsum, 32);
-      l_run = l_run * alpha + rsum;
-      m_run = m_new;
-#pragma unroll
-      for (int ct = 0; ct < kDV / 16; ++ct) acc[ct] *= alpha;
-
-      // P^T operand of key step s2: element e <-> key 32 s2 + 16 (e / 4) + 4g + e % 4.
-      bf16x8 pf[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[s2][e] = (__bf16)st[2 * s2 + (e >> 2)][e & 3];
-
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int ct = 0; ct < kDV / 16; ++ct)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_pair(vs, kVRow, 32 * s2, ct * 16, g, hl),
-                                                            pf[s2], acc[ct], 0, 0, 0);
     }
+
+    // Mask (keys past the block or the sequence; with CAUSAL keys after the
+    // row), then the online softmax in log2 units; a row's 64 logits sit in
+    // lanes j and j + 32.
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = tile0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+        const bool ok = key < key_end && (!CAUSAL || key <= row);
+        const float x = ok ? st[kt][i] * a.scale_log2 : -INFINITY;
+        st[kt][i] = x;
+        rmax = fmaxf(rmax, x);
+      }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float m_new = fmaxf(m_run, rmax);
+    // A row with no key yet keeps m = -inf: nothing to add, nothing to scale.
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    float rsum = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = live ? __builtin_amdgcn_exp2f(st[kt][i] - m_new) : 0.f;
+        rsum += p;
+        pf[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    rsum += __shfl_xor(rsum, 32);
+    l_run = l_run * alpha + rsum;
+    m_run = m_new;
+#pragma unroll
+    for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] *= alpha;
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int ct = 0; ct < kDV / 32; ++ct) {
+        const LDS_AS uint8_t* p = vs + (16 * u + vrow) * kVRow + ct * 64 + vcol;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 8 * kVRow));
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], acc[ct], 0, 0, 0);
+      }
   }
 
   if (row >= a.s) return;
-  // acc[ct][r] = O[row][16 ct + 4g + r] * l_run.
   float inv = 0.f, lse_v = INFINITY;
   if (l_run > 0.f) {
     inv = 1.f / l_run;
     lse_v = (m_run + __log2f(l_run)) * kLn2;
   }
-  __bf16* op = a.out + ((size_t)row * a.h_q + head) * kDV + g * 4;
+  __bf16* op = a.out + ((size_t)row * a.h_q + head) * kDV + 4 * half;
 #pragma unroll
-  for (int ct = 0; ct < kDV / 16; ++ct) {
-    const bf16x4 o4 = {(__bf16)(acc[ct][0] * inv), (__bf16)(acc[ct][1] * inv),
-                       (__bf16)(acc[ct][2] * inv), (__bf16)(acc[ct][3] * inv)};
-    *reinterpret_cast<bf16x4*>(op + ct * 16) = o4;
-  }
-  if (g == 0) a.lse[(size_t)row * a.h_q + head] = lse_v;
+  for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x4 o4 = {(__bf16)(acc[ct][4 * k] * inv), (__bf16)(acc[ct][4 * k + 1] * inv),
+                         (__bf16)(acc[ct][4 * k + 2] * inv), (__bf16)(acc[ct][4 * k + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(op + 32 * ct + 8 * k) = o4;
+    }
+  if (half == 0) a.lse[(size_t)row * a.h_q + head] = lse_v;
 }
 
 // host side
@@ -344,7 +344,7 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
   args.k_block = k_block;
   args.n_kblocks = (int32_t)(((int64_t)s + k_block - 1) / k_block);
   args.scale_log2 = sm_scale * kLog2e;
-  const int rows = q_block % 128 == 0 ? 128 : 64;
+  const int rows = q_block % 256 == 0 ? 256 : q_block % 128 == 0 ? 128 : 64;
   args.n_sub = (s + rows - 1) / rows;
   const int64_t items = (int64_t)args.n_sub * h_q;
   if (items > 0x7fffffffLL - 8)
@@ -352,8 +352,13 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
   args.per_xcd = (int32_t)((items + 7) / 8);
   const dim3 grid((unsigned)(8 * args.per_xcd));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 block((unsigned)(rows * 4));
-  if (rows == 128) {
+  const dim3 block((unsigned)(rows * 2));
+  if (rows == 256) {
+    if (causal)
+      hipLaunchKernelGGL((block_sparse_fwd_kernel<true, 256>), grid, block, 0, st, args);
+    else
+      hipLaunchKernelGGL((block_sparse_fwd_kernel<false, 256>), grid, block, 0, st, args);
+  } else if (rows == 128) {
     if (causal)
       hipLaunchKernelGGL((block_sparse_fwd_kernel<true, 128>), grid, block, 0, st, args);
     else
