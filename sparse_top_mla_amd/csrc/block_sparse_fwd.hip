@@ -90,7 +90,9 @@ __device__ __forceinline__ bool next_tile(const BsArgs& a, int e_end, int row_la
     ++e;
   }
   for (; e < e_end; ++e) {
-    const int b = a.col_idx[e];
+    // A scalar load (the index is wave-uniform and the list read-only): a
+    // vector load would make the wait for it cover the tile copies in flight.
+    const int b = ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)a.col_idx)[e];
     if (b < 0 || b >= a.n_kblocks) continue;
     t0 = b * a.k_block;
     kend = min(t0 + a.k_block, a.s);
@@ -291,6 +293,256 @@ __global__ void __launch_bounds__(ROWS * 2)
   if (half == 0) a.lse[(size_t)row * a.h_q + head] = lse_v;
 }
 
+// ---------------------------------------------------------------------------
+// 256-row workgroups with a 3-stage LDS ring filled by LDS DMA
+// ---------------------------------------------------------------------------
+// The tiles reach LDS by buffer loads in direct-to-LDS mode: 1 KiB per
+// instruction, per-lane source offsets, and keys past the tile and pad
+// chunks outside the buffer's records, so they zero-fill without a branch.
+// No register staging and no LDS stores; tile i + 2 is in flight while tile
+// i is computed, with one barrier per tile.  Each wave copies rows
+// 8w .. 8w + 7 of K (4 copies of 2 rows) and of V (2 copies of 4 rows), so
+// every wave issues 6 copies per tile (a tile past the end zero-fills) and
+// the wait for tile i is vmcnt(6).  LDS stage layout: 64 K rows of 512 B (24
+// data chunks of 16 B, 8 pad chunks; chunk c of row r at c ^ (r % 8)), then
+// 64 V rows of 256 B (chunk c of row r at c ^ 4 (r % 4)), so that the S^T
+// reads (32 rows, one chunk column) and the V^T reads (4 rows and 2 chunks
+// per 16-lane group) hit distinct banks.  The buffer resources sit 3 KiB
+// below the tensors (the instruction offset of a copy, up to 3 KiB, moves
+// the memory address as well as the LDS one).
+constexpr int kKRowD = 512, kVRowD = 256;
+constexpr int kStageD = kTile * (kKRowD + kVRowD);  // 48 KiB
+constexpr int kRingD = 3;
+constexpr uint32_t kBiasD = 3 * 1024;
+constexpr uint32_t kOobD = 0xFFFFE000u;  // + lane chunk + offset: outside, no wrap
+constexpr uint64_t kMaxDmaBytes = kOobD - kBiasD;  // K or V tensor bytes the resources reach
+
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4s dma_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)p - kBiasD;
+  u32x4s rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  rs[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu;  // stride 0
+  rs[2] = __builtin_amdgcn_readfirstlane(bytes + kBiasD);
+  rs[3] = 0x00020000u;  // 32-bit data format, no swizzle
+  return rs;
+}
+
+// One 1 KiB copy: LDS [m0 + OFF + 16 lane, +16) <- records + voff + OFF.
+template <int OFF>
+__device__ __forceinline__ void dma16(const u32x4s& rs, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds"
+               :
+               : "v"(voff), "s"(rs), "i"(OFF), "{m0}"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory");
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+block_sparse_fwd_ring_kernel(BsArgs a) {
+  constexpr int kRows = 256;
+  constexpr int kSteps16 = kDQK / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kRingD * kStageD];
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j32 = lane & 31, half = lane >> 5;
+  const int item = (int)(blockIdx.x % 8u) * a.per_xcd + (int)(blockIdx.x / 8u);
+  if (item >= a.n_sub * a.h_q) return;  // padding of the last XCD range (whole workgroup)
+  const int head = item / a.n_sub;
+  const int kvh = head / (a.h_q / a.h_kv);
+  const int row0 = (item % a.n_sub) * kRows;
+  const int row = row0 + wave * 32 + j32;          // this lane's query row
+  const int row_last = min(row0 + kRows, a.s) - 1;  // last row of the workgroup
+
+  // V^T read: lane (16-group g, i16) takes key rows 4 half + i16 / 4 (+ 16 u,
+  // + 8) at chunk 4 ct + 2 (g % 2) + (i16 % 4) / 2, byte 8 (i16 % 2); the
+  // swizzle term 4 (row % 4) is 4 ((i16 / 4) % 4) for all of them.
+  const int i16 = lane & 15, cb = (lane >> 4) & 1;
+  const int vrow = 4 * half + (i16 >> 2);
+  const int vchunk = 2 * cb + ((i16 & 3) >> 1), vswz = 4 * ((i16 >> 2) & 3), vbyte = 8 * (i16 & 1);
+
+  // Copy constants of this lane (rows relative to the tile start).
+  const u32x4s rk = dma_rsrc(a.k, (uint32_t)((uint64_t)a.s * a.h_kv * (kDQK * 2)));
+  const u32x4s rv = dma_rsrc(a.v, (uint32_t)((uint64_t)a.s * a.h_kv * (kDV * 2)));
+  const uint32_t kstride = (uint32_t)a.h_kv * (kDQK * 2), vstride = (uint32_t)a.h_kv * (kDV * 2);
+  // Copies of one tile (t0: first key, nk: keys, 0 for a zero-fill) into stage st.
+  auto issue = [&](int st, int t0, int nk) {
+    const uint32_t kb = (uint32_t)(uintptr_t)(lds + st * kStageD + 8 * wave * kKRowD);
+    const uint32_t vb = (uint32_t)(uintptr_t)(lds + st * kStageD + kTile * kKRowD + 8 * wave * kVRowD);
+    const int ln = lane_id();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * wave + 2 * k + (ln >> 5);
+      const int c = (ln & 31) ^ ((2 * k + (ln >> 5)) & 7);
+      const uint32_t off = (uint32_t)(t0 + r) * kstride + (uint32_t)kvh * (kDQK * 2) +
+                           (uint32_t)c * 16u + kBiasD - (uint32_t)k * 1024u;
+      const uint32_t voff = r < nk && c < 24 ? off : kOobD;
+      switch (k) {
+        case 0: dma16<0>(rk, voff, kb); break;
+        case 1: dma16<1024>(rk, voff, kb); break;
+        case 2: dma16<2048>(rk, voff, kb); break;
+        default: dma16<3072>(rk, voff, kb); break;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = 8 * wave + 4 * k + (ln >> 4);
+      const int c = (ln & 15) ^ (4 * ((ln >> 4) & 3));
+      const uint32_t off = (uint32_t)(t0 + r) * vstride + (uint32_t)kvh * (kDV * 2) +
+                           (uint32_t)c * 16u + kBiasD - (uint32_t)k * 1024u;
+      const uint32_t voff = r < nk ? off : kOobD;
+      if (k == 0) dma16<0>(rv, voff, vb);
+      else dma16<1024>(rv, voff, vb);
+    }
+  };
+
+  f32x16 acc[kDV / 32];
+#pragma unroll
+  for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
+  float m_run = -INFINITY;  // running max of the log2-scaled logits
+  float l_run = 0.f;        // running sum of exp2(logit - m_run)
+
+  const int qb = row0 / a.q_block;
+  const int e_end = a.row_ptr[qb + 1];
+  int e = a.row_ptr[qb], t0 = -1, kend = 0;
+  // Tiles i, i + 1 (first key, keys in the tile) and whether they exist.
+  bool h0 = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+  int t0_0 = t0, n_0 = h0 ? min(kTile, kend - t0) : 0;
+  issue(0, t0_0, n_0);
+  bool h1 = h0 && next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+  int t0_1 = t0, n_1 = h1 ? min(kTile, kend - t0) : 0;
+  issue(1, t0_1, n_1);
+  // The query slice lands with the first two tiles; the wait is the
+  // compiler's own, so it knows nothing is in flight inside the loop.
+  bf16x8 qf[kSteps16];
+  {
+    const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * kDQK + half * 8;
+#pragma unroll
+    for (int s = 0; s < kSteps16; ++s)
+      qf[s] = row < a.s ? *reinterpret_cast<const bf16x8*>(qp + s * 16) : bf16x8{};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  int st = 0;
+  while (h0) {
+    // Tile i has landed (tile i + 1's copies may stay in flight); the
+    // barrier also says every wave is done with tile i - 1's stage.
+    __builtin_amdgcn_s_waitcnt((6 & 15) | (7 << 4) | (15 << 8));  // vmcnt(6) only
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool h2 = h1 && next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+    const int t0_2 = t0, n_2 = h2 ? min(kTile, kend - t0) : 0;
+    issue(st == 0 ? 2 : st - 1, t0_2, n_2);  // stage (st + 2) % 3
+
+    const LDS_AS uint8_t* ks = lds + st * kStageD;
+    const LDS_AS uint8_t* vs = ks + kTile * kKRowD;
+    const int tile0 = t0_0, key_end = t0_0 + n_0;
+    f32x16 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sc[kt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < kSteps16; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(
+            ks + (kt * 32 + j32) * kKRowD + (((2 * s + half) ^ (j32 & 7)) << 4));
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kt], 0, 0, 0);
+      }
+    }
+    // Mask (keys past the tile; with CAUSAL keys after the row; a tile wholly
+    // inside both bounds for every row of the workgroup needs none), then the
+    // online softmax in log2 units; a row's 64 logits sit in lanes j, j + 32.
+    const bool full = tile0 + kTile <= key_end && (!CAUSAL || tile0 + kTile - 1 <= row0);
+    // The max is taken on the raw logits (the scale is positive) and the
+    // scale folds into the exponent.
+    float rmax = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, sc[kt][i]);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = tile0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
+          const bool ok = key < key_end && (!CAUSAL || key <= row);
+          const float x = ok ? sc[kt][i] : -INFINITY;
+          sc[kt][i] = x;
+          rmax = fmaxf(rmax, x);
+        }
+    }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32)) * a.scale_log2;
+    // Lazy rescale: the reference m_run moves only when a row's logit
+    // exceeds it by more than 8 (log2 units), so P stays below 2^8 and O and
+    // l are rescaled in few tiles (a wave-uniform branch; the first tile with
+    // a key sets the reference).  Only rounding differs from rescaling at
+    // every new maximum.
+    const bool grow = rmax > m_run + 8.f;  // m_run = -inf: any key grows it
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? rmax : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] *= alpha;
+      m_run = m_new;
+    }
+    // A row without a key so far has only -inf logits here: exp2 gives 0.
+    const float neg = m_run != -INFINITY ? -m_run : 0.f;
+    float rsum = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][i], a.scale_log2, neg));
+        rsum += p;
+        pf[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    rsum += __shfl_xor(rsum, 32);
+    l_run += rsum;
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int ct = 0; ct < kDV / 32; ++ct) {
+        const LDS_AS uint8_t* p =
+            vs + (16 * u + vrow) * kVRowD + (((4 * ct + vchunk) ^ vswz) << 4) + vbyte;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 8 * kVRowD));
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], acc[ct], 0, 0, 0);
+      }
+    h0 = h1;
+    t0_0 = t0_1;
+    n_0 = n_1;
+    h1 = h2;
+    t0_1 = t0_2;
+    n_1 = n_2;
+    st = st == 2 ? 0 : st + 1;
+  }
+  // The zero-fill copies past the last tile may still be landing.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  if (row >= a.s) return;
+  float inv = 0.f, lse_v = INFINITY;
+  if (l_run > 0.f) {
+    inv = 1.f / l_run;
+    lse_v = (m_run + __log2f(l_run)) * kLn2;
+  }
+  __bf16* op = a.out + ((size_t)row * a.h_q + head) * kDV + 4 * half;
+#pragma unroll
+  for (int ct = 0; ct < kDV / 32; ++ct)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x4 o4 = {(__bf16)(acc[ct][4 * k] * inv), (__bf16)(acc[ct][4 * k + 1] * inv),
+                         (__bf16)(acc[ct][4 * k + 2] * inv), (__bf16)(acc[ct][4 * k + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(op + 32 * ct + 8 * k) = o4;
+    }
+  if (half == 0) a.lse[(size_t)row * a.h_q + head] = lse_v;
+}
+
 // host side
 
 smla_status bs_fail(smla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -353,7 +605,13 @@ extern "C" smla_status sparse_mla_block_sparse_fwd(const void* q, const void* k,
   const dim3 grid((unsigned)(8 * args.per_xcd));
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 block((unsigned)(rows * 2));
-  if (rows == 256) {
+  const bool dma = (uint64_t)s * h_kv * (kDQK * 2) <= kMaxDmaBytes;
+  if (rows == 256 && dma) {
+    if (causal)
+      hipLaunchKernelGGL((block_sparse_fwd_ring_kernel<true>), grid, block, 0, st, args);
+    else
+      hipLaunchKernelGGL((block_sparse_fwd_ring_kernel<false>), grid, block, 0, st, args);
+  } else if (rows == 256) {
     if (causal)
       hipLaunchKernelGGL((block_sparse_fwd_kernel<true, 256>), grid, block, 0, st, args);
     else
