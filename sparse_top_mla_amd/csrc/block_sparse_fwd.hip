@@ -37,6 +37,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 #include "sparse_mla.h"
 
@@ -299,15 +300,16 @@ __global__ void __launch_bounds__(ROWS * 2)
 // The tiles reach LDS by buffer loads in direct-to-LDS mode: 1 KiB per
 // instruction, per-lane source offsets, and keys past the tile and pad
 // chunks outside the buffer's records, so they zero-fill without a branch.
-// No register staging and no LDS stores; tile i + 2 is in flight while tile
-// i is computed, with one barrier per tile.  Each wave copies rows
-// 8w .. 8w + 7 of K (4 copies of 2 rows) and of V (2 copies of 4 rows), so
-// every wave issues 6 copies per tile (a tile past the end zero-fills) and
-// the wait for tile i is vmcnt(6).  LDS stage layout: 64 K rows of 512 B (24
-// data chunks of 16 B, 8 pad chunks; chunk c of row r at c ^ (r % 8)), then
-// 64 V rows of 256 B (chunk c of row r at c ^ 4 (r % 4)), so that the S^T
-// reads (32 rows, one chunk column) and the V^T reads (4 rows and 2 chunks
-// per 16-lane group) hit distinct banks.  The buffer resources sit 3 KiB
+// No register staging and no LDS stores; one barrier per tile (the step
+// loop below says which tiles are in flight).  Each wave copies rows
+// 8w .. 8w + 7 of K (4 copies of 2 rows) and of V (2 copies of 4 rows).
+// LDS stage layout: 64 K rows of 512 B (24 data chunks of 16 B, 8 pad
+// chunks; chunk c of row r at c ^ (r % 16): a data chunk may land in the pad
+// range and the other way round), then 64 V rows of 256 B (chunk c of row r
+// at c ^ 4 (r % 4)).  The S^T reads (32 rows, one chunk column) and the V^T
+// reads (4 rows and 2 chunks per 16-lane group) are free of bank conflicts:
+// SQ_LDS_BANK_CONFLICT reads 0, against 37% of the LDS cycles with the K
+// swizzle c ^ (r % 8), which took 2% more time.  The buffer resources sit 3 KiB
 // below the tensors (the instruction offset of a copy, up to 3 KiB, moves
 // the memory address as well as the LDS one).
 constexpr int kKRowD = 512, kVRowD = 256;
@@ -376,7 +378,7 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 8 * wave + 2 * k + (ln >> 5);
-      const int c = (ln & 31) ^ ((2 * k + (ln >> 5)) & 7);
+      const int c = (ln & 31) ^ ((8 * wave + 2 * k + (ln >> 5)) & 15);
       const uint32_t off = (uint32_t)(t0 + r) * kstride + (uint32_t)kvh * (kDQK * 2) +
                            (uint32_t)c * 16u + kBiasD - (uint32_t)k * 1024u;
       const uint32_t voff = r < nk && c < 24 ? off : kOobD;
@@ -402,21 +404,23 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
   f32x16 acc[kDV / 32];
 #pragma unroll
   for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
-  float m_run = -INFINITY;  // running max of the log2-scaled logits
-  float l_run = 0.f;        // running sum of exp2(logit - m_run)
+  float m_run = -INFINITY;  // reference of the log2-scaled logits (see the lazy rescale)
+  float l_run = 0.f;        // sum of exp2(logit - m_run)
 
   const int qb = row0 / a.q_block;
   const int e_end = a.row_ptr[qb + 1];
   int e = a.row_ptr[qb], t0 = -1, kend = 0;
-  // Tiles i, i + 1 (first key, keys in the tile) and whether they exist.
+  // Tile i sits in stage i % 3.  Step i waits for tile i (issued in step
+  // i - 1); the barrier then also says that tile i - 2's stage is free (its
+  // P*V ran in step i - 1), and tile i + 1 goes there.  Then S^T of tile i,
+  // and P*V of tile i - 1 with tile i's softmax placed between its MFMAs
+  // (the two are independent: the rescale that tile i may call for is
+  // applied to O after the P*V of tile i - 1).
   bool h0 = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
   int t0_0 = t0, n_0 = h0 ? min(kTile, kend - t0) : 0;
-  issue(0, t0_0, n_0);
-  bool h1 = h0 && next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
-  int t0_1 = t0, n_1 = h1 ? min(kTile, kend - t0) : 0;
-  issue(1, t0_1, n_1);
-  // The query slice lands with the first two tiles; the wait is the
-  // compiler's own, so it knows nothing is in flight inside the loop.
+  if (h0) issue(0, t0_0, n_0);
+  // The query slice lands with the first tile; the wait is the compiler's
+  // own, so it knows nothing is in flight inside the loop.
   bf16x8 qf[kSteps16];
   {
     const __bf16* qp = a.q + ((size_t)row * a.h_q + head) * kDQK + half * 8;
@@ -425,18 +429,25 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
       qf[s] = row < a.s ? *reinterpret_cast<const bf16x8*>(qp + s * 16) : bf16x8{};
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  int st = 0;
-  while (h0) {
-    // Tile i has landed (tile i + 1's copies may stay in flight); the
-    // barrier also says every wave is done with tile i - 1's stage.
-    __builtin_amdgcn_s_waitcnt((6 & 15) | (7 << 4) | (15 << 8));  // vmcnt(6) only
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const bool h2 = h1 && next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
-    const int t0_2 = t0, n_2 = h2 ? min(kTile, kend - t0) : 0;
-    issue(st == 0 ? 2 : st - 1, t0_2, n_2);  // stage (st + 2) % 3
 
-    const LDS_AS uint8_t* ks = lds + st * kStageD;
-    const LDS_AS uint8_t* vs = ks + kTile * kKRowD;
+  // The lane pair max / sum over lanes j and j + 32 (v_permlane32_swap).
+  auto pair = [](float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const unsigned v = (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0xE4, 0xF, 0xF, false);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+    return uint2{r[0], r[1]};
+  };
+  bf16x8 pprev[4];  // P^T operands of the previous tile
+  int st = 0;
+  auto step = [&](auto do_pv) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int cur = st, nxt = st == 2 ? 0 : st + 1, prv = st == 0 ? 2 : st - 1;
+    const bool h1 = next_tile<CAUSAL>(a, e_end, row_last, e, t0, kend);
+    const int t0_1 = t0, n_1 = h1 ? min(kTile, kend - t0) : 0;
+    if (h1) issue(nxt, t0_1, n_1);
+
+    const LDS_AS uint8_t* ks = lds + cur * kStageD;
+    const LDS_AS uint8_t* vs = lds + prv * kStageD + kTile * kKRowD;  // tile i - 1's V
     const int tile0 = t0_0, key_end = t0_0 + n_0;
     f32x16 sc[2];
 #pragma unroll
@@ -445,64 +456,96 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
 #pragma unroll
       for (int s = 0; s < kSteps16; ++s) {
         const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(
-            ks + (kt * 32 + j32) * kKRowD + (((2 * s + half) ^ (j32 & 7)) << 4));
+            ks + (kt * 32 + j32) * kKRowD + (((2 * s + half) ^ (j32 & 15)) << 4));
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kt], 0, 0, 0);
       }
     }
-    // Mask (keys past the tile; with CAUSAL keys after the row; a tile wholly
-    // inside both bounds for every row of the workgroup needs none), then the
-    // online softmax in log2 units; a row's 64 logits sit in lanes j, j + 32.
+    // Tile i's softmax, in pieces: mask (keys past the tile; with CAUSAL keys
+    // after the row; a tile wholly inside both bounds for every row of the
+    // workgroup needs none), the max of the raw logits (the scale is
+    // positive), the lazy-rescale decision (the reference moves only when a
+    // logit exceeds it by more than 8 in log2 units, so P stays below 2^8),
+    // then P with the scale folded into the exponent, and the sum.
     const bool full = tile0 + kTile <= key_end && (!CAUSAL || tile0 + kTile - 1 <= row0);
-    // The max is taken on the raw logits (the scale is positive) and the
-    // scale folds into the exponent.
-    float rmax = -INFINITY;
-    if (full) {
+    float rmax = -INFINITY, alpha = 1.f, neg = 0.f, rsum = 0.f;
+    bool grow = false;
+    bf16x8 pf[4];
+    auto sm_piece = [&](int n) {
+      if (n < 2) {
+        if (!full) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) rmax = fmaxf(rmax, sc[kt][i]);
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = tile0 + 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool ok = key < key_end && (!CAUSAL || key <= row);
-          const float x = ok ? sc[kt][i] : -INFINITY;
-          sc[kt][i] = x;
-          rmax = fmaxf(rmax, x);
+          for (int i = 0; i < 16; ++i) {
+            const int key = tile0 + 32 * n + 8 * (i >> 2) + 4 * half + (i & 3);
+            const bool ok = key < key_end && (!CAUSAL || key <= row);
+            sc[n][i] = ok ? sc[n][i] : -INFINITY;
+          }
         }
+      } else if (n == 2) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
+        rmax = m;
+      } else if (n == 3) {
+        const uint2 r = pair(rmax);
+        rmax = fmaxf(__builtin_bit_cast(float, r.x), __builtin_bit_cast(float, r.y)) * a.scale_log2;
+        grow = rmax > m_run + 8.f;  // m_run = -inf: any key grows it
+        if (grow) {
+          alpha = __builtin_amdgcn_exp2f(m_run - rmax);
+          m_run = rmax;
+        }
+        // a row without a key so far has only -inf logits: exp2 gives 0
+        neg = m_run != -INFINITY ? -m_run : 0.f;
+      } else if (n < 12) {
+        const int q = n - 4;  // values 4q .. 4q + 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = 4 * q + i, kt = v >> 4, ii = v & 15;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][ii], a.scale_log2, neg));
+          rsum += p;
+          pf[2 * kt + (ii >> 3)][ii & 7] = (__bf16)p;
+        }
+      } else if (n == 12) {
+        const uint2 r = pair(rsum);
+        rsum = __builtin_bit_cast(float, r.x) + __builtin_bit_cast(float, r.y);
+      }
+    };
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      if constexpr (decltype(do_pv)::value) {
+        // O^T += V^T P^T of tile i - 1: key step u = n / 4, value tile ct = n % 4
+        const int u = n >> 2, ct = n & 3;
+        const LDS_AS uint8_t* p =
+            vs + (16 * u + vrow) * kVRowD + (((4 * ct + vchunk) ^ vswz) << 4) + vbyte;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 8 * kVRowD));
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pprev[u], acc[ct], 0, 0, 0);
+      }
+      sm_piece(n);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32)) * a.scale_log2;
-    // Lazy rescale: the reference m_run moves only when a row's logit
-    // exceeds it by more than 8 (log2 units), so P stays below 2^8 and O and
-    // l are rescaled in few tiles (a wave-uniform branch; the first tile with
-    // a key sets the reference).  Only rounding differs from rescaling at
-    // every new maximum.
-    const bool grow = rmax > m_run + 8.f;  // m_run = -inf: any key grows it
+    // The rescale tile i called for, after tile i - 1's P*V (a wave-uniform
+    // branch: rare once the reference has settled).
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? rmax : m_run;
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      l_run *= alpha;
 #pragma unroll
       for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] *= alpha;
-      m_run = m_new;
     }
-    // A row without a key so far has only -inf logits here: exp2 gives 0.
-    const float neg = m_run != -INFINITY ? -m_run : 0.f;
-    float rsum = 0.f;
-    bf16x8 pf[4];
+    l_run = l_run * alpha + rsum;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][i], a.scale_log2, neg));
-        rsum += p;
-        pf[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    rsum += __shfl_xor(rsum, 32);
-    l_run += rsum;
-    // O^T += V^T P^T.
+    for (int u = 0; u < 4; ++u) pprev[u] = pf[u];
+    h0 = h1;
+    t0_0 = t0_1;
+    n_0 = n_1;
+    st = nxt;
+  };
+  if (h0) {
+    step(std::false_type{});
+    while (h0) step(std::true_type{});
+    // P*V of the last tile (stage st - 1).
+    __syncthreads();
+    const LDS_AS uint8_t* vs = lds + (st == 0 ? 2 : st - 1) * kStageD + kTile * kKRowD;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -512,18 +555,9 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 8 * kVRowD));
         const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pprev[u], acc[ct], 0, 0, 0);
       }
-    h0 = h1;
-    t0_0 = t0_1;
-    n_0 = n_1;
-    h1 = h2;
-    t0_1 = t0_2;
-    n_1 = n_2;
-    st = st == 2 ? 0 : st + 1;
   }
-  // The zero-fill copies past the last tile may still be landing.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   if (row >= a.s) return;
   float inv = 0.f, lse_v = INFINITY;
