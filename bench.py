@@ -510,7 +510,7 @@ def kernel_file(workload):
 def kernel_name(workload):
     """Name fragment of the workload's dominant kernel in rocprofv3 records."""
     return {"bwd_h64": "sparse_mla_bwd_kernel",
-            "block_sparse_h8": "block_sparse_fwd_kernel"}.get(workload, "sparse_mla_fwd")
+            "block_sparse_h8": "block_sparse_fwd"}.get(workload, "sparse_mla_fwd")
 
 
 def kernel_source_digest(workload=None):
