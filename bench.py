@@ -56,8 +56,9 @@ def parse():
                          "and pmc_copy_<counter>/), and the MFMA-busy runs (pmc_<workload>_MFMA/), into "
                          "profiles/traffic_<workload>.json; no GPU needed")
     ap.add_argument("--attainable", action="store_true",
-                    help="measure this device's attainable dense bf16 MFMA rate (an MFMA loop) and HBM "
-                         "bandwidth (a streaming copy) into profiles/attainable_peaks.json")
+                    help="measure this device's attainable dense bf16 MFMA rate (an MFMA loop), HBM "
+                         "bandwidth (a read stream and a copy) and fp32 atomic-add rate into "
+                         "profiles/attainable_peaks.json")
     ap.add_argument("--groups", type=int, default=7,
                     help="groups of 20 back-to-back calls for the pages' statistic (0: none, e.g. "
                          "under a profiler)")
@@ -785,9 +786,25 @@ def attainable_peaks():
     read_ms = statistics.median(time_groups(read, groups=7, per_group=3))
     dst = torch.empty_like(src)
     copy_ms = statistics.median(time_groups(lambda: dst.copy_(src), groups=7, per_group=3))
+    del src, dst
+    lib.smla_probe_atomic_add.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.smla_probe_atomic_count.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.smla_probe_atomic_count.restype = ctypes.c_longlong
+    arows, ablocks, aiters = 4096, props.multi_processor_count * 8, 128
+    acc = torch.zeros(arows * 576, dtype=torch.float32, device="cuda:0")
+    atom = lambda: lib.smla_probe_atomic_add(acc.data_ptr(), arows, ablocks, aiters, stream)  # noqa: E731
+    assert atom() == 0
+    atom_ms = statistics.median(time_groups(atom, groups=7, per_group=3))
+    adds = lib.smla_probe_atomic_count(ablocks, aiters)
     return {"mfma_tflops": flops / (mfma_ms * 1e-3) / 1e12,
             "hbm_read_gbs": n / (read_ms * 1e-3) / 1e9,
             "hbm_gbs": 2.0 * n / (copy_ms * 1e-3) / 1e9,
+            "atomic_add_gps": adds / (atom_ms * 1e-3) / 1e9,
+            "atomic_probe": f"{ablocks} workgroups of 256 threads x {aiters} x 9 fp32 "
+                            f"global_atomic_add_f32 (4 hashed rows x 16 words per instruction) "
+                            f"into a [{arows}][576] accumulator, median of 7 group means of 3 "
+                            f"launches: {atom_ms:.3f} ms",
             "mfma_probe": f"{blocks} workgroups x 8 waves x {iters} x 4 independent "
                           f"v_mfma_f32_32x32x16_bf16, median of 7 group means of 3 launches: "
                           f"{mfma_ms:.3f} ms",
@@ -976,6 +993,15 @@ def main():
         result["attainable"] = {"mfma_tflops": p["mfma_tflops"], "hbm_copy_gbs": p["hbm_gbs"],
                                 "hbm_read_gbs": p.get("hbm_read_gbs"),
                                 "frac_of_attainable": result["roofline"]["achieved"] / att}
+        if bwd and p.get("atomic_add_gps"):
+            # The dkv reduction is one fp32 atomic add per valid (row, key)
+            # pair and d_qk column: its time at the probe's rate is a floor.
+            adds = float(counts["valid_pairs"]) * case.d_qk
+            floor_ms = adds / (p["atomic_add_gps"] * 1e9) * 1e3
+            result["atomic_bound"] = {"adds_per_call": adds,
+                                      "attainable_adds_per_s": p["atomic_add_gps"] * 1e9,
+                                      "floor_ms": floor_ms,
+                                      "frac": floor_ms / main_rec["kernel_ms"]}
     if args.cpu_seconds > 0 and bwd:
         result["cpu_baseline"] = cpu_baseline_bwd(case, counts, args.cpu_seconds)
     elif args.cpu_seconds > 0 and bs:

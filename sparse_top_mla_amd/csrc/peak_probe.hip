@@ -10,6 +10,13 @@
 // flight per lane, grid-stride) and writes one word per thread: the HBM rate
 // a read-dominated kernel can attain (the decode gathers are about 95%
 // reads), beside the read+write rate of a device copy.
+//
+// smla_probe_atomic_add adds 1.0 to fp32 words of a [rows][576] accumulator
+// with global_atomic_add_f32 (no return), in the backward's scatter pattern:
+// per wave instruction, four hashed rows x 16 consecutive words, nine
+// instructions per row group covering a wave's quarter of the 576 columns.
+// The host divides the adds by the time: the fp32 atomic-add rate this device
+// sustains, the floor of a kernel whose reduction is an atomic scatter.
 
 #include <hip/hip_runtime.h>
 
@@ -61,9 +68,48 @@ __global__ void __launch_bounds__(256) stream_read(const u32x4* __restrict__ p, 
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+constexpr int kAtomCols = 576;
+
+__global__ void __launch_bounds__(256) atomic_scatter(float* acc, uint32_t rows, int iters) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, hl = lane & 15;
+  const uint32_t seed = blockIdx.x * 977u + wave * 131u + 13u;
+  for (int it = 0; it < iters; ++it) {
+    const uint32_t row = mix32(seed + 4u * it + g) % rows;
+    float* p = acc + (size_t)row * kAtomCols + wave * (kAtomCols / 4) + hl;
+#pragma unroll
+    for (int c = 0; c < kAtomCols / 64; ++c)
+      __hip_atomic_fetch_add(p + 16 * c, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Atomic scatter into `acc` ([rows][576] fp32, rows > 0) with `blocks`
+// workgroups of 256 threads, each thread issuing iters * 9 adds of 1.0.
+// Returns 0 or the HIP error code of the launch.
+int smla_probe_atomic_add(float* acc, int rows, int blocks, int iters, void* stream) {
+  if (!acc || rows <= 0 || blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(atomic_scatter, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), acc, (uint32_t)rows, iters);
+  return (int)hipGetLastError();
+}
+
+// fp32 adds one atomic-probe launch issues.
+long long smla_probe_atomic_count(int blocks, int iters) {
+  return (long long)blocks * 256 * iters * (kAtomCols / 64);
+}
 
 // Reads `bytes` (a multiple of 16) from `src` with `blocks` workgroups of 256
 // threads; `out` holds blocks * 256 words.  Returns 0 or the HIP error code.
