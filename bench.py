@@ -993,7 +993,10 @@ def main():
         result["attainable"] = {"mfma_tflops": p["mfma_tflops"], "hbm_copy_gbs": p["hbm_gbs"],
                                 "hbm_read_gbs": p.get("hbm_read_gbs"),
                                 "frac_of_attainable": result["roofline"]["achieved"] / att}
-        if bwd and p.get("atomic_add_gps"):
+        if bwd:
+            import sparse_top_mla_amd as smla
+            result["dkv_path"] = smla.last_kernel()
+        if bwd and p.get("atomic_add_gps") and result.get("dkv_path") == "bwd_scatter":
             # The dkv reduction is one fp32 atomic add per valid (row, key)
             # pair and d_qk column: its time at the probe's rate is a floor.
             adds = float(counts["valid_pairs"]) * case.d_qk

@@ -218,16 +218,25 @@ smla_status sparse_mla_row_lengths(const int32_t *indices, const int32_t *topk_l
  *   attn_sink     fp32 [h_q] or NULL     the sink the forward used
  *   lse_base2     0: natural-log lse, 1: base-2 lse
  *   workspace     device memory of sparse_mla_bwd_workspace_bytes(s_q, s_kv,
- *                 d_qk) bytes, 16-byte aligned (the fp32 dkv accumulator and
- *                 the row lengths); no initialisation needed, garbage after;
- *                 calls that overlap on one workspace race
+ *                 d_qk) bytes, 16-byte aligned (the fp32 dkv accumulator, the
+ *                 row lengths and, where s_kv <= 16384 and s_q * s_kv <= 2^28,
+ *                 per-row statistics and key bitmaps of s_q * s_kv / 8 bytes);
+ *                 no initialisation needed, garbage after; calls that overlap
+ *                 on one workspace race
  *   dq            bf16 [s_q, h_q, d_qk]  (output)
  *   dkv           bf16 [s_kv, 1, d_qk]   (output; rows no query names are 0)
  *   d_sink        fp32 [h_q] or NULL     (output, needs attn_sink):
  *                 -sum_i exp(sink[h] - lse'_ih) (dout_ih . out_ih)
- * Supported: h_q = 64, h_kv = 1, d_qk 512 or 576, d_v = 512.  The dkv sums
- * are accumulated in a run-dependent order (fp32 atomics).  Four kernels are
- * enqueued on `stream` (zero fill, row lengths, backward, dkv conversion).
+ * Supported: h_q = 64, h_kv = 1, d_qk 512 or 576, d_v = 512.  Two ways to
+ * sum dkv, both in a run-dependent order (fp32 atomics):
+ *   where the workspace holds the bitmaps and s_kv <= 8 topk, a key-outer
+ *   pass ("bwd_key_outer" in sparse_mla_last_kernel): per block of 64 KV rows
+ *   and chunk of 128 query rows, P and dS are recomputed for the rows that
+ *   name a key of the block and dK + dV summed in registers, one atomic add
+ *   per element of the block; rows that name a key twice scatter per pair;
+ *   otherwise the row pass scatters every (row, key) pair ("bwd_scatter").
+ * Enqueued on `stream`: zero fill, row lengths, [key bitmaps], the row pass
+ * (dq, d_sink, and the scattered dkv), [the key-outer pass], dkv conversion.
  */
 size_t sparse_mla_bwd_workspace_bytes(int32_t s_q, int32_t s_kv, int32_t d_qk);
 
@@ -271,9 +280,10 @@ smla_status sparse_mla_block_sparse_fwd(const void *q, const void *k, const void
 const char *sparse_mla_last_error(void);
 
 /* Thread-local name of the attention kernel that the last call of
- * sparse_mla_fwd, sparse_mla_decode_fwd, sparse_mla_decode_fwd_split or
- * sparse_mla_decode_fwd_split_noalloc on this thread launched ("" if it
- * launched none, or the last such call was another entry point):
+ * sparse_mla_fwd, sparse_mla_decode_fwd, sparse_mla_decode_fwd_split,
+ * sparse_mla_decode_fwd_split_noalloc or sparse_mla_bwd on this thread
+ * launched ("" if it launched none, or the last such call was another entry
+ * point):
  *   "ring"        128 heads, rows of at most 2048 index positions
  *   "wide"        64 heads, or 128 heads with longer rows
  *   "ring_split"  split decode at 128 heads, at most 2048 positions per
@@ -282,7 +292,8 @@ const char *sparse_mla_last_error(void);
  *   "heads16"     every other head count, and KV tables whose rows the
  *                 others cannot address (above about 550 GB)
  * with a suffix "_big" on all but the last for KV tables above 4 GiB, which
- * those kernels address through a buffer resource rebased per copied row.
+ * those kernels address through a buffer resource rebased per copied row;
+ * and for the backward "bwd_key_outer" or "bwd_scatter", its dkv path.
  * The string is static; it is for tests and tools and is not an error
  * channel. */
 const char *sparse_mla_last_kernel(void);

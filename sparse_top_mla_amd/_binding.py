@@ -407,7 +407,8 @@ def block_sparse_fwd(q, k, v, q2k_row_ptr, q2k_col_idx, q_block, k_block, sm_sca
 
 
 def last_kernel():
-    """Name of the attention kernel the last forward or decode call on this
-    thread launched ("ring", "wide", "ring_split", "split", "heads16", all but
-    the last with "_big" for KV tables above 4 GiB; "" for none)."""
+    """Name of the attention kernel the last forward, decode or backward call
+    on this thread launched ("ring", "wide", "ring_split", "split", "heads16",
+    all but the last with "_big" for KV tables above 4 GiB; "bwd_key_outer" or
+    "bwd_scatter" for the backward's dkv path; "" for none)."""
     return load_library().sparse_mla_last_kernel().decode()

@@ -2678,3 +2678,6 @@ __attribute__((visibility("hidden"))) smla_status smla_report(smla_status s, con
   return s;
 }
 __attribute__((visibility("hidden"))) void smla_clear_error() { g_last_error.clear(); }
+__attribute__((visibility("hidden"))) void smla_set_last_kernel(const char* name) {
+  g_last_kernel = name;
+}

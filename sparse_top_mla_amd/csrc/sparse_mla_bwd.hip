@@ -45,12 +45,14 @@
 // Error reporting shared with the forward's host code (same library).
 __attribute__((visibility("hidden"))) smla_status smla_report(smla_status s, const char* msg);
 __attribute__((visibility("hidden"))) void smla_clear_error();
+__attribute__((visibility("hidden"))) void smla_set_last_kernel(const char* name);
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -78,6 +80,10 @@ struct BwdArgs {
   __bf16* dq;               // [s_q][64][D]
   float* dkv_acc;           // [s_kv][D], zeroed before the launch
   float* d_sink;            // [64] or null, zeroed before the launch
+  float* stats_out;         // [s_q][128] or null: per head the row's normaliser in
+                            // log2 units (0..63), then dout . out (64..127)
+  const int32_t* dup;       // [s_q]: 1 where the row names a key twice (key-outer mode)
+  int32_t key_outer;        // 1: dkv comes from the key-outer pass, except rows with dup
   int32_t s_q, s_kv, topk;
   float scale;              // sm_scale
   float lse_to_log2;        // log2(e) for natural-log lse, 1 for base-2 lse
@@ -143,6 +149,8 @@ sparse_mla_bwd_kernel(BwdArgs a) {
   const int head = wave * 16 + hl;
   const int row = blockIdx.x;
   const size_t rh = (size_t)row * kHeads + head;
+  // Whether this row scatters its own dkv (the same in every wave).
+  const bool scatter = a.key_outer == 0 || a.dup[row] != 0;
 
   // dO in registers: fragments of dP^T's B operand (own head) ...
   const __bf16* dop = a.dout + rh * kDV + g * 8;
@@ -160,26 +168,26 @@ sparse_mla_bwd_kernel(BwdArgs a) {
   delta += __shfl_xor(delta, 32);
 
   // ... and of dV's B operand (all 64 heads, this wave's value columns),
-  // read transposed from a staged copy of the row's dO.
-  {
+  // read transposed from a staged copy of the row's dO (rows that scatter).
+  bf16x8 dov[2][T::kWaveTiles];
+  const int ct0 = wave * T::kWaveTiles;
+  if (scatter) {
     const __bf16* drow = a.dout + (size_t)row * kHeads * kDV;
     for (int c = tid; c < kHeads * (kDV / 8); c += kWaves * 64) {
       const int h = c / (kDV / 8), ch = c % (kDV / 8);
       *reinterpret_cast<LDS_AS u32x4*>(qs + h * T::kDoRow + ch * 16) =
           *reinterpret_cast<const u32x4*>(drow + h * kDV + ch * 8);
     }
+    __syncthreads();
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int c = 0; c < T::kWaveTiles; ++c) {
+        const int ct = ct0 + c < kDV / 16 ? ct0 + c : 0;  // unused past the value columns
+        dov[hs][c] = tr_pair(qs, T::kDoRow, 32 * hs, ct * 16, g, hl);
+      }
+    __syncthreads();
   }
-  __syncthreads();
-  bf16x8 dov[2][T::kWaveTiles];
-  const int ct0 = wave * T::kWaveTiles;
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-    for (int c = 0; c < T::kWaveTiles; ++c) {
-      const int ct = ct0 + c < kDV / 16 ? ct0 + c : 0;  // unused past the value columns
-      dov[hs][c] = tr_pair(qs, T::kDoRow, 32 * hs, ct * 16, g, hl);
-    }
-  __syncthreads();
 
   // Query rows into LDS.
   {
@@ -202,6 +210,10 @@ sparse_mla_bwd_kernel(BwdArgs a) {
     }
   }
   const float scale_log2 = a.scale * kLog2e;
+  if (a.stats_out != nullptr && g == 0) {
+    a.stats_out[(size_t)row * 2 * kHeads + head] = l2;
+    a.stats_out[(size_t)row * 2 * kHeads + kHeads + head] = delta;
+  }
 
   f32x4 dqa[T::kTiles];
 #pragma unroll
@@ -266,14 +278,17 @@ sparse_mla_bwd_kernel(BwdArgs a) {
         const float p = valid ? __builtin_amdgcn_exp2f(st[kt][r] * scale_log2 - l2) : 0.f;
         const float ds = a.scale * p * (dpt[kt][r] - delta);
         dsf[kt * 4 + r] = (__bf16)ds;
-        *reinterpret_cast<LDS_AS __bf16*>(dst + key * T::kSRow + head * 2) = (__bf16)ds;
-        *reinterpret_cast<LDS_AS __bf16*>(pst + key * T::kSRow + head * 2) = (__bf16)p;
+        if (scatter) {
+          *reinterpret_cast<LDS_AS __bf16*>(dst + key * T::kSRow + head * 2) = (__bf16)ds;
+          *reinterpret_cast<LDS_AS __bf16*>(pst + key * T::kSRow + head * 2) = (__bf16)p;
+        }
       }
 
-    __syncthreads();  // dS^T and P^T of every wave are in LDS
+    if (scatter) __syncthreads();  // dS^T and P^T of every wave are in LDS
 
     // dKV of this wave's columns: element e of both operands is head
     // 32 hs + 16 (e / 4) + 4g + e % 4.
+    if (scatter)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x4 acc[T::kWaveTiles];
@@ -322,6 +337,334 @@ sparse_mla_bwd_kernel(BwdArgs a) {
     unsafeAtomicAdd(a.d_sink + head, -__builtin_amdgcn_exp2f(sk2 - l2) * delta);
 }
 
+// ---------------------------------------------------------------------------
+// Key-outer dkv pass
+// ---------------------------------------------------------------------------
+// When a call's selections are dense enough (the KV table is at most a few
+// times the row width), dkv is summed per block of 64 KV rows instead of
+// scattered per (row, key) pair: a workgroup owns one key block and a chunk
+// of query rows, recomputes P and dS for every row of the chunk that names a
+// key of the block (all 64 heads at once), and keeps the block's dK + dV in
+// its accumulator registers; one atomic add per element of the block and
+// chunk moves it to the fp32 accumulator.  A row that names one key twice is
+// left to the row pass (its per-occurrence scatter), so the mask below can be
+// a plain bitmap.
+
+constexpr int kKoKeys = 64;       // keys per block
+constexpr int kAhead = 4;         // LDS operand reads in flight per S / dP chain
+constexpr int kKoMaxRows = 128;   // query rows per chunk, at most
+constexpr int kKoMaxKv = 16384;   // widest KV table with a bitmap in LDS
+
+// Row bitmap of the keys each row names (valid entries before its length),
+// and whether the row names a key twice.  One workgroup per query row.
+__global__ void __launch_bounds__(256) bwd_mask_kernel(const int32_t* indices, const int32_t* row_len,
+                                                       int32_t topk, int32_t s_kv, int32_t nw,
+                                                       uint32_t* bits, int32_t* dup) {
+  __shared__ uint32_t words[kKoMaxKv / 32];
+  __shared__ int any_dup;
+  const int row = blockIdx.x;
+  for (int w = threadIdx.x; w < nw; w += 256) words[w] = 0u;
+  if (threadIdx.x == 0) any_dup = 0;
+  __syncthreads();
+  const int L = row_len[row];
+  const int32_t* ir = indices + (size_t)row * topk;
+  bool twice = false;
+  for (int p = threadIdx.x; p < L; p += 256) {
+    const int j = ir[p];
+    if (j >= 0 && j < s_kv) {
+      const uint32_t bit = 1u << (j & 31);
+      twice |= (atomicOr(&words[j >> 5], bit) & bit) != 0u;
+    }
+  }
+  if (twice) any_dup = 1;
+  __syncthreads();
+  uint32_t* out = bits + (size_t)row * nw;
+  for (int w = threadIdx.x; w < nw; w += 256) out[w] = words[w];
+  if (threadIdx.x == 0) dup[row] = any_dup;
+}
+
+struct DkvArgs {
+  const __bf16* q;          // [s_q][64][D]
+  const __bf16* kv;         // [s_kv][D]
+  const __bf16* dout;       // [s_q][64][512]
+  const uint32_t* bits;     // [s_q][nw]
+  const int32_t* dup;       // [s_q]
+  const float* stats;       // [s_q][128]: the row pass's normaliser in log2 units, then delta
+  float* dkv_acc;           // [s_kv][D]
+  int32_t s_q, s_kv, nw, n_kb, chunk_rows, n_chunks;
+  float scale, scale_log2;
+};
+
+template <int D>
+struct KoTile {
+  static constexpr int kQRow = 2 * D + 16;             // padded LDS row of a query head
+  static constexpr int kDoRow = 2 * kDV + 16;          // ... of a dout head
+  static constexpr int kSRow = 2 * kHeads + 16;        // ... of dS^T / P^T (one key)
+  static constexpr int kQBytes = kHeads * kQRow;
+  static constexpr int kDoBytes = kHeads * kDoRow;
+  static constexpr int kSBytes = kKoKeys * kSRow;
+  static constexpr int kStatBytes = 2 * kHeads * 4;   // a row's normalisers and deltas
+  static constexpr int kLds = kQBytes + kDoBytes + 2 * kSBytes + kStatBytes + kKoMaxRows * 12 + 16;
+  static constexpr int kSteps = D / 16;                // 32x32x16 steps over d_qk
+  static constexpr int kVSteps = kDV / 16;             // ... over d_v
+  static constexpr int kWaveCols = D / 64;             // 32-column dkv tiles per wave
+  static constexpr int kQCopies = (kHeads / kWaves) * (D > kDV ? 2 : 1);  // per wave and row
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(kQCopies < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// B operand of a 32x32x16 product read down the rows of an LDS tile: lane
+// (half, j) receives rows r0 + 8 half + (0..7) of column c0 + j, by two
+// ds_read_b64_tr_b16 over 4 x 16 sub-tiles.
+__device__ __forceinline__ bf16x8 tr_col8(const LDS_AS uint8_t* tile, int row_bytes, int r0, int c0,
+                                          int lane) {
+  const int grp = lane >> 4, i = lane & 15;
+  const LDS_AS uint8_t* p = tile + (r0 + 8 * (grp >> 1) + (i >> 2)) * row_bytes +
+                            (c0 + 16 * (grp & 1) + 4 * (i & 3)) * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 4 * row_bytes));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// LDS [lds + 16 lane, +16) <- this lane's 16 bytes at src, by LDS DMA.  The
+// compiler does not count it: the kernel waits for it with vmcnt itself.
+__device__ __forceinline__ void lds_dma16(const void* src, LDS_AS uint8_t* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// One workgroup per (row chunk, key block), heaviest chunks first.  Wave w
+// computes S^T and dP^T for keys 32 (w / 2) .. +31 and heads 32 (w % 2) ..
+// +31 (its K fragments stay in registers for the whole chunk), and owns the
+// dkv tiles of the same 32 keys and half of the 32-column tiles.
+// Each row's query heads, dout heads and statistics reach LDS by DMA in two
+// parts, so that each overlaps products of the row before:
+//   top of row t: dout_t and stats_t in LDS, q_t in flight;
+//   dP^T (dout_t); wait for q_t; S^T (q_t); P, dS to LDS;
+//   dV += P^T dout_t; barrier; dout and stats of the next row in flight;
+//   dK += dS^T q_t; barrier; the next row's q in flight; wait for its dout.
+template <int D>
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sparse_mla_bwd_dkv_kernel(DkvArgs a) {
+  using T = KoTile<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[T::kLds];
+  LDS_AS uint8_t* qs = (LDS_AS uint8_t*)lds_raw;     // query heads [64][kQRow]
+  LDS_AS uint8_t* dos = qs + T::kQBytes;              // dout heads [64][kDoRow]
+  LDS_AS uint8_t* dss = dos + T::kDoBytes;            // dS^T [64 keys][kSRow]
+  LDS_AS uint8_t* pss = dss + T::kSBytes;             // P^T  [64 keys][kSRow]
+  LDS_AS uint8_t* sts = pss + T::kSBytes;             // l2[64], delta[64] of the row
+  LDS_AS uint64_t* rsel = (LDS_AS uint64_t*)(sts + T::kStatBytes);  // their key masks
+  LDS_AS int32_t* rlist = (LDS_AS int32_t*)(rsel + kKoMaxRows);      // rows of the chunk
+  LDS_AS int32_t* wcnt = rlist + kKoMaxRows;          // per-wave row counts
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j32 = lane & 31, half = lane >> 5;
+  const int kb = (int)(blockIdx.x % (unsigned)a.n_kb);
+  const int chunk = a.n_chunks - 1 - (int)(blockIdx.x / (unsigned)a.n_kb);
+  const int r0 = chunk * a.chunk_rows;
+  const int key0 = kb * kKoKeys;
+  const int w0 = 2 * kb;
+
+  // The chunk's rows that name a key of the block, in order, with their
+  // masks of the block's keys.
+  {
+    const int t = r0 + tid;
+    uint64_t sel = 0;
+    if (tid < a.chunk_rows && t < a.s_q && a.dup[t] == 0) {
+      const uint32_t* b = a.bits + (size_t)t * a.nw;
+      sel = (uint64_t)b[w0] | ((uint64_t)(w0 + 1 < a.nw ? b[w0 + 1] : 0u) << 32);
+    }
+    const bool present = sel != 0;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(present);
+    if (lane == 0) wcnt[wave] = __builtin_popcountll(m);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wcnt[w];
+    if (present) {
+      const int at = base + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+      rlist[at] = t;
+      rsel[at] = sel;
+    }
+    __syncthreads();
+  }
+  const int n_rows = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  if (n_rows == 0) return;
+
+  // DMA of a row's parts: this wave's 16 heads of dout (and wave 0: the
+  // statistics), then of q.
+  auto issue_dout = [&](int t) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.dout + (size_t)t * kHeads * kDV);
+#pragma unroll
+    for (int h = wave; h < kHeads; h += kWaves)
+      lds_dma16(src + h * 2 * kDV + lane * 16, dos + h * T::kDoRow);
+    if (wave == 0 && lane < T::kStatBytes / 16)
+      lds_dma16(reinterpret_cast<const uint8_t*>(a.stats + (size_t)t * 2 * kHeads) + lane * 16, sts);
+  };
+  auto issue_q = [&](int t) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q + (size_t)t * kHeads * D);
+#pragma unroll
+    for (int h = wave; h < kHeads; h += kWaves) {
+      lds_dma16(src + h * 2 * D + lane * 16, qs + h * T::kQRow);
+      if (D > kDV && lane < (2 * D - 2 * kDV) / 16)
+        lds_dma16(src + h * 2 * D + 2 * kDV + lane * 16, qs + h * T::kQRow + 2 * kDV);
+    }
+  };
+
+  const int kh = wave >> 1, hh = wave & 1;
+  // K fragments (A operand of S^T and, over the first d_v columns, of dP^T):
+  // key 32 kh + j32, columns 16 s + 8 half .. +7.  A key past the table reads
+  // row 0 instead: no row names it, so its P and dS are set to 0.
+  bf16x8 kf[T::kSteps];
+  {
+    const int key = key0 + 32 * kh + j32;
+    const __bf16* kp = a.kv + (size_t)(key < a.s_kv ? key : 0) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < T::kSteps; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+  }
+  // The wave's dkv column tiles: 8 value tiles 8 hh .. 8 hh + 7 (the same
+  // count in both waves), then at d576 the rope tile 16 + hh.
+  auto tile_col = [&](int c) { return c < kDV / 64 ? 8 * hh + c : kDV / 32 + hh; };
+  f32x16 acc[T::kWaveCols];
+#pragma unroll
+  for (int c = 0; c < T::kWaveCols; ++c) acc[c] = f32x16{};
+
+  const int head = 32 * hh + j32;
+  int t = __builtin_amdgcn_readfirstlane(rlist[0]);
+  issue_dout(t);
+  issue_q(t);
+  // Everything, the K fragments included: the loop then has no load the
+  // compiler would wait for.
+  wait_vm<0>();
+  __syncthreads();
+  for (int v = 0; v < n_rows; ++v) {
+    const uint64_t sel = rsel[v];
+    const float l2 = *reinterpret_cast<const LDS_AS float*>(sts + 4 * head);
+    const float dl = *reinterpret_cast<const LDS_AS float*>(sts + 4 * (kHeads + head));
+
+    // dP^T, then S^T: element i is key 32 kh + 8 (i / 4) + 4 half + i % 4 of
+    // the block, head `head`.
+    f32x16 dpt = f32x16{}, st = f32x16{};
+    const LDS_AS uint8_t* drow = dos + head * T::kDoRow + 16 * half;
+    // The B operands are read kAhead steps ahead of their products.
+    {
+      bf16x8 bq[kAhead];
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) bq[s] = *reinterpret_cast<const LDS_AS bf16x8*>(drow + 32 * s);
+#pragma unroll
+      for (int s = 0; s < T::kVSteps; ++s) {
+        const bf16x8 cur = bq[s % kAhead];
+        if (s + kAhead < T::kVSteps)
+          bq[s % kAhead] = *reinterpret_cast<const LDS_AS bf16x8*>(drow + 32 * (s + kAhead));
+        dpt = mfma32(kf[s], cur, dpt);
+        __builtin_amdgcn_sched_barrier(0);  // keeps the read-ahead distance
+      }
+    }
+    wait_vm<0>();  // this wave's q copies
+    __syncthreads();
+    const LDS_AS uint8_t* qrow = qs + head * T::kQRow + 16 * half;
+    {
+      bf16x8 bq[kAhead];
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) bq[s] = *reinterpret_cast<const LDS_AS bf16x8*>(qrow + 32 * s);
+#pragma unroll
+      for (int s = 0; s < T::kSteps; ++s) {
+        const bf16x8 cur = bq[s % kAhead];
+        if (s + kAhead < T::kSteps)
+          bq[s % kAhead] = *reinterpret_cast<const LDS_AS bf16x8*>(qrow + 32 * (s + kAhead));
+        st = mfma32(kf[s], cur, st);
+        __builtin_amdgcn_sched_barrier(0);  // keeps the read-ahead distance
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 32 * kh + 8 * (i >> 2) + 4 * half + (i & 3);
+      const bool on = (sel >> key) & 1ull;
+      const float p = on ? __builtin_amdgcn_exp2f(st[i] * a.scale_log2 - l2) : 0.f;
+      const float ds = on ? a.scale * p * (dpt[i] - dl) : 0.f;
+      *reinterpret_cast<LDS_AS __bf16*>(dss + key * T::kSRow + head * 2) = (__bf16)ds;
+      *reinterpret_cast<LDS_AS __bf16*>(pss + key * T::kSRow + head * 2) = (__bf16)p;
+    }
+    __syncthreads();  // dS^T and P^T of the block are in LDS
+
+    // dkv[32 keys x 32 columns] += P^T dO on the value columns, then dS^T Q,
+    // contracted over the 64 heads in four steps of 16.  Product n of a
+    // phase is head step n / C and tile n % C; its B operand is read kAhead
+    // products ahead.
+    bf16x8 af[4], pf[4];
+#pragma unroll
+    for (int hs = 0; hs < 4; ++hs) {
+      af[hs] = *reinterpret_cast<const LDS_AS bf16x8*>(dss + (32 * kh + j32) * T::kSRow + 32 * hs +
+                                                       16 * half);
+      pf[hs] = *reinterpret_cast<const LDS_AS bf16x8*>(pss + (32 * kh + j32) * T::kSRow + 32 * hs +
+                                                       16 * half);
+    }
+    {
+      constexpr int C = kDV / 64, N = 4 * C;
+      auto bop = [&](int n) { return tr_col8(dos, T::kDoRow, 16 * (n / C), 32 * tile_col(n % C), lane); };
+      bf16x8 bq[kAhead];
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) bq[n] = bop(n);
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const bf16x8 cur = bq[n % kAhead];
+        if (n + kAhead < N) bq[n % kAhead] = bop(n + kAhead);
+        acc[n % C] = mfma32(pf[n / C], cur, acc[n % C]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const bool more = v + 1 < n_rows;
+    const int tn = more ? __builtin_amdgcn_readfirstlane(rlist[v + 1]) : t;
+    __syncthreads();  // dout and stats are free
+    if (more) issue_dout(tn);
+    {
+      constexpr int C = T::kWaveCols, N = 4 * C;
+      auto bop = [&](int n) { return tr_col8(qs, T::kQRow, 16 * (n / C), 32 * tile_col(n % C), lane); };
+      bf16x8 bq[kAhead];
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) bq[n] = bop(n);
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const bf16x8 cur = bq[n % kAhead];
+        if (n + kAhead < N) bq[n % kAhead] = bop(n + kAhead);
+        acc[n % C] = mfma32(af[n / C], cur, acc[n % C]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();  // q, dS^T and P^T are free
+    if (more) {
+      issue_q(tn);
+      wait_vm<T::kQCopies>();  // the next row's dout and stats
+      __syncthreads();
+    }
+    t = tn;
+  }
+
+  // acc[c][i] is dkv[key0 + 32 kh + 8 (i / 4) + 4 half + i % 4][32 tile_col(c) + j32].
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = key0 + 32 * kh + 8 * (i >> 2) + 4 * half + (i & 3);
+    if (key < a.s_kv) {
+      float* drow = a.dkv_acc + (size_t)key * D + j32;
+#pragma unroll
+      for (int c = 0; c < T::kWaveCols; ++c) unsafeAtomicAdd(drow + 32 * tile_col(c), acc[c][i]);
+    }
+  }
+}
+
 // Zero fill (also the fp32 accumulators before a launch).
 __global__ void __launch_bounds__(256) bwd_zero_kernel(float* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
@@ -361,11 +704,55 @@ int grid_for(size_t n) {
   return (int)(g < 4096 ? (g > 0 ? g : 1) : 4096);
 }
 
+// Shapes whose key-outer buffers the workspace holds: the row bitmaps fit
+// LDS and stay under 32 MB.
+bool key_outer_eligible(int32_t s_q, int32_t s_kv) {
+  return s_kv > 0 && s_kv <= kKoMaxKv && (size_t)s_q * (size_t)s_kv <= ((size_t)1 << 28);
+}
+
+// The key-outer pass runs where the KV table is at most 8 row widths: it
+// visits up to every (row, 64-key block) pair, about 4x the cost of a pair's
+// scatter per key, so it wins below ~13 row widths for random selections and
+// further out for local ones.
+constexpr int kKoWidths = 8;
+constexpr int kKoChunk = 128;  // query rows per key-outer workgroup
+
+struct BwdWorkspace {
+  float* acc;        // [s_kv][d_qk] fp32 dkv accumulator
+  int32_t* row_len;  // [s_q]
+  float* stats;      // [s_q][128] (key-outer shapes)
+  int32_t* dup;      // [s_q]
+  uint32_t* bits;    // [s_q][nw]
+  int32_t nw;
+  size_t bytes;
+};
+
+BwdWorkspace workspace_layout(void* base, int32_t s_q, int32_t s_kv, int32_t d_qk) {
+  BwdWorkspace w{};
+  uint8_t* p = static_cast<uint8_t*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    uint8_t* at = p ? p + off : nullptr;
+    off += align_up(n);
+    return at;
+  };
+  w.acc = reinterpret_cast<float*>(take((size_t)s_kv * (size_t)d_qk * sizeof(float)));
+  w.row_len = reinterpret_cast<int32_t*>(take((size_t)s_q * sizeof(int32_t)));
+  if (key_outer_eligible(s_q, s_kv)) {
+    w.nw = (s_kv + 31) / 32;
+    w.stats = reinterpret_cast<float*>(take((size_t)s_q * 2 * kHeads * sizeof(float)));
+    w.dup = reinterpret_cast<int32_t*>(take((size_t)s_q * sizeof(int32_t)));
+    w.bits = reinterpret_cast<uint32_t*>(take((size_t)s_q * w.nw * sizeof(uint32_t)));
+  }
+  w.bytes = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" size_t sparse_mla_bwd_workspace_bytes(int32_t s_q, int32_t s_kv, int32_t d_qk) {
   if (s_q < 0 || s_kv < 0 || d_qk <= 0) return 0;
-  return align_up((size_t)s_kv * (size_t)d_qk * sizeof(float)) + align_up((size_t)s_q * sizeof(int32_t));
+  return workspace_layout(nullptr, s_q, s_kv, d_qk).bytes;
 }
 
 extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void* out,
@@ -377,6 +764,7 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
                                       void* workspace, size_t workspace_bytes, void* dq, void* dkv,
                                       float* d_sink, smla_stream_t stream) {
   smla_clear_error();
+  smla_set_last_kernel("");
   if (s_q < 0 || s_kv < 0 || topk <= 0)
     return bwd_fail(SMLA_ERR_BAD_SHAPE, "bad sizes (s_q=%d s_kv=%d topk=%d)", s_q, s_kv, topk);
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
@@ -403,9 +791,11 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
                     "sparse_mla_bwd: q, out, dout, indices, lse, dq (s_q > 0) and kv, dkv "
                     "(s_kv > 0) are required");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* acc = static_cast<float*>(workspace);
-  int32_t* row_len = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
-                                                align_up((size_t)s_kv * d_qk * sizeof(float)));
+  const BwdWorkspace ws = workspace_layout(workspace, s_q, s_kv, d_qk);
+  float* acc = ws.acc;
+  int32_t* row_len = ws.row_len;
+  const bool key_outer = s_q > 0 && key_outer_eligible(s_q, s_kv) &&
+                         (size_t)s_kv <= (size_t)kKoWidths * (size_t)topk;
   const size_t n_acc = (size_t)s_kv * d_qk;
   if (n_acc > 0) {
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(grid_for(n_acc)), dim3(256), 0, st, acc, n_acc);
@@ -419,6 +809,11 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
     if (smla_status e = sparse_mla_row_lengths(indices, topk_length, nullptr, s_q, 1, topk, s_kv, 0,
                                                row_len, stream))
       return e;
+    if (key_outer) {
+      hipLaunchKernelGGL(bwd_mask_kernel, dim3(s_q), dim3(256), 0, st, indices, row_len, topk, s_kv,
+                         ws.nw, ws.bits, ws.dup);
+      if (smla_status e = launched()) return e;
+    }
     BwdArgs args{};
     args.q = static_cast<const __bf16*>(q);
     args.kv = static_cast<const __bf16*>(kv);
@@ -436,6 +831,11 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
     args.topk = topk;
     args.scale = sm_scale;
     args.lse_to_log2 = lse_base2 ? 1.f : kLog2e;
+    if (key_outer) {
+      args.stats_out = ws.stats;
+      args.dup = ws.dup;
+      args.key_outer = 1;
+    }
     const bool sink = attn_sink != nullptr;
     if (d_qk == 576) {
       if (sink)
@@ -449,11 +849,37 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
         hipLaunchKernelGGL((sparse_mla_bwd_kernel<512, false>), dim3(s_q), dim3(256), 0, st, args);
     }
     if (smla_status e = launched()) return e;
+    if (key_outer) {
+      DkvArgs k{};
+      k.q = args.q;
+      k.kv = args.kv;
+      k.dout = args.dout;
+      k.bits = ws.bits;
+      k.dup = ws.dup;
+      k.stats = ws.stats;
+      k.dkv_acc = acc;
+      k.s_q = s_q;
+      k.s_kv = s_kv;
+      k.nw = ws.nw;
+      k.n_kb = (s_kv + kKoKeys - 1) / kKoKeys;
+      k.chunk_rows = kKoChunk;
+      k.n_chunks = (s_q + kKoChunk - 1) / kKoChunk;
+      k.scale = sm_scale;
+      k.scale_log2 = sm_scale * kLog2e;
+      const dim3 grid((unsigned)(k.n_kb * k.n_chunks));
+      if (d_qk == 576)
+        hipLaunchKernelGGL((sparse_mla_bwd_dkv_kernel<576>), grid, dim3(256), 0, st, k);
+      else
+        hipLaunchKernelGGL((sparse_mla_bwd_dkv_kernel<512>), grid, dim3(256), 0, st, k);
+      if (smla_status e = launched()) return e;
+    }
   }
   if (n_acc > 0) {
     hipLaunchKernelGGL(bwd_convert_kernel, dim3(grid_for(n_acc / 4)), dim3(256), 0, st, acc,
                        static_cast<__bf16*>(dkv), n_acc / 4);
     if (smla_status e = launched()) return e;
   }
+  // After the row-length entry point, which resets the name.
+  smla_set_last_kernel(s_q == 0 ? "" : key_outer ? "bwd_key_outer" : "bwd_scatter");
   return SMLA_OK;
 }

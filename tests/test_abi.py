@@ -194,8 +194,12 @@ def _bwd(lib, **kw):
 
 def test_bwd_workspace_bytes(lib):
     f = lib.sparse_mla_bwd_workspace_bytes
-    assert f(8, 64, 576) == 64 * 576 * 4 + 256
-    assert f(300, 1, 512) == 2048 + 1280
+    # fp32 accumulator and row lengths, then (s_kv <= 16384, s_q * s_kv <=
+    # 2^28) the key-outer buffers: statistics [s_q][128] fp32, flags [s_q],
+    # bitmaps [s_q][ceil(s_kv / 32)] words; each part rounded up to 256 bytes.
+    assert f(8, 64, 576) == 64 * 576 * 4 + 256 + 8 * 128 * 4 + 256 + 256
+    assert f(300, 1, 512) == 2048 + 1280 + 300 * 128 * 4 + 1280 + 1280
+    assert f(8, 20000, 576) == 20000 * 576 * 4 + 256
     assert f(0, 0, 576) == 0 and f(-1, 4, 576) == 0
 
 

@@ -11,6 +11,7 @@ Tolerances (fp32 accumulation, bf16 P, dS and outputs; the oracle is fp64):
 relative L2 error <= 1e-2 and max-abs error <= 2e-2 of the largest reference
 magnitude, for dq, dkv and d_sink.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -93,6 +94,10 @@ def test_bwd_matches_oracle(d_qk, with_length, with_sink):
     dout = W.bwd_dout(case, seed=5)
     out, lse = _oracle_stats(case)
     dq, dkv, ds = _run(case, out, lse, dout)
+    # s_kv = 200 is within 8 row widths of topk = 96: the key-outer dkv pass,
+    # with row 1 of the unlengthed case (a key named three times) scattered
+    # by the row pass.
+    assert smla.last_kernel() == "bwd_key_outer"
     rq, rkv, rs = oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse,
                                         case.sm_scale, case.d_v, attn_sink=case.attn_sink,
                                         topk_length=case.topk_length,
@@ -146,6 +151,7 @@ def test_bwd_full_size_sampled():
     dout = W.bwd_dout(case, seed=8)
     out, lse = W.bwd_synthetic_stats(case, seed=9)
     dq, dkv, _ = _run(case, out, lse, dout)
+    assert smla.last_kernel() == "bwd_key_outer"
     rows = np.array([0, 1, 31, 32, 1023, 2047, 2048, 2049, 3000, 4094, 4095])
     kv_rows = np.array([0, 1, 17, 640, 2047, 2048, 3071, 4000, 4095])
     rq, rkv, _ = oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse,
@@ -207,3 +213,34 @@ def test_bwd_random_shapes():
         _close(f"dkv {case.name}", dkv[:, 0, :], rkv)
         if sink:
             _close(f"d_sink {case.name}", ds, rs)
+
+
+@pytest.mark.parametrize("d_qk", [576, 512])
+def test_bwd_key_outer_and_scatter_paths_agree(d_qk):
+    """One selection through both dkv paths: topk = 40 over s_kv = 400 KV rows
+    scatters per (row, key) pair (the table is more than 8 row widths), and
+    the same indices padded with -1 to topk = 64 go through the key-outer
+    pass.  Both match the oracle; ragged key blocks (400 = 6 x 64 + 16) and
+    rows past one 128-row chunk (s_q = 150) included."""
+    case = W.make_prefill(f"bwd_paths_d{d_qk}", s_q=150, s_kv=400, h_q=64, d_qk=d_qk, d_v=512,
+                          topk=40, layout="scattered", invalid_frac=0.1, empty_frac=0.05,
+                          seed=77, with_sink=True)
+    dout = W.bwd_dout(case, seed=78)
+    out, lse = _oracle_stats(case)
+    dq_s, dkv_s, ds_s = _run(case, out, lse, dout)
+    assert smla.last_kernel() == "bwd_scatter"
+    padded = torch.full((150, 1, 64), -1, dtype=torch.int32)
+    padded[:, :, :40] = case.indices
+    wide = dataclasses.replace(case, name=case.name + "_padded", indices=padded)
+    dq_k, dkv_k, ds_k = _run(wide, out, lse, dout)
+    assert smla.last_kernel() == "bwd_key_outer"
+    rq, rkv, rs = oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse,
+                                        case.sm_scale, case.d_v, attn_sink=case.attn_sink,
+                                        want_d_sink=True)
+    for tag, dq, dkv, ds in (("scatter", dq_s, dkv_s, ds_s), ("key-outer", dq_k, dkv_k, ds_k)):
+        _close(f"dq ({tag})", dq, rq)
+        _close(f"dkv ({tag})", dkv[:, 0, :], rkv)
+        _close(f"d_sink ({tag})", ds, rs)
+    # dq comes from the same per-row sums on both paths (d_sink's cross-row
+    # atomic sum has a run-dependent order).
+    assert torch.equal(dq_s, dq_k)
