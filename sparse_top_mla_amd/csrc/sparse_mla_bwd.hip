@@ -96,7 +96,7 @@ struct BwdTile {
   static constexpr int kKBytes = kBK * kRow;
   static constexpr int kSRow = 2 * kHeads + 16;    // padded LDS row of dS^T / P^T (one key)
   static constexpr int kSBytes = kBK * kSRow;
-  static constexpr int kLds = kQBytes + kKBytes + 2 * kSBytes;
+  static constexpr int kLds = kQBytes + 2 * kKBytes + 2 * kSBytes;
   static constexpr int kDSteps = D / 32;           // MFMA K steps over d_qk
   static constexpr int kVSteps = kDV / 32;         // ... over d_v
   static constexpr int kTiles = D / 16;            // 16-column tiles of a KV row
@@ -108,6 +108,16 @@ struct BwdTile {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS [lds + 16 lane, +16) <- this lane's 16 bytes at src, by LDS DMA.  The
+// compiler does not count it: the kernel waits for it with vmcnt itself.
+__device__ __forceinline__ void lds_dma16(const void* src, LDS_AS uint8_t* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
+
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -137,8 +147,8 @@ sparse_mla_bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[T::kLds];
   LDS_AS uint8_t* qs = (LDS_AS uint8_t*)lds_raw;     // query rows [64][kRow]
-  LDS_AS uint8_t* ks = qs + T::kQBytes;                // KV block [32][kRow]
-  LDS_AS uint8_t* dst = ks + T::kKBytes;               // dS^T [32 keys][kSRow]
+  LDS_AS uint8_t* ks0 = qs + T::kQBytes;               // KV blocks [2][32][kRow]
+  LDS_AS uint8_t* dst = ks0 + 2 * T::kKBytes;          // dS^T [32 keys][kSRow]
   LDS_AS uint8_t* pst = dst + T::kSBytes;              // P^T  [32 keys][kSRow]
 
   const int tid = threadIdx.x;
@@ -222,31 +232,42 @@ sparse_mla_bwd_kernel(BwdArgs a) {
   const int L = a.row_len[row];
   const int32_t* idx_row = a.indices + (size_t)row * a.topk;
   const int nblk = (L + kBK - 1) / kBK;
-  for (int kb = 0; kb < nblk; ++kb) {
+  // Block kb's KV rows go to buffer kb % 2 by LDS DMA while block kb - 1 is
+  // computed (masked rows as zeros); lane j < 32 holds position 32 kb + j.
+  auto load_idx = [&](int kb) {
     const int pos = kb * kBK + lane;
-    const int idx = (lane < kBK && pos < L) ? idx_row[pos] : -1;
-    const bool ok = idx >= 0 && idx < a.s_kv;
-    const uint64_t mask = __builtin_amdgcn_ballot_w64(ok);
-    if (mask == 0) continue;  // the same in every wave
-
-    __syncthreads();  // the previous block's readers of ks / dst / pst are done
+    return (kb < nblk && lane < kBK && pos < L) ? idx_row[pos] : -1;
+  };
+  auto gather = [&](int idx, uint64_t mask, LDS_AS uint8_t* kbuf) {
     for (int j = wave; j < kBK; j += kWaves) {
-      LDS_AS uint8_t* d = ks + j * T::kRow;
+      LDS_AS uint8_t* d = kbuf + j * T::kRow;
       if ((mask >> j) & 1ull) {
         const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv) +
                              (size_t)(uint32_t)__builtin_amdgcn_readlane(idx, j) * (2 * D);
-        __builtin_amdgcn_global_load_lds((const void*)(src + lane * 16), (LDS_AS void*)d, 16, 0, 0);
-        if (D > kDV && lane < (2 * D - 2 * kDV) / 16)
-          __builtin_amdgcn_global_load_lds((const void*)(src + 2 * kDV + lane * 16),
-                                           (LDS_AS void*)(d + 2 * kDV), 16, 0, 0);
+        lds_dma16(src + lane * 16, d);
+        if (D > kDV && lane < (2 * D - 2 * kDV) / 16) lds_dma16(src + 2 * kDV + lane * 16, d + 2 * kDV);
       } else {
         *reinterpret_cast<LDS_AS u32x4*>(d + lane * 16) = u32x4{0u, 0u, 0u, 0u};
         if (D > kDV && lane < (2 * D - 2 * kDV) / 16)
           *reinterpret_cast<LDS_AS u32x4*>(d + 2 * kDV + lane * 16) = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    wait_vm_all();
-    __syncthreads();
+  };
+  auto valid_mask = [&](int idx) { return __builtin_amdgcn_ballot_w64(idx >= 0 && idx < a.s_kv); };
+  int idx_nxt = load_idx(0);
+  uint64_t mask_nxt = valid_mask(idx_nxt);
+  if (nblk > 0) gather(idx_nxt, mask_nxt, ks0);
+  int idx_far = load_idx(1);
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int idx = idx_nxt;
+    const uint64_t mask = mask_nxt;
+    LDS_AS uint8_t* ks = ks0 + (kb & 1) * T::kKBytes;
+    wait_vm_all();    // block kb's copies (and the previous block's atomics)
+    __syncthreads();  // ... of every wave; block kb - 1's readers are done
+    idx_nxt = idx_far;
+    mask_nxt = valid_mask(idx_nxt);
+    if (kb + 1 < nblk) gather(idx_nxt, mask_nxt, ks0 + ((kb + 1) & 1) * T::kKBytes);
+    idx_far = load_idx(kb + 2);
 
     // S^T and dP^T: lane (g, hl) holds keys 16 kt + 4g + r of head `head`.
     f32x4 st[2], dpt[2];
@@ -428,15 +449,6 @@ __device__ __forceinline__ bf16x8 tr_col8(const LDS_AS uint8_t* tile, int row_by
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 4 * row_bytes));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// LDS [lds + 16 lane, +16) <- this lane's 16 bytes at src, by LDS DMA.  The
-// compiler does not count it: the kernel waits for it with vmcnt itself.
-__device__ __forceinline__ void lds_dma16(const void* src, LDS_AS uint8_t* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
-               : "memory");
 }
 
 template <int N>
