@@ -60,6 +60,8 @@ constexpr int kHeads = 64;       // h_q
 constexpr int kWaves = 4;        // 16 heads each
 constexpr int kDV = 512;         // value width
 constexpr int kBK = 32;          // keys per block
+constexpr int kRowAhead = 2;     // S / dP steps whose LDS operands are read ahead
+constexpr int kDqAhead = 4;      // dQ products whose K^T operands are read ahead
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ds_read_b64_tr_b16: in each 16-lane group, lane i gives the address of four
@@ -276,15 +278,33 @@ sparse_mla_bwd_kernel(BwdArgs a) {
       st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       dpt[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // The step's three LDS operands (query slice, two key rows) are read
+    // kRowAhead steps ahead of its products.
+    {
+      auto rd = [&](int s, int k) {  // k = 0: query; 1, 2: key rows kt = k - 1
+        const LDS_AS uint8_t* p = k == 0 ? qs + head * T::kRow : ks + ((k - 1) * 16 + hl) * T::kRow;
+        return *reinterpret_cast<const LDS_AS bf16x8*>(p + s * 64 + g * 16);
+      };
+      bf16x8 buf[kRowAhead][3];
 #pragma unroll
-    for (int s = 0; s < T::kDSteps; ++s) {
-      const bf16x8 qf = *reinterpret_cast<const LDS_AS bf16x8*>(qs + head * T::kRow + s * 64 + g * 16);
+      for (int s = 0; s < kRowAhead; ++s)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kf =
-            *reinterpret_cast<const LDS_AS bf16x8*>(ks + (kt * 16 + hl) * T::kRow + s * 64 + g * 16);
-        st[kt] = mfma(kf, qf, st[kt]);
-        if (s < T::kVSteps) dpt[kt] = mfma(kf, dor[s], dpt[kt]);
+        for (int k = 0; k < 3; ++k) buf[s][k] = rd(s, k);
+#pragma unroll
+      for (int s = 0; s < T::kDSteps; ++s) {
+        const bf16x8 qf = buf[s % kRowAhead][0];
+        const bf16x8 kf0 = buf[s % kRowAhead][1];
+        const bf16x8 kf1 = buf[s % kRowAhead][2];
+        if (s + kRowAhead < T::kDSteps)
+#pragma unroll
+          for (int k = 0; k < 3; ++k) buf[s % kRowAhead][k] = rd(s + kRowAhead, k);
+        st[0] = mfma(kf0, qf, st[0]);
+        st[1] = mfma(kf1, qf, st[1]);
+        if (s < T::kVSteps) {
+          dpt[0] = mfma(kf0, dor[s], dpt[0]);
+          dpt[1] = mfma(kf1, dor[s], dpt[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keeps the read-ahead distance
       }
     }
 
@@ -341,9 +361,19 @@ sparse_mla_bwd_kernel(BwdArgs a) {
     // dQ^T += K^T dS^T, after the atomic adds so that they drain behind it
     // (the next block's loads wait for them): element e of both operands is
     // key 16 (e / 4) + 4g + e % 4.
+    {
+      bf16x8 kt_op[kDqAhead];
 #pragma unroll
-    for (int ct = 0; ct < T::kTiles; ++ct)
-      dqa[ct] = mfma(tr_pair(ks, T::kRow, 0, ct * 16, g, hl), dsf, dqa[ct]);
+      for (int ct = 0; ct < kDqAhead; ++ct) kt_op[ct] = tr_pair(ks, T::kRow, 0, ct * 16, g, hl);
+#pragma unroll
+      for (int ct = 0; ct < T::kTiles; ++ct) {
+        const bf16x8 cur = kt_op[ct % kDqAhead];
+        if (ct + kDqAhead < T::kTiles)
+          kt_op[ct % kDqAhead] = tr_pair(ks, T::kRow, 0, (ct + kDqAhead) * 16, g, hl);
+        dqa[ct] = mfma(cur, dsf, dqa[ct]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 
   // dq[row][head][16 ct + 4g + r] = dqa[ct][r].
