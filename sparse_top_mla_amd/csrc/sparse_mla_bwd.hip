@@ -548,18 +548,23 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
 
   // DMA of a row's parts: this wave's 16 heads of dout (and wave 0: the
   // statistics), then of q.
-  auto issue_dout = [&](int t) {
+  // (copy i of 16 per wave: head wave + 4 i; the statistics with copy 15).
+  auto issue_dout_one = [&](int t, int i) {
+    const int h = wave + kWaves * i;
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.dout + (size_t)t * kHeads * kDV);
-#pragma unroll
-    for (int h = wave; h < kHeads; h += kWaves)
-      lds_dma16(src + h * 2 * kDV + lane * 16, dos + h * T::kDoRow);
-    if (wave == 0 && lane < T::kStatBytes / 16)
+    lds_dma16(src + h * 2 * kDV + lane * 16, dos + h * T::kDoRow);
+    if (i == kHeads / kWaves - 1 && wave == 0 && lane < T::kStatBytes / 16)
       lds_dma16(reinterpret_cast<const uint8_t*>(a.stats + (size_t)t * 2 * kHeads) + lane * 16, sts);
+  };
+  auto issue_dout = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < kHeads / kWaves; ++i) issue_dout_one(t, i);
   };
   auto issue_q = [&](int t) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q + (size_t)t * kHeads * D);
 #pragma unroll
-    for (int h = wave; h < kHeads; h += kWaves) {
+    for (int i = 0; i < kHeads / kWaves; ++i) {
+      const int h = wave + kWaves * i;
       lds_dma16(src + h * 2 * D + lane * 16, qs + h * T::kQRow);
       if (D > kDV && lane < (2 * D - 2 * kDV) / 16)
         lds_dma16(src + h * 2 * D + 2 * kDV + lane * 16, qs + h * T::kQRow + 2 * kDV);
@@ -671,9 +676,10 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
     const bool more = v + 1 < n_rows;
     const int tn = more ? __builtin_amdgcn_readfirstlane(rlist[v + 1]) : t;
     __syncthreads();  // dout and stats are free
-    if (more) issue_dout(tn);
     {
+      // The next row's dout copies go out one per product, under the MFMAs.
       constexpr int C = T::kWaveCols, N = 4 * C;
+      static_assert(N >= kHeads / kWaves, "one copy per product");
       auto bop = [&](int n) { return tr_col8(qs, T::kQRow, 16 * (n / C), 32 * tile_col(n % C), lane); };
       bf16x8 bq[kAhead];
 #pragma unroll
@@ -683,6 +689,7 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
         const bf16x8 cur = bq[n % kAhead];
         if (n + kAhead < N) bq[n % kAhead] = bop(n + kAhead);
         acc[n % C] = mfma32(af[n / C], cur, acc[n % C]);
+        if (n < kHeads / kWaves && more) issue_dout_one(tn, n);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
