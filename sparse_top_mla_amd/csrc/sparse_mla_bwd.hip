@@ -35,6 +35,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -487,7 +488,7 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// One workgroup per (row chunk, key block), heaviest chunks first.  Wave w
+// One workgroup per (row chunk, key block).  Wave w
 // computes S^T and dP^T for keys 32 (w / 2) .. +31 and heads 32 (w % 2) ..
 // +31 (its K fragments stay in registers for the whole chunk), and owns the
 // dkv tiles of the same 32 keys and half of the 32-column tiles.
@@ -515,8 +516,15 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j32 = lane & 31, half = lane >> 5;
-  const int kb = (int)(blockIdx.x % (unsigned)a.n_kb);
-  const int chunk = a.n_chunks - 1 - (int)(blockIdx.x / (unsigned)a.n_kb);
+  // Workgroup i runs on XCD i % 8 (round-robin dispatch).  Chunks, heaviest
+  // (last) first, are dealt to the XCDs in snake order, and each XCD walks
+  // the key blocks of its chunks in turn: the workgroups that read one row's
+  // q and dout at about the same time share an L2.
+  const int xcd = (int)(blockIdx.x % 8u), k = (int)(blockIdx.x / 8u);
+  const int round = k / a.n_kb, kb = k % a.n_kb;
+  const int j = 8 * round + ((round & 1) ? 7 - xcd : xcd);
+  if (j >= a.n_chunks) return;
+  const int chunk = a.n_chunks - 1 - j;
   const int r0 = chunk * a.chunk_rows;
   const int key0 = kb * kKoKeys;
   const int w0 = 2 * kb;
@@ -911,11 +919,12 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
       k.s_kv = s_kv;
       k.nw = ws.nw;
       k.n_kb = (s_kv + kKoKeys - 1) / kKoKeys;
-      k.chunk_rows = kKoChunk;
-      k.n_chunks = (s_q + kKoChunk - 1) / kKoChunk;
+      // At least 8 chunks, one per XCD, where the rows allow.
+      k.chunk_rows = std::min(kKoChunk, std::max(1, (s_q + 7) / 8));
+      k.n_chunks = (s_q + k.chunk_rows - 1) / k.chunk_rows;
       k.scale = sm_scale;
       k.scale_log2 = sm_scale * kLog2e;
-      const dim3 grid((unsigned)(k.n_kb * k.n_chunks));
+      const dim3 grid((unsigned)(8 * k.n_kb * ((k.n_chunks + 7) / 8)));
       if (d_qk == 576)
         hipLaunchKernelGGL((sparse_mla_bwd_dkv_kernel<576>), grid, dim3(256), 0, st, k);
       else
