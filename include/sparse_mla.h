@@ -229,7 +229,7 @@ smla_status sparse_mla_row_lengths(const int32_t *indices, const int32_t *topk_l
  *                 -sum_i exp(sink[h] - lse'_ih) (dout_ih . out_ih)
  * Supported: h_q = 64, h_kv = 1, d_qk 512 or 576, d_v = 512.  Two ways to
  * sum dkv, both in a run-dependent order (fp32 atomics):
- *   where the workspace holds the bitmaps and s_kv <= 8 topk, a key-outer
+ *   where the workspace holds the bitmaps and s_kv <= 4 topk, a key-outer
  *   pass ("bwd_key_outer" in sparse_mla_last_kernel): per block of 64 KV rows
  *   and chunk of 128 query rows, P and dS are recomputed for the rows that
  *   name a key of the block and dK + dV summed in registers, one atomic add

@@ -94,7 +94,7 @@ def test_bwd_matches_oracle(d_qk, with_length, with_sink):
     dout = W.bwd_dout(case, seed=5)
     out, lse = _oracle_stats(case)
     dq, dkv, ds = _run(case, out, lse, dout)
-    # s_kv = 200 is within 8 row widths of topk = 96: the key-outer dkv pass,
+    # s_kv = 200 is within 4 row widths of topk = 96: the key-outer dkv pass,
     # with row 1 of the unlengthed case (a key named three times) scattered
     # by the row pass.
     assert smla.last_kernel() == "bwd_key_outer"
@@ -218,10 +218,10 @@ def test_bwd_random_shapes():
 @pytest.mark.parametrize("d_qk", [576, 512])
 def test_bwd_key_outer_and_scatter_paths_agree(d_qk):
     """One selection through both dkv paths: topk = 40 over s_kv = 400 KV rows
-    scatters per (row, key) pair (the table is more than 8 row widths), and
-    the same indices padded with -1 to topk = 64 go through the key-outer
+    scatters per (row, key) pair (the table is more than 4 row widths), and
+    the same indices padded with -1 to topk = 100 go through the key-outer
     pass.  Both match the oracle; ragged key blocks (400 = 6 x 64 + 16) and
-    rows past one 128-row chunk (s_q = 150) included."""
+    a ragged last row chunk (s_q = 150) included."""
     case = W.make_prefill(f"bwd_paths_d{d_qk}", s_q=150, s_kv=400, h_q=64, d_qk=d_qk, d_v=512,
                           topk=40, layout="scattered", invalid_frac=0.1, empty_frac=0.05,
                           seed=77, with_sink=True)
@@ -229,7 +229,7 @@ def test_bwd_key_outer_and_scatter_paths_agree(d_qk):
     out, lse = _oracle_stats(case)
     dq_s, dkv_s, ds_s = _run(case, out, lse, dout)
     assert smla.last_kernel() == "bwd_scatter"
-    padded = torch.full((150, 1, 64), -1, dtype=torch.int32)
+    padded = torch.full((150, 1, 100), -1, dtype=torch.int32)
     padded[:, :, :40] = case.indices
     wide = dataclasses.replace(case, name=case.name + "_padded", indices=padded)
     dq_k, dkv_k, ds_k = _run(wide, out, lse, dout)
