@@ -510,8 +510,16 @@ def kernel_file(workload):
 
 def kernel_name(workload):
     """Name fragment of the workload's dominant kernel in rocprofv3 records."""
-    return {"bwd_h64": "sparse_mla_bwd_kernel",
+    return {"bwd_h64": "sparse_mla_bwd_dkv_kernel",
             "block_sparse_h8": "block_sparse_fwd"}.get(workload, "sparse_mla_fwd")
+
+
+def call_kernels(workload):
+    """Name fragments of the kernels whose counters one call adds up: the
+    dominant kernel, and for the backward also its row pass."""
+    if workload == "bwd_h64":
+        return ["sparse_mla_bwd_dkv_kernel", "sparse_mla_bwd_kernel<"]
+    return [kernel_name(workload)]
 
 
 def kernel_source_digest(workload=None):
@@ -590,22 +598,26 @@ def ingest_counters(d):
         if w == "copy":
             continue
         digest = kernel_source_digest(w)
-        f = _counter_values(sub / "run_counter_collection.csv", kernel_name(w))
-        wr = _counter_values(d / f"pmc_{w}_WRITE_SIZE" / "run_counter_collection.csv", kernel_name(w))
-        if not f or not wr:
+        f = [_counter_values(sub / "run_counter_collection.csv", k) for k in call_kernels(w)]
+        wr = [_counter_values(d / f"pmc_{w}_WRITE_SIZE" / "run_counter_collection.csv", k)
+              for k in call_kernels(w)]
+        if not all(f) or not all(wr):
             continue
-        fetch = statistics.fmean(f) * 1024.0 * cal["FETCH_SIZE"]
-        write = statistics.fmean(wr) * 1024.0 * cal["WRITE_SIZE"]
+        # Per call: the sum over the call's kernels of each one's mean per dispatch.
+        fetch = sum(statistics.fmean(v) for v in f) * 1024.0 * cal["FETCH_SIZE"]
+        write = sum(statistics.fmean(v) for v in wr) * 1024.0 * cal["WRITE_SIZE"]
         rec = {"workload": w, "hbm_bytes_per_launch": fetch + write,
                "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
-               "fetch_kib_raw_mean": statistics.fmean(f), "write_kib_raw_mean": statistics.fmean(wr),
-               "dispatches": [len(f), len(wr)],
+               "kernels": call_kernels(w),
+               "fetch_kib_raw_mean": [statistics.fmean(v) for v in f],
+               "write_kib_raw_mean": [statistics.fmean(v) for v in wr],
+               "dispatches": [[len(v) for v in f], [len(v) for v in wr]],
                "copy_calibration_factor": {"FETCH_SIZE": cal["FETCH_SIZE"], "WRITE_SIZE": cal["WRITE_SIZE"]},
                "command": f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> -o run --output-format csv -- "
                           f"python3 -u bench.py --workload {w} --no-variants --groups 0 --steps 3 --warmup 1 --cpu-seconds 0 --replicas 0; "
                           f"calibration: ... -- python3 -u bench.py --calibrate-copy",
                "kernel_source_sha256_16": digest}
-        busy = _mfma_busy(d / f"pmc_{w}_MFMA", kernel_name(w))
+        busy = _mfma_busy(d / f"pmc_{w}_MFMA", call_kernels(w))
         if busy is not None:
             rec.update(busy)
         PROFILES.mkdir(exist_ok=True)
@@ -665,12 +677,13 @@ def write_counter_summary(d, cal):
     print("wrote profiles/counters_summary.md")
 
 
-def _mfma_busy(sub, kernel="sparse_mla_fwd"):
-    """MFMA-busy fraction of the attention kernel from one rocprofv3 run with
+def _mfma_busy(sub, kernels=("sparse_mla_fwd",)):
+    """MFMA-busy fraction of a call's kernels from one rocprofv3 run with
     SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.  The SQ counter sums busy
     cycles over every SIMD; GRBM_GUI_ACTIVE sums the active cycles of every
     XCD; the agent record gives the SIMD and XCD counts:
-        busy = MFMA_BUSY / ((GUI_ACTIVE / Num_Xcc) * Simd_Count)."""
+        busy = MFMA_BUSY / ((GUI_ACTIVE / Num_Xcc) * Simd_Count),
+    each summed over the call's kernels (means per dispatch)."""
     import csv
     f = sub / "run_counter_collection.csv"
     a = sub / "run_agent_info.csv"
@@ -681,17 +694,20 @@ def _mfma_busy(sub, kernel="sparse_mla_fwd"):
         for r in csv.DictReader(fh):
             if r.get("Name", "").startswith("gfx"):
                 simd, xcc = int(r["Simd_Count"]), int(r["Num_Xcc"])
-    vals = {}
     with open(f) as fh:
-        rows = [r for r in csv.DictReader(fh) if kernel in r["Kernel_Name"]]
-    if not rows or not simd:
-        return None
-    name = rows[0]["Kernel_Name"]
-    for r in rows:
-        if r["Kernel_Name"] == name:
-            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    busy = statistics.fmean(vals["SQ_VALU_MFMA_BUSY_CYCLES"])
-    gui = statistics.fmean(vals["GRBM_GUI_ACTIVE"])
+        all_rows = list(csv.DictReader(fh))
+    busy = gui = 0.0
+    for kernel in kernels:
+        rows = [r for r in all_rows if kernel in r["Kernel_Name"]]
+        if not rows or not simd:
+            return None
+        name = rows[0]["Kernel_Name"]
+        vals = {}
+        for r in rows:
+            if r["Kernel_Name"] == name:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        busy += statistics.fmean(vals["SQ_VALU_MFMA_BUSY_CYCLES"])
+        gui += statistics.fmean(vals["GRBM_GUI_ACTIVE"])
     return {"mfma_busy_frac": busy / ((gui / xcc) * simd),
             "mfma_busy_cycles_mean": busy, "grbm_gui_active_mean": gui,
             "mfma_busy_command": f"rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE -o run "
@@ -719,7 +735,7 @@ def summarize_traces(d):
         line = json.loads(bench_f.read_text().strip().splitlines()[-1])
         stats = [r for r in csv.DictReader(open(stats_f))
                  if "sparse_mla" in r["Name"] or "block_sparse" in r["Name"] or "combine" in r["Name"]
-                 or "row_lengths" in r["Name"] or "dkv" in r["Name"]]
+                 or "row_lengths" in r["Name"] or "dkv" in r["Name"] or "bwd_" in r["Name"]]
         name_frag = kernel_name(w)
         disp = sorted((r for r in csv.DictReader(open(trace_f)) if name_frag in r["Kernel_Name"]),
                       key=lambda r: int(r["Start_Timestamp"]))
