@@ -451,15 +451,17 @@ template <int D>
 struct KoTile {
   static constexpr int kQRow = 2 * D + 16;             // padded LDS row of a query head
   static constexpr int kDoRow = 2 * kDV + 16;          // ... of a dout head
-  static constexpr int kSRow = 2 * kHeads + 16;        // ... of dS^T / P^T (one key)
+  static constexpr int kSRow = 2 * kKoKeys + 16;       // ... of dS / P (one head, 64 keys)
   static constexpr int kQBytes = kHeads * kQRow;
   static constexpr int kDoBytes = kHeads * kDoRow;
-  static constexpr int kSBytes = kKoKeys * kSRow;
+  static constexpr int kSBytes = kHeads * kSRow;
   static constexpr int kStatBytes = 2 * kHeads * 4;   // a row's normalisers and deltas
   static constexpr int kLds = kQBytes + kDoBytes + 2 * kSBytes + kStatBytes + kKoMaxRows * 12 + 16;
   static constexpr int kSteps = D / 16;                // 32x32x16 steps over d_qk
   static constexpr int kVSteps = kDV / 16;             // ... over d_v
-  static constexpr int kWaveCols = D / 64;             // 32-column dkv tiles per wave
+  // A wave's dkv tiles, for both 32-key halves of the block: value tiles
+  // 4w .. 4w + 3 and, at d576, waves 0 and 1 the rope tiles 16 and 17.
+  static constexpr int kWaveCols = D > kDV ? 5 : 4;
   static constexpr int kQCopies = (kHeads / kWaves) * (D > kDV ? 2 : 1);  // per wave and row
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(kQCopies < 64, "vmcnt range");
@@ -491,7 +493,8 @@ __device__ __forceinline__ void wait_vm() {
 // One workgroup per (row chunk, key block).  Wave w
 // computes S^T and dP^T for keys 32 (w / 2) .. +31 and heads 32 (w % 2) ..
 // +31 (its K fragments stay in registers for the whole chunk), and owns the
-// dkv tiles of the same 32 keys and half of the 32-column tiles.
+// dkv tiles of a quarter of the value columns (and at d576 half of the rope
+// columns) for all 64 keys.
 // Each row's query heads, dout heads and statistics reach LDS by DMA in two
 // parts, so that each overlaps products of the row before:
 //   top of row t: dout_t and stats_t in LDS, q_t in flight;
@@ -505,8 +508,8 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[T::kLds];
   LDS_AS uint8_t* qs = (LDS_AS uint8_t*)lds_raw;     // query heads [64][kQRow]
   LDS_AS uint8_t* dos = qs + T::kQBytes;              // dout heads [64][kDoRow]
-  LDS_AS uint8_t* dss = dos + T::kDoBytes;            // dS^T [64 keys][kSRow]
-  LDS_AS uint8_t* pss = dss + T::kSBytes;             // P^T  [64 keys][kSRow]
+  LDS_AS uint8_t* dss = dos + T::kDoBytes;            // dS [64 heads][kSRow]
+  LDS_AS uint8_t* pss = dss + T::kSBytes;             // P  [64 heads][kSRow]
   LDS_AS uint8_t* sts = pss + T::kSBytes;             // l2[64], delta[64] of the row
   LDS_AS uint64_t* rsel = (LDS_AS uint64_t*)(sts + T::kStatBytes);  // their key masks
   LDS_AS int32_t* rlist = (LDS_AS int32_t*)(rsel + kKoMaxRows);      // rows of the chunk
@@ -590,12 +593,13 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
 #pragma unroll
     for (int s = 0; s < T::kSteps; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
   }
-  // The wave's dkv column tiles: 8 value tiles 8 hh .. 8 hh + 7 (the same
-  // count in both waves), then at d576 the rope tile 16 + hh.
-  auto tile_col = [&](int c) { return c < kDV / 64 ? 8 * hh + c : kDV / 32 + hh; };
-  f32x16 acc[T::kWaveCols];
+  // The wave's dkv column tiles (both key halves): value tiles 4w .. 4w + 3,
+  // then at d576 the rope tile 16 + w for waves 0 and 1 (`has_rope`).
+  auto tile_col = [&](int c) { return c < 4 ? 4 * wave + c : kDV / 32 + (wave & 1); };
+  const bool has_rope = D > kDV && wave < 2;
+  f32x16 acc[2][T::kWaveCols];
 #pragma unroll
-  for (int c = 0; c < T::kWaveCols; ++c) acc[c] = f32x16{};
+  for (int c = 0; c < T::kWaveCols; ++c) acc[0][c] = acc[1][c] = f32x16{};
 
   const int head = 32 * hh + j32;
   int t = __builtin_amdgcn_readfirstlane(rlist[0]);
@@ -644,31 +648,41 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
         __builtin_amdgcn_sched_barrier(0);  // keeps the read-ahead distance
       }
     }
+    // dS and P go to LDS as [head][key]: the lane's four consecutive keys
+    // 32 kh + 8 g + 4 half .. +3 in one 8-byte store.
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 32 * kh + 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool on = (sel >> key) & 1ull;
-      const float p = on ? __builtin_amdgcn_exp2f(st[i] * a.scale_log2 - l2) : 0.f;
-      const float ds = on ? a.scale * p * (dpt[i] - dl) : 0.f;
-      *reinterpret_cast<LDS_AS __bf16*>(dss + key * T::kSRow + head * 2) = (__bf16)ds;
-      *reinterpret_cast<LDS_AS __bf16*>(pss + key * T::kSRow + head * 2) = (__bf16)p;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 d4, p4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        const int key = 32 * kh + 8 * g + 4 * half + r;
+        const bool on = (sel >> key) & 1ull;
+        const float p = on ? __builtin_amdgcn_exp2f(st[i] * a.scale_log2 - l2) : 0.f;
+        const float ds = on ? a.scale * p * (dpt[i] - dl) : 0.f;
+        d4[r] = (__bf16)ds;
+        p4[r] = (__bf16)p;
+      }
+      const int off = head * T::kSRow + (32 * kh + 8 * g + 4 * half) * 2;
+      *reinterpret_cast<LDS_AS bf16x4*>(dss + off) = d4;
+      *reinterpret_cast<LDS_AS bf16x4*>(pss + off) = p4;
     }
-    __syncthreads();  // dS^T and P^T of the block are in LDS
+    __syncthreads();  // dS and P of the block are in LDS
 
     // dkv[32 keys x 32 columns] += P^T dO on the value columns, then dS^T Q,
-    // contracted over the 64 heads in four steps of 16.  Product n of a
-    // phase is head step n / C and tile n % C; its B operand is read kAhead
-    // products ahead.
-    bf16x8 af[4], pf[4];
+    // contracted over the 64 heads in four steps of 16, for both key halves:
+    // each B operand (read kAhead reads ahead) serves two products.  Read n
+    // of a phase is head step n / C and tile n % C.
+    bf16x8 af[2][4], pf[2][4];
 #pragma unroll
-    for (int hs = 0; hs < 4; ++hs) {
-      af[hs] = *reinterpret_cast<const LDS_AS bf16x8*>(dss + (32 * kh + j32) * T::kSRow + 32 * hs +
-                                                       16 * half);
-      pf[hs] = *reinterpret_cast<const LDS_AS bf16x8*>(pss + (32 * kh + j32) * T::kSRow + 32 * hs +
-                                                       16 * half);
-    }
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int hs = 0; hs < 4; ++hs) {
+        af[k2][hs] = tr_col8(dss, T::kSRow, 16 * hs, 32 * k2, lane);
+        pf[k2][hs] = tr_col8(pss, T::kSRow, 16 * hs, 32 * k2, lane);
+      }
     {
-      constexpr int C = kDV / 64, N = 4 * C;
+      constexpr int C = 4, N = 4 * C;
       auto bop = [&](int n) { return tr_col8(dos, T::kDoRow, 16 * (n / C), 32 * tile_col(n % C), lane); };
       bf16x8 bq[kAhead];
 #pragma unroll
@@ -677,7 +691,8 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
       for (int n = 0; n < N; ++n) {
         const bf16x8 cur = bq[n % kAhead];
         if (n + kAhead < N) bq[n % kAhead] = bop(n + kAhead);
-        acc[n % C] = mfma32(pf[n / C], cur, acc[n % C]);
+        acc[0][n % C] = mfma32(pf[0][n / C], cur, acc[0][n % C]);
+        acc[1][n % C] = mfma32(pf[1][n / C], cur, acc[1][n % C]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -685,9 +700,9 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
     const int tn = more ? __builtin_amdgcn_readfirstlane(rlist[v + 1]) : t;
     __syncthreads();  // dout and stats are free
     {
-      // The next row's dout copies go out one per product, under the MFMAs.
+      // The next row's dout copies go out one per B read, under the MFMAs.
       constexpr int C = T::kWaveCols, N = 4 * C;
-      static_assert(N >= kHeads / kWaves, "one copy per product");
+      static_assert(N >= kHeads / kWaves, "one copy per read");
       auto bop = [&](int n) { return tr_col8(qs, T::kQRow, 16 * (n / C), 32 * tile_col(n % C), lane); };
       bf16x8 bq[kAhead];
 #pragma unroll
@@ -696,7 +711,10 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
       for (int n = 0; n < N; ++n) {
         const bf16x8 cur = bq[n % kAhead];
         if (n + kAhead < N) bq[n % kAhead] = bop(n + kAhead);
-        acc[n % C] = mfma32(af[n / C], cur, acc[n % C]);
+        if (n % C < 4 || has_rope) {
+          acc[0][n % C] = mfma32(af[0][n / C], cur, acc[0][n % C]);
+          acc[1][n % C] = mfma32(af[1][n / C], cur, acc[1][n % C]);
+        }
         if (n < kHeads / kWaves && more) issue_dout_one(tn, n);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -710,16 +728,19 @@ sparse_mla_bwd_dkv_kernel(DkvArgs a) {
     t = tn;
   }
 
-  // acc[c][i] is dkv[key0 + 32 kh + 8 (i / 4) + 4 half + i % 4][32 tile_col(c) + j32].
+  // acc[k2][c][i] is dkv[key0 + 32 k2 + 8 (i / 4) + 4 half + i % 4][32 tile_col(c) + j32].
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = key0 + 32 * kh + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (key < a.s_kv) {
-      float* drow = a.dkv_acc + (size_t)key * D + j32;
+  for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int c = 0; c < T::kWaveCols; ++c) unsafeAtomicAdd(drow + 32 * tile_col(c), acc[c][i]);
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + 32 * k2 + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (key < a.s_kv) {
+        float* drow = a.dkv_acc + (size_t)key * D + j32;
+#pragma unroll
+        for (int c = 0; c < T::kWaveCols; ++c)
+          if (c < 4 || has_rope) unsafeAtomicAdd(drow + 32 * tile_col(c), acc[k2][c][i]);
+      }
     }
-  }
 }
 
 // Zero fill (also the fp32 accumulators before a launch).
