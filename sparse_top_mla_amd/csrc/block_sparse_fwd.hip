@@ -449,15 +449,22 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
     const LDS_AS uint8_t* ks = lds + cur * kStageD;
     const LDS_AS uint8_t* vs = lds + prv * kStageD + kTile * kKRowD;  // tile i - 1's V
     const int tile0 = t0_0, key_end = t0_0 + n_0;
-    f32x16 sc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sc[kt] = f32x16{};
+    // S^T as two interleaved chains (the tile's two 32-key halves), each
+    // step's K fragments read one step ahead of its MFMAs.
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    {
+      auto rd = [&](int s, int kt) {
+        return *reinterpret_cast<const LDS_AS bf16x8*>(
+            ks + (kt * 32 + j32) * kKRowD + (((2 * s + half) ^ (j32 & 15)) << 4));
+      };
+      bf16x8 kr[2] = {rd(0, 0), rd(0, 1)};
 #pragma unroll
       for (int s = 0; s < kSteps16; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const LDS_AS bf16x8*>(
-            ks + (kt * 32 + j32) * kKRowD + (((2 * s + half) ^ (j32 & 15)) << 4));
-        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kt], 0, 0, 0);
+        const bf16x8 k0 = kr[0], k1 = kr[1];
+        if (s + 1 < kSteps16) { kr[0] = rd(s + 1, 0); kr[1] = rd(s + 1, 1); }
+        sc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sc[0], 0, 0, 0);
+        sc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sc[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Tile i's softmax, in pieces: mask (keys past the tile; with CAUSAL keys
@@ -511,16 +518,24 @@ block_sparse_fwd_ring_kernel(BsArgs a) {
         rsum = __builtin_bit_cast(float, r.x) + __builtin_bit_cast(float, r.y);
       }
     };
+    // V^T fragment of P*V product n, read one product ahead.
+    auto vread = [&](int n) {
+      const int u = n >> 2, ct = n & 3;
+      const LDS_AS uint8_t* p =
+          vs + (16 * u + vrow) * kVRowD + (((4 * ct + vchunk) ^ vswz) << 4) + vbyte;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 8 * kVRowD));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 vnext{};
+    if constexpr (decltype(do_pv)::value) vnext = vread(0);
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
       if constexpr (decltype(do_pv)::value) {
         // O^T += V^T P^T of tile i - 1: key step u = n / 4, value tile ct = n % 4
         const int u = n >> 2, ct = n & 3;
-        const LDS_AS uint8_t* p =
-            vs + (16 * u + vrow) * kVRowD + (((4 * ct + vchunk) ^ vswz) << 4) + vbyte;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)p);
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(p + 8 * kVRowD));
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = vnext;
+        if (n + 1 < 16) vnext = vread(n + 1);
         acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pprev[u], acc[ct], 0, 0, 0);
       }
       sm_piece(n);
