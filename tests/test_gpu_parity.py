@@ -680,6 +680,9 @@ def test_full_prefill_h128():
     assert torch.isfinite(lse[~is_empty]).all()
     rl = smla.row_lengths(c.indices.to(DEV), s_kv=c.s_kv).cpu().numpy()
     assert np.array_equal(rl, oracle.row_lengths(c.indices, s_kv=c.s_kv))
+    # Every row: the derived lengths given explicitly change nothing, bit for bit.
+    explicit = run_prefill(c, topk_length=torch.from_numpy(rl).to(torch.int32))
+    assert_bitwise(res, explicit, "full h128: derived vs explicit length")
 
 
 def test_full_decode_dynamic():
@@ -699,3 +702,14 @@ def test_full_decode_fixed():
     rows = sample_rows(c.batch * c.s_q, 12, seed=3)
     assert_parity(res, oracle_decode(c, rows=rows), c.name, rows=rows)
     assert torch.isfinite(res[0].float()).all() and torch.isfinite(res[1]).all()
+    # Every row: lengths topk - (row % 64) given explicitly, against the same
+    # positions past each length poisoned with INT_MAX (an invalid index) and
+    # the length left to the tail scan; the two must agree bit for bit.
+    B, s_q, topk = c.indices.shape
+    lengths = (topk - torch.arange(B * s_q) % 64).to(torch.int32).view(B, s_q)
+    poisoned = c.indices.clone()
+    pos = torch.arange(topk).view(1, 1, topk)
+    poisoned[pos >= lengths.unsqueeze(-1)] = 2**31 - 1
+    explicit = run_decode(c, topk_length=lengths)
+    derived = run_decode(c, topk_length=None, indices=poisoned)
+    assert_bitwise(explicit, derived, "full decode: explicit lengths vs INT_MAX past them")
