@@ -87,6 +87,7 @@ struct BwdArgs {
                             // log2 units (0..63), then dout . out (64..127)
   const int32_t* dup;       // [s_q]: 1 where the row names a key twice (key-outer mode)
   int32_t key_outer;        // 1: dkv comes from the key-outer pass, except rows with dup
+  int32_t dup_only;         // 1: only rows with dup run (their dq again, and their scatter)
   int32_t s_q, s_kv, topk;
   float scale;              // sm_scale
   float lse_to_log2;        // log2(e) for natural-log lse, 1 for base-2 lse
@@ -111,6 +112,12 @@ struct BwdTile {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // LDS [lds + 16 lane, +16) <- this lane's 16 bytes at src, by LDS DMA.  The
 // compiler does not count it: the kernel waits for it with vmcnt itself.
@@ -162,6 +169,7 @@ sparse_mla_bwd_kernel(BwdArgs a) {
   const int head = wave * 16 + hl;
   const int row = blockIdx.x;
   const size_t rh = (size_t)row * kHeads + head;
+  if (a.dup_only && a.dup[row] == 0) return;  // the whole workgroup
   // Whether this row scatters its own dkv (the same in every wave).
   const bool scatter = a.key_outer == 0 || a.dup[row] != 0;
 
@@ -385,6 +393,200 @@ sparse_mla_bwd_kernel(BwdArgs a) {
                       (__bf16)dqa[ct][3]};
     *reinterpret_cast<bf16x4*>(dqp + ct * 16) = v;
   }
+  if (SINK && a.d_sink != nullptr && !a.dup_only && g == 0 && !__builtin_isinf(l2))
+    unsafeAtomicAdd(a.d_sink + head, -__builtin_amdgcn_exp2f(sk2 - l2) * delta);
+}
+
+// ---------------------------------------------------------------------------
+// dq pass of key-outer calls
+// ---------------------------------------------------------------------------
+// The row pass without the scatter (rows that name a key twice run the row
+// pass above afterwards, alone): the query slice stays in registers, so LDS
+// holds four 32-key KV blocks and the row's index list, and each block's
+// rows are gathered three blocks ahead.  Masked rows copy a row of zeros,
+// so every block takes the same number of copies and the waits count them.
+
+constexpr int kDqBufs = 4;          // KV blocks in LDS
+constexpr int kDqMaxTopk = 3072;    // the row's index list in LDS
+
+template <int D>
+struct DqTile {
+  static constexpr int kRow = 2 * D + 16;          // padded LDS row of a KV row
+  static constexpr int kKBytes = kBK * kRow;
+  static constexpr int kLds = kDqBufs * kKBytes + kDqMaxTopk * 4;
+  static constexpr int kDSteps = D / 32;           // 16x16x32 steps over d_qk
+  static constexpr int kVSteps = kDV / 32;         // ... over d_v
+  static constexpr int kTiles = D / 16;            // 16-column tiles of a KV row
+  static constexpr int kCopies = (kBK / kWaves) * (D > kDV ? 2 : 1);  // per wave and block
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static_assert(2 * kCopies < 64, "vmcnt range");
+};
+
+__device__ __attribute__((aligned(16))) const uint8_t g_zero_kv_row[2 * 576] = {};
+
+template <int D, bool SINK>
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+sparse_mla_bwd_dq_kernel(BwdArgs a) {
+  using T = DqTile<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[T::kLds];
+  LDS_AS uint8_t* kbuf = (LDS_AS uint8_t*)lds_raw;                          // [4][32][kRow]
+  LDS_AS int32_t* idx_l = (LDS_AS int32_t*)(kbuf + kDqBufs * T::kKBytes);  // the row's indices
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int hl = lane & 15;
+  const int head = wave * 16 + hl;
+  const int row = blockIdx.x;
+  const size_t rh = (size_t)row * kHeads + head;
+
+  // dO (B operand of dP^T) and the query slice (of S^T) in registers, for
+  // this lane's head: columns 32 s + 8 g .. +7.
+  const __bf16* dop = a.dout + rh * kDV + g * 8;
+  const __bf16* op = a.out + rh * kDV + g * 8;
+  bf16x8 dor[T::kVSteps];
+  float delta = 0.f;
+#pragma unroll
+  for (int s = 0; s < T::kVSteps; ++s) {
+    dor[s] = *reinterpret_cast<const bf16x8*>(dop + s * 32);
+    const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(op + s * 32);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) delta += (float)dor[s][e] * (float)o8[e];
+  }
+  delta += __shfl_xor(delta, 16);
+  delta += __shfl_xor(delta, 32);
+  bf16x8 qr[T::kDSteps];
+  {
+    const __bf16* qp = a.q + rh * D + g * 8;
+#pragma unroll
+    for (int s = 0; s < T::kDSteps; ++s) qr[s] = *reinterpret_cast<const bf16x8*>(qp + s * 32);
+  }
+
+  float l2 = a.lse[rh] * a.lse_to_log2;
+  float sk2 = 0.f;
+  if (SINK) {
+    sk2 = a.attn_sink[head] * kLog2e;
+    if (!__builtin_isinf(l2)) {
+      const float m = fmaxf(l2, sk2);
+      l2 = m + __log2f(__builtin_amdgcn_exp2f(l2 - m) + __builtin_amdgcn_exp2f(sk2 - m));
+    }
+  }
+  const float scale_log2 = a.scale * kLog2e;
+  if (a.stats_out != nullptr && g == 0) {
+    a.stats_out[(size_t)row * 2 * kHeads + head] = l2;
+    a.stats_out[(size_t)row * 2 * kHeads + kHeads + head] = delta;
+  }
+
+  const int L = a.row_len[row];
+  const int nblk = (L + kBK - 1) / kBK;
+  {
+    const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+    for (int p = tid; p < nblk * kBK; p += kWaves * 64) idx_l[p] = p < L ? idx_row[p] : -1;
+  }
+  f32x4 dqa[T::kTiles];
+#pragma unroll
+  for (int ct = 0; ct < T::kTiles; ++ct) dqa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Every load above has landed: the loop has none the compiler would wait for.
+  wait_vm<0>();
+  __syncthreads();
+
+  // Rows wave + 4 i of block kb into buffer kb % 4.
+  auto gather = [&](int kb) {
+    LDS_AS uint8_t* buf = kbuf + (kb % kDqBufs) * T::kKBytes;
+#pragma unroll
+    for (int i = 0; i < kBK / kWaves; ++i) {
+      const int j = wave + kWaves * i;
+      const int e = __builtin_amdgcn_readfirstlane(idx_l[kb * kBK + j]);
+      const uint8_t* src = e >= 0 && e < a.s_kv
+                               ? reinterpret_cast<const uint8_t*>(a.kv) + (size_t)(uint32_t)e * (2 * D)
+                               : g_zero_kv_row;
+      lds_dma16(src + lane * 16, buf + j * T::kRow);
+      if (D > kDV && lane < (2 * D - 2 * kDV) / 16)
+        lds_dma16(src + 2 * kDV + lane * 16, buf + j * T::kRow + 2 * kDV);
+    }
+  };
+  for (int kb = 0; kb < nblk && kb < kDqBufs - 1; ++kb) gather(kb);
+
+  for (int kb = 0; kb < nblk; ++kb) {
+    // Block kb's copies are done once at most the later blocks' are pending.
+    const int later = min(nblk - 1 - kb, kDqBufs - 2);
+    if (later >= 2) wait_vm<2 * T::kCopies>();
+    else if (later == 1) wait_vm<T::kCopies>();
+    else wait_vm<0>();
+    __syncthreads();  // ... in every wave; block kb - 1's readers are done
+    if (kb + kDqBufs - 1 < nblk) gather(kb + kDqBufs - 1);
+    const LDS_AS uint8_t* ks = kbuf + (kb % kDqBufs) * T::kKBytes;
+    const int idx = lane < kBK ? idx_l[kb * kBK + lane] : -1;
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(idx >= 0 && idx < a.s_kv);
+
+    // S^T and dP^T: lane (g, hl) holds keys 16 kt + 4g + r of head `head`;
+    // the two key rows of a step are read kRowAhead steps ahead.
+    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 dpt[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      auto rd = [&](int s, int kt) {
+        return *reinterpret_cast<const LDS_AS bf16x8*>(ks + (kt * 16 + hl) * T::kRow + s * 64 + g * 16);
+      };
+      bf16x8 buf[kRowAhead][2];
+#pragma unroll
+      for (int s = 0; s < kRowAhead; ++s) {
+        buf[s][0] = rd(s, 0);
+        buf[s][1] = rd(s, 1);
+      }
+#pragma unroll
+      for (int s = 0; s < T::kDSteps; ++s) {
+        const bf16x8 kf0 = buf[s % kRowAhead][0], kf1 = buf[s % kRowAhead][1];
+        if (s + kRowAhead < T::kDSteps) {
+          buf[s % kRowAhead][0] = rd(s + kRowAhead, 0);
+          buf[s % kRowAhead][1] = rd(s + kRowAhead, 1);
+        }
+        st[0] = mfma(kf0, qr[s], st[0]);
+        st[1] = mfma(kf1, qr[s], st[1]);
+        if (s < T::kVSteps) {
+          dpt[0] = mfma(kf0, dor[s], dpt[0]);
+          dpt[1] = mfma(kf1, dor[s], dpt[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keeps the read-ahead distance
+      }
+    }
+
+    // dS (scaled by sm_scale); masked keys get 0.
+    bf16x8 dsf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt * 16 + 4 * g + r;
+        const bool valid = (mask >> key) & 1ull;
+        const float p = valid ? __builtin_amdgcn_exp2f(st[kt][r] * scale_log2 - l2) : 0.f;
+        dsf[kt * 4 + r] = (__bf16)(a.scale * p * (dpt[kt][r] - delta));
+      }
+
+    // dQ^T += K^T dS^T: element e of both operands is key 16 (e / 4) + 4g + e % 4.
+    {
+      bf16x8 kt_op[kDqAhead];
+#pragma unroll
+      for (int ct = 0; ct < kDqAhead; ++ct) kt_op[ct] = tr_pair(ks, T::kRow, 0, ct * 16, g, hl);
+#pragma unroll
+      for (int ct = 0; ct < T::kTiles; ++ct) {
+        const bf16x8 cur = kt_op[ct % kDqAhead];
+        if (ct + kDqAhead < T::kTiles)
+          kt_op[ct % kDqAhead] = tr_pair(ks, T::kRow, 0, (ct + kDqAhead) * 16, g, hl);
+        dqa[ct] = mfma(cur, dsf, dqa[ct]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // dq[row][head][16 ct + 4g + r] = dqa[ct][r].
+  __bf16* dqp = a.dq + rh * D + g * 4;
+#pragma unroll
+  for (int ct = 0; ct < T::kTiles; ++ct) {
+    const bf16x4 v = {(__bf16)dqa[ct][0], (__bf16)dqa[ct][1], (__bf16)dqa[ct][2],
+                      (__bf16)dqa[ct][3]};
+    *reinterpret_cast<bf16x4*>(dqp + ct * 16) = v;
+  }
   if (SINK && a.d_sink != nullptr && g == 0 && !__builtin_isinf(l2))
     unsafeAtomicAdd(a.d_sink + head, -__builtin_amdgcn_exp2f(sk2 - l2) * delta);
 }
@@ -484,11 +686,6 @@ __device__ __forceinline__ bf16x8 tr_col8(const LDS_AS uint8_t* tile, int row_by
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 // One workgroup per (row chunk, key block).  Wave w
 // computes S^T and dP^T for keys 32 (w / 2) .. +31 and heads 32 (w % 2) ..
@@ -918,18 +1115,42 @@ extern "C" smla_status sparse_mla_bwd(const void* q, const void* kv, const void*
       args.key_outer = 1;
     }
     const bool sink = attn_sink != nullptr;
-    if (d_qk == 576) {
-      if (sink)
-        hipLaunchKernelGGL((sparse_mla_bwd_kernel<576, true>), dim3(s_q), dim3(256), 0, st, args);
-      else
-        hipLaunchKernelGGL((sparse_mla_bwd_kernel<576, false>), dim3(s_q), dim3(256), 0, st, args);
+    auto row_pass = [&](const BwdArgs& ra) {
+      if (d_qk == 576) {
+        if (sink)
+          hipLaunchKernelGGL((sparse_mla_bwd_kernel<576, true>), dim3(s_q), dim3(256), 0, st, ra);
+        else
+          hipLaunchKernelGGL((sparse_mla_bwd_kernel<576, false>), dim3(s_q), dim3(256), 0, st, ra);
+      } else {
+        if (sink)
+          hipLaunchKernelGGL((sparse_mla_bwd_kernel<512, true>), dim3(s_q), dim3(256), 0, st, ra);
+        else
+          hipLaunchKernelGGL((sparse_mla_bwd_kernel<512, false>), dim3(s_q), dim3(256), 0, st, ra);
+      }
+      return launched();
+    };
+    if (key_outer && topk <= kDqMaxTopk) {
+      // dq, d_sink and the statistics for every row, then the rows that name
+      // a key twice again through the row pass, for their scatter.
+      if (d_qk == 576) {
+        if (sink)
+          hipLaunchKernelGGL((sparse_mla_bwd_dq_kernel<576, true>), dim3(s_q), dim3(256), 0, st, args);
+        else
+          hipLaunchKernelGGL((sparse_mla_bwd_dq_kernel<576, false>), dim3(s_q), dim3(256), 0, st, args);
+      } else {
+        if (sink)
+          hipLaunchKernelGGL((sparse_mla_bwd_dq_kernel<512, true>), dim3(s_q), dim3(256), 0, st, args);
+        else
+          hipLaunchKernelGGL((sparse_mla_bwd_dq_kernel<512, false>), dim3(s_q), dim3(256), 0, st, args);
+      }
+      if (smla_status e = launched()) return e;
+      BwdArgs dup_args = args;
+      dup_args.stats_out = nullptr;
+      dup_args.dup_only = 1;
+      if (smla_status e = row_pass(dup_args)) return e;
     } else {
-      if (sink)
-        hipLaunchKernelGGL((sparse_mla_bwd_kernel<512, true>), dim3(s_q), dim3(256), 0, st, args);
-      else
-        hipLaunchKernelGGL((sparse_mla_bwd_kernel<512, false>), dim3(s_q), dim3(256), 0, st, args);
+      if (smla_status e = row_pass(args)) return e;
     }
-    if (smla_status e = launched()) return e;
     if (key_outer) {
       DkvArgs k{};
       k.q = args.q;
