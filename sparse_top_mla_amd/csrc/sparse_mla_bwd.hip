@@ -491,13 +491,15 @@ sparse_mla_bwd_dq_kernel(BwdArgs a) {
   wait_vm<0>();
   __syncthreads();
 
-  // Rows wave + 4 i of block kb into buffer kb % 4.
+  // Rows wave + 4 i of block kb into buffer kb % 4 (their indices read in
+  // one LDS access, lane i holding row wave + 4 i's).
   auto gather = [&](int kb) {
     LDS_AS uint8_t* buf = kbuf + (kb % kDqBufs) * T::kKBytes;
+    const int mine = idx_l[kb * kBK + wave + kWaves * (lane & (kBK / kWaves - 1))];
 #pragma unroll
     for (int i = 0; i < kBK / kWaves; ++i) {
       const int j = wave + kWaves * i;
-      const int e = __builtin_amdgcn_readfirstlane(idx_l[kb * kBK + j]);
+      const int e = __builtin_amdgcn_readlane(mine, i);
       const uint8_t* src = e >= 0 && e < a.s_kv
                                ? reinterpret_cast<const uint8_t*>(a.kv) + (size_t)(uint32_t)e * (2 * D)
                                : g_zero_kv_row;
