@@ -16,10 +16,12 @@
 //                                  dkv[idx_j] += p dout_h (value columns)
 // and, with a sink, d_sink[h] -= exp(sink[h] - lse') delta, once per row.
 //
-// Layout of work: one workgroup per query row, four waves, 16 heads per wave
-// (h_q = 64, the shape the pages give for this operation).  Per block of 32
-// keys:
-//   gather the KV rows into LDS (masked rows as zeros);
+// Three kernels share the work (h_q = 64, the shape the pages give for this
+// operation; four waves, one per SIMD, in each):
+//
+// The row pass (sparse_mla_bwd_kernel), one workgroup per query row, 16 heads
+// per wave.  Per block of 32 keys, gathered into LDS while the block before
+// is computed (masked rows as zeros):
 //   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_16x16x32_bf16 (each lane owns
 //   one head, so lse' and delta are per-lane scalars);
 //   P and dS in registers; dS^T and P^T also go to LDS as bf16;
@@ -28,10 +30,13 @@
 //   added to the fp32 accumulator with global_atomic_add_f32;
 //   dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16 and dS^T taken from
 //   the registers (the key order of both operands is permuted alike).
-// The atomic adds bound the kernel: one fp32 add per valid (row, key) pair
-// and d_qk column.
-// The query rows stay in LDS for the whole row; dO stays in registers (its
-// B-operand fragments for both products).
+// Those atomic adds, one per valid (row, key) pair and d_qk column, bound it.
+//
+// Where the selections are dense enough, the scatter is replaced: the dq
+// pass (sparse_mla_bwd_dq_kernel) is the row pass without it, and the
+// key-outer pass (sparse_mla_bwd_dkv_kernel) sums dK + dV per block of 64 KV
+// rows over the query rows that name them, in registers, with one atomic add
+// per element of the block.  Rows that name a key twice still scatter.
 
 #include <hip/hip_runtime.h>
 
