@@ -2001,7 +2001,7 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
 // weight 0 (it is finite), so the sums keep the split order.
 template <bool SINK>
 __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long w = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (w >= (long long)a.rows * a.h_q) return;
   const int row = (int)(w / a.h_q), head = (int)(w % a.h_q), lane = lane_id();
   const int S = a.splits;
@@ -2304,8 +2304,9 @@ smla_status launch_split(const FwdArgs& args, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   const long long waves = (long long)args.rows * args.h_q;
-  hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                     stream, args);
+  // One wave per workgroup: the (row, head) waves spread over every CU.
+  hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)waves), dim3(64), 0, stream,
+                     args);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
@@ -2325,8 +2326,9 @@ smla_status launch_ring_split(const FwdArgs& args, hipStream_t stream) {
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_kernel = BIG ? "ring_split_big" : "ring_split";
   const long long waves = (long long)args.rows * args.h_q;
-  hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                     stream, args);
+  // One wave per workgroup: the (row, head) waves spread over every CU.
+  hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)waves), dim3(64), 0, stream,
+                     args);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
