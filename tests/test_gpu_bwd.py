@@ -244,3 +244,23 @@ def test_bwd_key_outer_and_scatter_paths_agree(d_qk):
     # dq comes from the same per-row sums on both paths (d_sink's cross-row
     # atomic sum has a run-dependent order).
     assert torch.equal(dq_s, dq_k)
+
+
+def test_bwd_key_outer_with_wide_rows():
+    """topk = 3200 (above the dq pass's 3072-entry index list) over s_kv = 4000:
+    a key-outer call whose dq comes from the row pass itself, with a row that
+    names a key twice among them."""
+    case = W.make_prefill("bwd_wide_rows_d576", s_q=6, s_kv=4000, h_q=64, d_qk=576, d_v=512,
+                          topk=3200, layout="scattered", invalid_frac=0.1, empty_frac=0.0,
+                          seed=97, with_sink=True)
+    case.indices[2, 0, 3000] = case.indices[2, 0, 17]
+    dout = W.bwd_dout(case, seed=98)
+    out, lse = _oracle_stats(case)
+    dq, dkv, ds = _run(case, out, lse, dout)
+    assert smla.last_kernel() == "bwd_key_outer"
+    rq, rkv, rs = oracle.sparse_mla_bwd(case.q, case.kv, out, dout, case.indices, lse,
+                                        case.sm_scale, case.d_v, attn_sink=case.attn_sink,
+                                        want_d_sink=True)
+    _close("dq (wide rows)", dq, rq)
+    _close("dkv (wide rows)", dkv[:, 0, :], rkv)
+    _close("d_sink (wide rows)", ds, rs)
