@@ -70,6 +70,12 @@ constexpr int kRowAhead = 2;     // S / dP steps whose LDS operands are read ahe
 constexpr int kDqAhead = 4;      // dQ products whose K^T operands are read ahead
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Padded LDS row of `bytes` of bf16: 16 bytes of pad, or 32 for a 1 KiB row,
+// so that consecutive rows start 36 or 8 banks apart and neither the 16-byte
+// row reads nor the ds_read_b64_tr_b16 reads (4 rows x 32 bytes per 16 lanes)
+// meet in a bank.
+constexpr int padded_row(int bytes) { return bytes + (bytes == 1024 ? 32 : 16); }
+
 // ds_read_b64_tr_b16: in each 16-lane group, lane i gives the address of four
 // consecutive 16-bit values at row (i >> 2), columns 4 (i & 3) .. +3 of a
 // 4 x 16 tile, and lane n receives column n of the four rows.
@@ -100,7 +106,7 @@ struct BwdArgs {
 
 template <int D>
 struct BwdTile {
-  static constexpr int kRow = 2 * D + 16;          // padded LDS row (query head or KV row)
+  static constexpr int kRow = padded_row(2 * D);   // padded LDS row (query head or KV row)
   static constexpr int kQBytes = kHeads * kRow;
   static constexpr int kKBytes = kBK * kRow;
   static constexpr int kSRow = 2 * kHeads + 16;    // padded LDS row of dS^T / P^T (one key)
@@ -110,7 +116,7 @@ struct BwdTile {
   static constexpr int kVSteps = kDV / 32;         // ... over d_v
   static constexpr int kTiles = D / 16;            // 16-column tiles of a KV row
   static constexpr int kWaveTiles = kTiles / kWaves;  // dKV column tiles per wave
-  static constexpr int kDoRow = 2 * kDV + 16;      // padded LDS row of the staged dO
+  static constexpr int kDoRow = padded_row(2 * kDV);  // padded LDS row of the staged dO
   static_assert(kHeads * kDoRow <= kQBytes + kKBytes, "dO staging fits");
   static_assert(kTiles % kWaves == 0, "column split");
 };
@@ -416,7 +422,7 @@ constexpr int kDqMaxTopk = 3072;    // the row's index list in LDS
 
 template <int D>
 struct DqTile {
-  static constexpr int kRow = 2 * D + 16;          // padded LDS row of a KV row
+  static constexpr int kRow = padded_row(2 * D);   // padded LDS row of a KV row
   static constexpr int kKBytes = kBK * kRow;
   static constexpr int kLds = kDqBufs * kKBytes + kDqMaxTopk * 4;
   static constexpr int kDSteps = D / 32;           // 16x16x32 steps over d_qk
@@ -658,8 +664,8 @@ struct DkvArgs {
 
 template <int D>
 struct KoTile {
-  static constexpr int kQRow = 2 * D + 16;             // padded LDS row of a query head
-  static constexpr int kDoRow = 2 * kDV + 16;          // ... of a dout head
+  static constexpr int kQRow = padded_row(2 * D);      // padded LDS row of a query head
+  static constexpr int kDoRow = padded_row(2 * kDV);   // ... of a dout head
   static constexpr int kSRow = 2 * kKoKeys + 16;       // ... of dS / P (one head, 64 keys)
   static constexpr int kQBytes = kHeads * kQRow;
   static constexpr int kDoBytes = kHeads * kDoRow;
