@@ -488,6 +488,14 @@ __device__ __forceinline__ BlockMeta block_meta(const FwdArgs& a, bool ok, int i
 // bases) would otherwise each be hoisted into a register of their own.
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
 
+// A wave-uniform value that the compiler takes as new where this is called:
+// what is derived from it is computed there, not hoisted out of the
+// enclosing loop (where it would be live across the stage loop and spilled).
+__device__ __forceinline__ int fresh_s(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 // The lane index, computed where it is called: lane_id() is a pure builtin
 // that the compiler computes once and keeps (or spills) for the whole kernel.
 // Values derived from this one are computed per row of the row loop instead
@@ -1450,7 +1458,20 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
 constexpr int kRingStages = 4;       // LDS stages of the gather ring
 constexpr int kRingKeys = 32;        // keys per stage: one tile per wave
 constexpr int kRingMaxTopk = 2048;   // index positions per row (the key list lives in LDS)
-constexpr int kRingChunks = kRingMaxTopk / (kWideWaves * 64);  // 64-position chunks per wave
+
+// The row prologue's division of the waves.  Unsplit (every wave copies a
+// quarter of the query slice, then reads a quarter of the positions), a wave
+// waits for its index and block-table loads behind its query copies: the
+// memory counter completes in issue order.  Split (paged decode rows), two
+// waves copy the query slice while the other two read the index vector and
+// the block table and compact the keys, so the two latencies overlap.
+template <bool WAVE_SPLIT>
+struct RingPrologue {
+  static constexpr bool kSplit = WAVE_SPLIT;
+  static constexpr int kQWaves = WAVE_SPLIT ? 2 : kWideWaves;     // query-copy waves
+  static constexpr int kListWaves = WAVE_SPLIT ? 2 : kWideWaves;  // the last kListWaves waves
+  static constexpr int kChunks = kRingMaxTopk / (kListWaves * 64);  // 64-position chunks per wave
+};
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15: no wait on those).
@@ -1743,12 +1764,22 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t keys_raw[kRingMaxTopk];
   __shared__ int counts_raw[NW];
   __shared__ float sink_lds[SINK ? kHeads : 1];
+  __shared__ uint32_t rsrc_raw[4];
   LDS_AS uint8_t* ring = (LDS_AS uint8_t*)ring_raw;
   LDS_AS uint32_t* keys = (LDS_AS uint32_t*)keys_raw;
   LDS_AS int* counts = (LDS_AS int*)counts_raw;
+  using PRO = RingPrologue<PAGED && !SPLIT>;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_k = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (SINK && (int)threadIdx.x < kHeads) sink_lds[threadIdx.x] = a.attn_sink[threadIdx.x];
+  // The table's resource, read from LDS where a row needs it: kept in
+  // registers across the stage loop it is spilled, and each reload waits for
+  // every copy in flight.
+  if (threadIdx.x == 0) {
+    const u32x4s r = BIG ? big_table_rsrc(a) : table_rsrc(a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ((LDS_AS uint32_t*)rsrc_raw)[i] = r[i];
+  }
 
   bf16x8 qf[T::kDSteps];
   int turn = 0;
@@ -1756,27 +1787,15 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
   for (int unit = turn_row(units, turn, PAGED); unit >= 0; unit = turn_row(units, ++turn, PAGED)) {
     const int row = SPLIT ? unit / a.splits : unit;
     const int lane = lane_fresh();
+    const int wave = fresh_s(wave_k);
     const int seq = row / a.rows_per_seq;
-    const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
-    const int32_t* idx_row = a.indices + (size_t)row * a.topk;
-    // Positions examined: below the explicit length, else the whole vector
-    // (a split unit: its blocks' positions [lo, scan) below the row length).
-    int lo = 0, scan = DYNAMIC ? clamp_length(a.topk_length[row], a.topk) : a.topk;
-    if constexpr (SPLIT) {
-      const int L = DYNAMIC ? scan
-                            : finish_tail_scan(load_tail_round(idx_row, a.topk, lane), idx_row,
-                                               a.topk, bound);
-      const int nblk = (L + 63) / 64, split = unit % a.splits;
-      lo = (int)((long long)split * nblk / a.splits) * 64;
-      const int hi = (int)((long long)(split + 1) * nblk / a.splits) * 64;
-      scan = hi < L ? hi : L;
-      scan = scan > lo ? scan : lo;
-    }
-
     // The previous row's epilogue has read the ring (and the sinks are staged).
     __syncthreads();
-    // Query slice into the ring: head h is row h % 32 of stage buffer h / 32.
-    {
+    const int lw = wave - (NW - PRO::kListWaves);  // list wave, or < 0
+    if (!PRO::kSplit || wave < PRO::kQWaves) {
+      // Query slice into the ring: head h is row h % 32 of stage buffer
+      // h / 32, in row groups of 8 per stage; wave w copies groups w + j
+      // kQWaves.
       const u32x4s rsrc = query_rsrc(a, row, T::kRowBytes);
       const int heads = lane & 31;  // lane j: head 32 st + j, offset moved down by (j % 4) KiB
 #pragma unroll
@@ -1784,57 +1803,111 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
         LDS_AS uint8_t* buf = ring + st * T::kBufBytes;
         const int o = (int)((uint32_t)(st * 32 + heads) * (uint32_t)T::kRowBytes + kSpanBias -
                             (uint32_t)(lane & 3) * 1024u);
-        stage_rope<D_QK, BK, NW>(buf, rsrc, o, wave);
-        RingPump<D_QK>{rsrc, buf, 8 * wave, __shfl(o, 8 * wave + (lane & 7)),
-                       (lane * 16) ^ ((wave & 1) << 5), 0u, 0u}
-            .copy_all();
+#pragma unroll
+        for (int j = 0; j < NW / PRO::kQWaves; ++j) {
+          const int g = PRO::kSplit ? wave + j * PRO::kQWaves : wave;
+          stage_rope<D_QK, BK, NW>(buf, rsrc, o, g);
+          RingPump<D_QK>{rsrc, buf, 8 * g, __shfl(o, 8 * g + (lane & 7)),
+                         (lane * 16) ^ ((g & 1) << 5), 0u, 0u}
+              .copy_all();
+        }
       }
     }
-
-    // Compaction: wave w examines positions [lo + w * per, lo + (w + 1) * per).
-    const int per = ((scan - lo + 255) >> 8) << 6;  // a multiple of 64, at most kRingChunks * 64
-    const int p0 = lo + wave * per;
-    int idxv[kRingChunks];
+    constexpr int KC = PRO::kChunks;
+    uint64_t mk[KC];
+    uint32_t offv[KC];
+    if (!PRO::kSplit || lw >= 0) {
+      const int bound = row_bound(PAGED, a.cache_seqlens, seq, a.s_kv, a.mbps);
+      const int32_t* idx_row = a.indices + (size_t)row * a.topk;
+      // Positions examined: below the explicit length, else the whole vector
+      // (a split unit: its blocks' positions [lo, scan) below the row length).
+      int lo = 0, scan = DYNAMIC ? clamp_length(a.topk_length[row], a.topk) : a.topk;
+      if constexpr (SPLIT) {
+        const int L = DYNAMIC ? scan
+                              : finish_tail_scan(load_tail_round(idx_row, a.topk, lane), idx_row,
+                                                 a.topk, bound);
+        const int nblk = (L + 63) / 64, split = unit % a.splits;
+        lo = (int)((long long)split * nblk / a.splits) * 64;
+        const int hi = (int)((long long)(split + 1) * nblk / a.splits) * 64;
+        scan = hi < L ? hi : L;
+        scan = scan > lo ? scan : lo;
+      }
+      // Compaction: list wave v examines positions [lo + v per, lo + (v + 1) per).
+      const int per = ((scan - lo + 64 * PRO::kListWaves - 1) / (64 * PRO::kListWaves)) * 64;
+      const int p0 = lo + lw * per;
+      int idxv[KC];
 #pragma unroll
-    for (int k = 0; k < kRingChunks; ++k) {
-      const int pos = p0 + 64 * k + lane;
-      idxv[k] = 64 * k < per && pos < scan ? idx_row[pos] : -1;
-    }
-    int pgv[kRingChunks];
+      for (int k = 0; k < KC; ++k) {
+        const int pos = p0 + 64 * k + lane;
+        idxv[k] = 64 * k < per && pos < scan ? idx_row[pos] : -1;
+      }
+      int pgv[KC];
 #pragma unroll
-    for (int k = 0; k < kRingChunks; ++k) {
-      const bool ok = idxv[k] >= 0 && idxv[k] < bound;
-      pgv[k] = page_lookup<PAGED>(a, seq, ok, idxv[k]);
-    }
-    uint64_t mk[kRingChunks];
-    uint32_t offv[kRingChunks];
-    int cnt = 0;
+      for (int k = 0; k < KC; ++k) {
+        const bool ok = idxv[k] >= 0 && idxv[k] < bound;
+        pgv[k] = page_lookup<PAGED>(a, seq, ok, idxv[k]);
+      }
+      int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < kRingChunks; ++k) {
-      const bool ok = idxv[k] >= 0 && idxv[k] < bound;
-      const BlockMeta m = block_meta<PAGED>(a, ok, idxv[k], pgv[k]);
-      mk[k] = m.mask;
-      offv[k] = BIG ? (uint32_t)m.phys * (uint32_t)(T::kRowBytes / kBigUnit)
-                    : (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias;
-      cnt += __builtin_popcountll(m.mask);
+      for (int k = 0; k < KC; ++k) {
+        const bool ok = idxv[k] >= 0 && idxv[k] < bound;
+        const BlockMeta m = block_meta<PAGED>(a, ok, idxv[k], pgv[k]);
+        mk[k] = m.mask;
+        offv[k] = BIG ? (uint32_t)m.phys * (uint32_t)(T::kRowBytes / kBigUnit)
+                      : (uint32_t)m.phys * (uint32_t)T::kRowBytes + kSpanBias;
+        cnt += __builtin_popcountll(m.mask);
+      }
+      if constexpr (PRO::kListWaves == 2) {
+        // The valid keys' table offsets in position order, written before
+        // the barrier (held across it, they would be spilled): list wave 0
+        // from the start of the list, list wave 1 (whose start depends on
+        // wave 0's count) against the end of the list area, moved below.
+        int base = lw == 0 ? 0 : kRingMaxTopk - cnt;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const uint64_t m = mk[k];
+          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if ((m >> lane) & 1ull) keys[base + below] = offv[k];
+          base += __builtin_popcountll(m);
+        }
+      }
+      if (lane == 0) counts[lw] = cnt;
     }
-    if (lane == 0) counts[wave] = cnt;
     wait_vm_all();  // this wave's query copies have landed
     __syncthreads();
-    int base = 0, n = 0;
+    int n = 0, base = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < PRO::kListWaves; ++w) {
       const int c = counts[w];
-      base += w < wave ? c : 0;
+      base += w < lw ? c : 0;
       n += c;
     }
+    if constexpr (PRO::kListWaves == 2) {
+      if (lw == 1) {
+        // All reads before any write: the two ranges may overlap.
+        const int c1 = n - base;
+        uint32_t e[KC];
 #pragma unroll
-    for (int k = 0; k < kRingChunks; ++k) {
-      const uint64_t m = mk[k];
-      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if ((m >> lane) & 1ull) keys[base + below] = offv[k];
-      base += __builtin_popcountll(m);
+        for (int k = 0; k < KC; ++k) {
+          const int i = 64 * k + lane;
+          e[k] = i < c1 ? keys[kRingMaxTopk - c1 + i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const int i = 64 * k + lane;
+          if (i < c1) keys[base + i] = e[k];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const uint64_t m = mk[k];
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if ((m >> lane) & 1ull) keys[base + below] = offv[k];
+        base += __builtin_popcountll(m);
+      }
     }
     __syncthreads();  // the key list and every wave's query rows are in LDS
     load_query_lds<D_QK, BK>(qf, ring + wave * T::kBufBytes, 0, lane);
@@ -1848,10 +1921,14 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
       for (int ct = 0; ct < kDV / 32; ++ct) acc[ct] = f32x16{};
       st = SoftmaxState{m_preset, 0.f, -INFINITY, false};
       __syncthreads();  // the query rows (or a previous attempt's stages) have been read
-      const u32x4s rsrc = BIG ? big_table_rsrc(a) : table_rsrc(a);
+      u32x4s rsrc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rsrc[i] = __builtin_amdgcn_readfirstlane(((const volatile LDS_AS uint32_t*)rsrc_raw)[i]);
+      const int wave_a = fresh_s(wave);
 #pragma unroll
       for (int t = 0; t < kAhead; ++t)
-        ring_copy_stage<D_QK, BIG>(ring + t * T::kBufBytes, rsrc, keys, n, t, wave, lane_id());
+        ring_copy_stage<D_QK, BIG>(ring + t * T::kBufBytes, rsrc, keys, n, t, wave_a, lane_id());
       // Step t: wait for stage t (stage t+1 stays in flight), issue stage
       // t + kAhead into the buffer of stage t - 2 (its rope part now, its
       // nope rows under the S^T MFMAs), S^T of stage t, then P*V of stage
@@ -1860,7 +1937,7 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
       bf16x8 pprev[2];
       // The list entries of the stage a step gathers are read one step
       // earlier (no LDS wait at the top of the step).
-      RingOffs offs = RingOffs::read(keys, kAhead, wave, lane_id());
+      RingOffs offs = RingOffs::read(keys, kAhead, wave_a, lane_id());
       auto step = [&](int t, auto first, auto masked) {
         __builtin_amdgcn_s_waitcnt(vmcnt_only((kAhead - 1) * kGather));
         barrier_lds();
