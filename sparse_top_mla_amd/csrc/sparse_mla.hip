@@ -1158,6 +1158,17 @@ __device__ __forceinline__ void load_query_lds(bf16x8 (&qf)[WideTile<D_QK>::kDSt
                : buf + rrow + ((32 * (d - 32)) ^ rw));
 }
 
+// Split decode's partial outputs: unit u (row * splits + split) stores the
+// fp32 output of head group g (32 heads x 512 values) as the tile at
+// split_tile(u, g, h_q / 32): 64 chunks of 1 KiB, chunk 4 ct + j holding
+// acc[ct][4 j .. 4 j + 3] of lane L at floats 4 L .. 4 L + 3, i.e. head
+// 32 g + L % 32 at columns 32 ct + 8 j + 4 (L / 32) .. + 3 (the MFMA
+// accumulator layout).  Each store instruction then writes 1 KiB
+// contiguous, straight from the accumulators.
+__device__ __forceinline__ size_t split_tile(size_t unit, int g, int groups) {
+  return (unit * (size_t)groups + (size_t)g) * (32 * kDV);
+}
+
 // SPLIT (paged decode without a key split): a unit is a (row, split) pair
 // covering blocks [split * nblk / splits, (split + 1) * nblk / splits) of the
 // row; it writes its partial output normalised by its own sum, with its lse
@@ -1315,14 +1326,16 @@ sparse_mla_fwd_wide_kernel(FwdArgs a) {
     // accumulator layout; an empty split has lse = -inf (no contribution).
     const size_t u = (size_t)unit * a.h_q + head;
     const float inv = l_fin > 0.f ? 1.f / l_fin : 0.f;
-    float* o = a.ws_o + u * kDV + 4 * half;
+    float* o = a.ws_o + split_tile(unit, hg, a.h_q / 32) + 4 * lane;
 #pragma unroll
     for (int ct = 0; ct < kDV / 32; ++ct)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * j) =
+        // non-temporal: the merge kernel reads the partials once
+        __builtin_nontemporal_store(
             f32x4{acc[ct][4 * j] * inv, acc[ct][4 * j + 1] * inv, acc[ct][4 * j + 2] * inv,
-                  acc[ct][4 * j + 3] * inv};
+                  acc[ct][4 * j + 3] * inv},
+            reinterpret_cast<f32x4*>(o + (4 * ct + j) * 256));
     if (half == 0) {
       a.ws_stats[2 * u] = l_fin > 0.f ? lse_v : -INFINITY;
       a.ws_stats[2 * u + 1] = ml_v;
@@ -1992,40 +2005,21 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
     const int lane_e = lane_fresh(), hl = lane_e & 31, half = lane_e >> 5, head = wave * 32 + hl;
     if constexpr (SPLIT) {
       // The unit's output normalised by its own sum (the sink joins once,
-      // in the merge); an empty unit has lse = -inf (no contribution).  The
-      // wave's fp32 tile (32 heads x 512) leaves in two halves of 256
-      // columns through its own ring buffer: the accumulator layout
-      // acc[ct][i] = O[head][32 ct + 8 (i / 4) + 4 half + i % 4] puts 16 B
-      // chunk 8 (ct % 8) + 2 (i / 4) + half of the head's 1 KiB half row in
-      // a lane, written at chunk c ^ hl of LDS row hl; then each store
-      // instruction writes one head's half row, 1 KiB contiguous (stored
-      // from the accumulator layout, an instruction would touch 32 rows
-      // with 32 B each).
+      // in the merge); an empty unit has lse = -inf (no contribution).
+      // Stored in the accumulator layout (split_tile): 1 KiB per store
+      // instruction.
       const size_t u = (size_t)unit * a.h_q + head;
       const float inv = st.l_sum > 0.f ? 1.f / st.l_sum : 0.f;
-      LDS_AS uint8_t* tile = ring + wave * T::kBufBytes;
-      static_assert(T::kBufBytes >= 32 * 1024, "a 32 x 256 fp32 half tile fits a ring buffer");
-      float* obase = a.ws_o + ((size_t)unit * a.h_q + wave * 32) * kDV + 4 * lane_e;
+      float* obase = a.ws_o + split_tile(unit, wave, a.h_q / 32) + 4 * lane_e;
 #pragma unroll
-      for (int K = 0; K < 2; ++K) {
+      for (int ct = 0; ct < kDV / 32; ++ct)
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int ct = 8 * K + c, chunk = 8 * c + 2 * j + half;
-            *reinterpret_cast<LDS_AS f32x4*>(tile + hl * 1024 + ((chunk ^ hl) << 4)) =
-                f32x4{acc[ct][4 * j] * inv, acc[ct][4 * j + 1] * inv, acc[ct][4 * j + 2] * inv,
-                      acc[ct][4 * j + 3] * inv};
-          }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the half tile is complete
-#pragma unroll 4
-        for (int h = 0; h < 32; ++h) {
-          const f32x4 v = *reinterpret_cast<const LDS_AS f32x4*>(tile + h * 1024 + ((lane_e ^ h) << 4));
+        for (int j = 0; j < 4; ++j)
           // non-temporal: the merge kernel reads the partials once
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(obase + (size_t)h * kDV + 256 * K));
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read before the next half overwrites it
-      }
+          __builtin_nontemporal_store(
+              f32x4{acc[ct][4 * j] * inv, acc[ct][4 * j + 1] * inv, acc[ct][4 * j + 2] * inv,
+                    acc[ct][4 * j + 3] * inv},
+              reinterpret_cast<f32x4*>(obase + (4 * ct + j) * 256));
       if (half == 0) {
         a.ws_stats[2 * u] = st.l_sum > 0.f ? (st.m_ref + __log2f(st.l_sum)) * kLn2 : -INFINITY;
         a.ws_stats[2 * u + 1] = st.l_sum > 0.f ? st.m_max * kLn2 : -INFINITY;
@@ -2066,40 +2060,67 @@ sparse_mla_fwd_ring_kernel(FwdArgs a) {
   }
 }
 
-// Merge of the splits of split decode, one wave per (row, head): the split
-// lses give lse = logsumexp over the splits, each split's output enters with
-// weight exp(lse_s - lse), and an empty split (lse_s = -inf) contributes
-// nothing; the sink joins the denominator once, after the merge; a row
-// whose splits are all empty gives out = 0, lse = +inf, max_logits = -inf.
-// Lane l takes value columns 8l .. 8l + 7.  The splits are read eight at a
-// time, every load of a round issued before any is used (a loop over single
-// splits waits one memory latency per split); the statistics are
-// wave-uniform loads.  Rounds past the last split re-read that split with
-// weight 0 (it is finite), so the sums keep the split order.
+// Merge of the splits of split decode.  The split lses give lse =
+// logsumexp over the splits, each split's output enters with weight
+// exp(lse_s - lse), and an empty split (lse_s = -inf) contributes nothing;
+// the sink joins the denominator once, after the merge; a row whose splits
+// are all empty gives out = 0, lse = +inf, max_logits = -inf.
+// One wave per (row, group of 32 heads, 32 value columns ct): the partials
+// are stored in the attention kernels' accumulator layout (split_tile), so
+// lane (half, j32) reads 16 B chunks j = 0..3 of its tile, values of head
+// 32 g + j32 at columns 32 ct + 8 j + 4 half .. + 3.  The splits are read
+// eight at a time, every load of a round issued before any is used (a loop
+// over single splits waits one memory latency per split).  Rounds past the
+// last split re-read that split with weight 0 (it is finite), so the sums
+// keep the split order.
 template <bool SINK>
 __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
+  const int groups = a.h_q / 32;
   const long long w = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (w >= (long long)a.rows * a.h_q) return;
-  const int row = (int)(w / a.h_q), head = (int)(w % a.h_q), lane = lane_id();
+  if (w >= (long long)a.rows * groups * (kDV / 32)) return;
+  const int ct = (int)(w % (kDV / 32));
+  const int g = (int)((w / (kDV / 32)) % groups), row = (int)(w / (kDV / 32) / groups);
+  const int lane = lane_id(), j32 = lane & 31, half = lane >> 5, head = g * 32 + j32;
   const int S = a.splits;
   const float* st = a.ws_stats + ((size_t)row * S * a.h_q + head) * 2;
   const size_t sstride = (size_t)a.h_q * 2;  // between the splits of one head
   constexpr int R = 8;                       // splits per round
-  const float* o = a.ws_o + ((size_t)row * S * a.h_q + head) * kDV + 8 * lane;
-  const size_t ostride = (size_t)a.h_q * kDV;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* o = a.ws_o + split_tile((size_t)row * S, g, groups) + (size_t)ct * 4 * 256 + 4 * lane;
+  const size_t ostride = (size_t)groups * 32 * kDV;  // between the splits' tiles
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   float lse_v = INFINITY, ml_v = -INFINITY;
+  auto add_round = [&](int s0, float lse) {
+    f32x4 v[R][4];
+    float wg[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int s = s0 + j < S ? s0 + j : S - 1;
+      wg[j] = st[s * sstride];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[j][c] = *reinterpret_cast<const f32x4*>(o + s * ostride + c * 256);
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float wgt = s0 + j < S ? expf(wg[j] - lse) : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * c + e] += wgt * v[j][c][e];
+    }
+  };
   if (S <= R) {
     // One round: every statistic and partial loaded before any is used.
+    f32x4 v[R][4];
     float l8[R], x8[R];
-    f32x4 v0[R], v1[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int s = j < S ? j : S - 1;
       l8[j] = st[s * sstride];
       x8[j] = st[s * sstride + 1];
-      v0[j] = *reinterpret_cast<const f32x4*>(o + s * ostride);
-      v1[j] = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[j][c] = *reinterpret_cast<const f32x4*>(o + s * ostride + c * 256);
     }
     float m = -INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -2117,10 +2138,9 @@ __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
       for (int j = 0; j < R; ++j) {
         const float wgt = j < S ? expf(l8[j] - lse) : 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] += wgt * v0[j][e];
-          acc[4 + e] += wgt * v1[j][e];
-        }
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * c + e] += wgt * v[j][c][e];
       }
       lse_v = lse;
       ml_v = mx;
@@ -2153,26 +2173,7 @@ __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
           if (s0 + j < S) z += expf(e8[j] - m);  // exp(-inf) = 0
       }
       const float lse = m + logf(z);
-      for (int s0 = 0; s0 < S; s0 += R) {
-        f32x4 v0[R], v1[R];
-        float wg[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          const int s = s0 + j < S ? s0 + j : S - 1;
-          wg[j] = st[s * sstride];
-          v0[j] = *reinterpret_cast<const f32x4*>(o + s * ostride);
-          v1[j] = *reinterpret_cast<const f32x4*>(o + s * ostride + 4);
-        }
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-          const float wgt = s0 + j < S ? expf(wg[j] - lse) : 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[e] += wgt * v0[j][e];
-            acc[4 + e] += wgt * v1[j][e];
-          }
-        }
-      }
+      for (int s0 = 0; s0 < S; s0 += R) add_round(s0, lse);
       lse_v = lse;
       ml_v = mx;
     }
@@ -2181,18 +2182,19 @@ __global__ void __launch_bounds__(256) split_combine_kernel(FwdArgs a) {
     float f = 1.f;
     if (SINK) f = 1.f / (1.f + expf(a.attn_sink[head] - lse_v));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= f;
+    for (int e = 0; e < 16; ++e) acc[e] *= f;
   }
-  bf16x8 ob;
+  __bf16* orow = a.out + ((size_t)row * a.h_q + head) * kDV + 32 * ct + 4 * half;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ob[e] = (__bf16)acc[e];
-  *reinterpret_cast<bf16x8*>(a.out + ((size_t)row * a.h_q + head) * kDV + 8 * lane) = ob;
-  if (lane == 0) {
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<bf16x4*>(orow + 8 * c) =
+        bf16x4{(__bf16)acc[4 * c], (__bf16)acc[4 * c + 1], (__bf16)acc[4 * c + 2],
+               (__bf16)acc[4 * c + 3]};
+  if (ct == 0 && half == 0) {
     a.lse[(size_t)row * a.h_q + head] = lse_v;
     if (a.max_logits) a.max_logits[(size_t)row * a.h_q + head] = ml_v;
   }
 }
-
 
 // Row lengths from the same routines the attention kernels use; one wave per row.
 __global__ void __launch_bounds__(256) row_lengths_kernel(const int32_t* indices,
@@ -2380,8 +2382,9 @@ smla_status launch_split(const FwdArgs& args, hipStream_t stream) {
   g_last_kernel = BIG ? "split_big" : "split";
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
-  const long long waves = (long long)args.rows * args.h_q;
-  // One wave per workgroup: the (row, head) waves spread over every CU.
+  const long long waves = (long long)args.rows * (args.h_q / 32) * (kDV / 32);
+  // One wave per workgroup: the (row, head group, column tile) waves spread
+  // over every CU.
   hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)waves), dim3(64), 0, stream,
                      args);
   e = hipGetLastError();
@@ -2402,8 +2405,9 @@ smla_status launch_ring_split(const FwdArgs& args, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(SMLA_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_kernel = BIG ? "ring_split_big" : "ring_split";
-  const long long waves = (long long)args.rows * args.h_q;
-  // One wave per workgroup: the (row, head) waves spread over every CU.
+  const long long waves = (long long)args.rows * (args.h_q / 32) * (kDV / 32);
+  // One wave per workgroup: the (row, head group, column tile) waves spread
+  // over every CU.
   hipLaunchKernelGGL((split_combine_kernel<SINK>), dim3((unsigned)waves), dim3(64), 0, stream,
                      args);
   e = hipGetLastError();
