@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=3,
                     help="decode: also time calls that rotate over this many copies of the inputs "
                          "(cold Infinity Cache); 0 disables")
+    ap.add_argument("--splits", type=int, default=1,
+                    help="decode workloads: time the split-KV path with this many splits as the "
+                         "main line (1: the unsplit path)")
     ap.add_argument("--big-pool-gib", type=float, default=0.0,
                     help="decode: also time the same call with its pages scattered over a pool of "
                          "this many GiB (above 4 GiB the kernels rebase a resource per copied row)")
@@ -716,7 +719,7 @@ def _mfma_busy(sub, kernels=("sparse_mla_fwd",)):
 
 
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d <dir>/trace_{w} -o run --output-format csv -- "
-                 "python3 -u bench.py --workload {w} --no-variants --cpu-seconds 0 --replicas 0")
+                 "python3 -u bench.py --workload {wl} --no-variants --cpu-seconds 0 --replicas 0{extra}")
 
 
 def summarize_traces(d):
@@ -725,9 +728,13 @@ def summarize_traces(d):
     kernel's timed region (its last `steps` dispatches before the group
     calls) and the bench.py line of the same run."""
     import csv
+    import re
     d = Path(d)
     for sub in sorted(d.glob("trace_*")):
         w = sub.name[len("trace_"):]
+        # trace_<workload>_split<N>: the split-KV path (bench.py --splits N)
+        m = re.match(r"^(.*)_split(\d+)$", w)
+        wl, extra = (m.group(1), f" --splits {m.group(2)}") if m else (w, "")
         stats_f, trace_f = sub / "run_kernel_stats.csv", sub / "run_kernel_trace.csv"
         bench_f = d / f"bench_{w}.json"
         if not stats_f.exists() or not trace_f.exists() or not bench_f.exists():
@@ -736,7 +743,7 @@ def summarize_traces(d):
         stats = [r for r in csv.DictReader(open(stats_f))
                  if "sparse_mla" in r["Name"] or "block_sparse" in r["Name"] or "combine" in r["Name"]
                  or "row_lengths" in r["Name"] or "dkv" in r["Name"] or "bwd_" in r["Name"]]
-        name_frag = kernel_name(w)
+        name_frag = kernel_name(wl)
         disp = sorted((r for r in csv.DictReader(open(trace_f)) if name_frag in r["Kernel_Name"]),
                       key=lambda r: int(r["Start_Timestamp"]))
         groups = line.get("kernel_ms", {}).get("group_groups", 0) or 0
@@ -747,7 +754,7 @@ def summarize_traces(d):
         short = kname.replace("(anonymous namespace)::", "").replace("void ", "").split("<")[0]
         out = [f"# {short} — {line['config']['workload']}", "",
                "Command (from the repository root on one MI355X; `export TMPDIR=/tmp` first):", "",
-               "```", TRACE_COMMAND.format(w=w), "```", "",
+               "```", TRACE_COMMAND.format(w=w, wl=wl, extra=extra), "```", "",
                f"bench.py timed {steps} calls after {line['warmup']} warmups through the C entry point "
                f"(and {groups} groups of 20 calls after them).", "",
                "rocprofv3 kernel statistics (run_kernel_stats.csv):", "",
@@ -843,15 +850,16 @@ def calibrate_copy():
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
-def measure(workload, case, dev, steps, warmup, groups=7):
+def measure(workload, case, dev, steps, warmup, groups=7, num_splits=1):
     """Times one workload: exactly `steps` calls after `warmup` (wall clock and
     events around the timed region), then the pages' 7 groups of 20 calls.
-    Returns (record, counts)."""
+    num_splits > 1 (decode): the split-KV path.  Returns (record, counts)."""
     import torch
     bwd = workload == "bwd_h64"
     bs = is_block_sparse(case)
     counts = bwd_counts(case) if bwd else bs_counts(case) if bs else algorithmic_counts(case)
-    call = gpu_call_bwd(case, dev) if bwd else gpu_call_bs(case, dev) if bs else gpu_call(case, dev)
+    call = (gpu_call_bwd(case, dev) if bwd else gpu_call_bs(case, dev) if bs
+            else gpu_call(case, dev, num_splits=num_splits))
     torch.cuda.synchronize()
     ms_per_step, kernel_ms = time_steps(call, steps, warmup)
     gm = time_groups(call, groups=groups) if groups > 0 else [kernel_ms]
@@ -909,7 +917,13 @@ def main():
     case = make_case(args.workload)
     bwd = args.workload == "bwd_h64"
     bs = is_block_sparse(case)
-    main_rec, counts = measure(args.workload, case, dev, args.steps, args.warmup, args.groups)
+    if args.splits > 1 and not is_decode(case):
+        sys.exit("--splits applies to the decode workloads")
+    main_rec, counts = measure(args.workload, case, dev, args.steps, args.warmup, args.groups,
+                               num_splits=args.splits)
+    if args.splits > 1:
+        # The stored counter records are the unsplit path's.
+        main_rec["roofline"]["traffic"] = None
     value = counts["flops"] / (main_rec["ms_per_call"] * 1e-3) / 1e12
 
     variants = {}
@@ -951,7 +965,7 @@ def main():
         torch.cuda.empty_cache()
     rows = case.batch * case.s_q if is_decode(case) else counts["rows"]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if is_decode(case) and rows < cus and case.h_q == 128:
+    if is_decode(case) and rows < cus and case.h_q == 128 and args.splits == 1:
         # Fewer rows than CUs: the split-KV path, at the binding's split count.
         import sparse_top_mla_amd as smla
         splits = max(2, smla.decode_num_splits(case.batch, case.s_q, case.topk))
@@ -991,6 +1005,7 @@ def main():
             "algorithmic_bytes_per_call": counts["bytes"],
             "topk_length": case.topk_length is not None,
             "attn_sink": case.attn_sink is not None,
+            **({"num_splits": args.splits} if args.splits > 1 else {}),
         }),
         "kernel_ms": {"timed_region_mean": main_rec["kernel_ms"],
                       **{f"group_{k}": v for k, v in main_rec["group_means_ms"].items()}},
